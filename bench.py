@@ -1,0 +1,210 @@
+"""Benchmark of the tile-sparse attention forward pass on one MI355X.
+
+One step = one tsa_attention_fwd call (bitmap in -> O out: on-the-fly mask
+compaction, kept-K/V staging, QK^T, online softmax, PV, normalisation) on
+the Wan 2.1 480p shape with 16x8 tiles at 70% frame-structured sparsity,
+inputs resident in HBM.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "kept-tile effective TFLOPS (% bf16 MFMA peak) + ms/call at 70% sparsity"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}     # MI355X dense matrix-core peaks
+KERNEL_SOURCES = ("tile_sparse_attention_amd/csrc/attention_fwd_impl.h",
+                  "tile_sparse_attention_amd/csrc/attention_fwd_inst.h",
+                  "tile_sparse_attention_amd/csrc/tsa_device.h")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def make_mask(w, q, k):
+    """Device keep-bitmap of the workload (int32 storage of uint32 words)."""
+    import numpy as np
+    import torch
+
+    import tile_sparse_attention_amd as T
+    import workloads as W
+    kind = w.mask.kind
+    if kind == "hash":
+        return T.maskgen_hash(w.B, w.H, w.L, w.M, w.N, **W.hash_params(w))
+    if kind == "predicted":
+        return T.predict_mask(q, k, w.M, w.N, w.mask.sparsity_percent)
+    bits = W.mask_bits(w)
+    return torch.from_numpy(bits.view(np.int32)).cuda()
+
+
+def kept_flops_device(w, mask) -> int:
+    """4*d*sum over kept tiles of m_i*n_j, counted on the GPU from the bitmap
+    (row counts from the library's compaction call, last partial key tile
+    corrected with its bit)."""
+    import torch
+
+    import tile_sparse_attention_amd as T
+    row_ptr, _ = T.mask_compact(mask, w.L, w.M, w.N, col_capacity=0)
+    counts = (row_ptr[1:] - row_ptr[:-1]).view(w.B, w.H, w.T_q)
+    m = torch.clamp(w.L - torch.arange(w.T_q, device=mask.device) * w.M, max=w.M).to(torch.int64)
+    n_last = w.L - (w.T_k - 1) * w.N
+    last = w.T_k - 1
+    last_bit = ((mask[..., last // 32] >> (last % 32)) & 1).to(torch.int64)
+    keys = counts * w.N - last_bit * (w.N - n_last)
+    return int(4 * w.d * (keys * m).sum().item())
+
+
+def time_calls(fn, steps, warmup):
+    """(ms per step over the bracketed region, mean per-call ms from events)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    per = [a.elapsed_time(b) for a, b in ev]
+    return wall / steps, sum(per) / len(per), min(per)
+
+
+def cpu_baseline(w, q, k, v, mask, budget_s=15.0):
+    """fp64 oracle on a bounded sample of query tiles of head 0, same metric unit."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    bits_h0 = mask[0, 0].cpu().numpy().view(np.uint32)
+    tiles = W.sample_tiles(w)[0, 0]
+    qh, kh, vh = q[0, 0].cpu(), k[0, 0].cpu(), v[0, 0].cpu()
+    # one probe group to size the sample to the time budget
+    t0 = time.perf_counter()
+    oracle.attention_rows(qh, kh, vh, bits_h0, w.M, w.N, w.scale, tiles[:8], group=8)
+    per_tile = (time.perf_counter() - t0) / 8
+    n = int(max(8, min(len(tiles), budget_s / max(per_tile, 1e-6))))
+    sample = tiles[:n]
+    t0 = time.perf_counter()
+    oracle.attention_rows(qh, kh, vh, bits_h0, w.M, w.N, w.scale, sample, group=16)
+    secs = time.perf_counter() - t0
+    # kept FLOPs of the sampled rows (the oracle itself does dense work)
+    keep = oracle.unpack_mask(bits_h0[sample], w.T_k)
+    m = np.minimum(w.M, w.L - sample * w.M)
+    nj = np.minimum(w.N, w.L - np.arange(w.T_k) * w.N)
+    kept = 4 * w.d * int((m[:, None] * keep * nj[None, :]).sum())
+    return {"value": kept / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} sampled query tiles ({n * w.M} rows) of head 0, all {w.L} keys, fp64 "
+                      f"numpy, {secs:.1f} s; kept FLOPs of those rows / time"}
+
+
+def traffic_for(workload: str, sha: str):
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(every (batch, head) is independent; see the sharding note in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import tile_sparse_attention_amd as T
+    import workloads as W
+    name = args.workload or W.HEADLINE
+    w = W.get(name)
+    log(f"workload {name}: B={w.B} H={w.H} L={w.L} d={w.d} M={w.M} N={w.N} {w.dtype}")
+    t0 = time.perf_counter()
+    q, k, v = W.make_qkv(w)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    mask = make_mask(w, qd, kd)
+    torch.cuda.synchronize()
+    out = torch.empty_like(qd)
+    flops = kept_flops_device(w, mask)
+    dense_flops = 4 * w.B * w.H * w.L * w.L * w.d
+    log(f"kept FLOPs {flops:.4e} ({flops / dense_flops:.4f} of dense)")
+
+    def step():
+        T.attention_fwd(qd, kd, vd, mask, w.M, w.N, w.scale, out=out)
+
+    ms_step, ms_kernel, ms_min = time_calls(step, args.steps, args.warmup)
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    log(f"sparse: {ms_step:.3f} ms/step, kernel mean {ms_kernel:.3f} ms (min {ms_min:.3f}), "
+        f"{tflops:.1f} TFLOP/s")
+    peak = PEAK_TFLOPS[w.dtype]
+    cfg = {"workload": name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "M": w.M, "N": w.N,
+           "mask": w.description, "kept_fraction": round(flops / dense_flops, 6),
+           "kept_flops": flops, "pct_of_peak": round(100 * tflops / peak, 2),
+           "peak_tflops": peak}
+    if not args.no_dense:
+        ones = torch.full_like(mask, -1)
+        out2 = torch.empty_like(qd)
+
+        def dense_step():
+            T.attention_fwd(qd, kd, vd, ones, w.M, w.N, w.scale, out=out2)
+        d_step, d_kernel, _ = time_calls(dense_step, max(3, args.steps // 4), 1)
+        cfg["all_ones_ms"] = round(d_step, 4)
+        cfg["all_ones_tflops"] = round(dense_flops / (d_step * 1e-3) / 1e12, 2)
+        cfg["speedup_vs_all_ones"] = round(d_step / ms_step, 3)
+        log(f"all-ones: {d_step:.3f} ms/step ({cfg['all_ones_tflops']} TFLOP/s), "
+            f"sparse speedup {cfg['speedup_vs_all_ones']}x")
+        del ones, out2
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
+    sha = kernel_sha()
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic_for(name, sha),
+            "kernel": "attn_fwd_kernel", "kernel_sha": sha}
+    rec = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": w.dtype, "data": "synthetic (seeded normal Q/K/V, generated masks)",
+           "config": cfg, "roofline": roof}
+    if not args.no_cpu:
+        log("timing the CPU oracle on a bounded sample ...")
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, mask)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,126 @@
+/*
+ * tsa.h - fine-grained tile-sparse softmax attention (forward) for AMD MI355X (gfx950).
+ *
+ * The operation is the one described in the abstract of "FG-Attn: Leveraging
+ * Fine-Grained Sparse Attention in Video Diffusion Models" (section Abstract):
+ * the attention score matrix of each (batch, head) is cut into tiles of M
+ * queries by N keys (M >= 16, N >= 1); a tile is either computed or skipped as
+ * a whole, and skipped scores take no part in the softmax.
+ *
+ * Conventions shared by every call:
+ *   - Q, K, V, O are contiguous row-major [B][H][L][d] device arrays of one
+ *     element type (fp32 or bf16); d is innermost.
+ *   - The keep-bitmap is a contiguous uint32 device array [B][H][T_q][W] with
+ *     T_q = ceil(L/M), T_k = ceil(L/N), W = ceil(T_k/32).  Key tile j of query
+ *     tile i is bit (j % 32) of word (j / 32) of row (b, h, i), least significant
+ *     bit first; 1 keeps the tile.  Bits at j >= T_k are padding and ignored.
+ *   - The last query tile and the last key tile may be partial (L need not be a
+ *     multiple of M or N); rows and keys at index >= L do not exist.
+ *   - A query row with no kept key gets O = 0 and LSE = -inf.
+ *   - Every call is asynchronous on the caller's `stream` (a hipStream_t; NULL
+ *     is the default stream).  Outputs are valid once the stream has reached
+ *     the work.  The library allocates no device memory and keeps no state
+ *     between calls; the caller owns every buffer.
+ *   - Arguments are checked before anything is enqueued.  A failed check
+ *     enqueues nothing and returns a status; no call aborts or throws.
+ *     tsa_last_error() returns the calling thread's detail text of its last
+ *     failure.
+ *
+ * Supported problem set: dtype in {F32, BF16}; d in {64, 128}; M in {16, 32, 64};
+ * N in {1, 2, 4, 8, 16, 32, 64}; 1 <= L <= 2^26; B*H <= 2^20.  Other values
+ * return TSA_ERR_UNSUPPORTED.
+ */
+#ifndef TSA_H_
+#define TSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TSA_OK = 0,
+  TSA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, bad scale, ... */
+  TSA_ERR_UNSUPPORTED = 2,        /* (dtype, d, M, N) outside the supported set */
+  TSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  TSA_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} tsa_status_t;
+
+typedef enum { TSA_DTYPE_F32 = 0, TSA_DTYPE_BF16 = 1 } tsa_dtype_t;
+
+typedef enum {
+  TSA_OP_ATTENTION_FWD = 0,
+  TSA_OP_MASK_COMPACT = 1,
+  TSA_OP_PREDICT_MASK = 2
+} tsa_op_t;
+
+/* Problem shape: batch B, heads H, sequence length L, head dim d, tile M x N. */
+typedef struct {
+  int32_t B, H, L, d, M, N;
+  tsa_dtype_t dtype;
+} tsa_problem_t;
+
+/* Number of uint32 words per bitmap row, ceil(ceil(L/N)/32); 0 if L or N < 1.
+ * Host only. */
+int64_t tsa_mask_row_words(int32_t L, int32_t N);
+
+/* Device workspace in bytes that `op` needs for problem `p` (may be 0).  Host
+ * only; enqueues nothing. */
+tsa_status_t tsa_workspace_size(tsa_op_t op, const tsa_problem_t* p, size_t* bytes);
+
+/* Tile-sparse attention forward (FG-Attn abstract: scores skipped per M x N
+ * tile, skipped scores excluded from the softmax):
+ *   O[b,h,r,:] = sum_c P[r,c] V[b,h,c,:],  P[r,:] = softmax over kept c of
+ *   scale * Q[b,h,r,:] . K[b,h,c,:], where c is kept iff bit(b,h,r/M,c/N) = 1.
+ * q, k, v: [B,H,L,d] of p->dtype.  mask_bits: [B,H,T_q,W] uint32.
+ * o: [B,H,L,d] of p->dtype, written for every row (must not alias q, k, v).
+ * lse: optional [B,H,L] fp32 natural-log sum-exp of the kept scaled scores
+ * (NULL skips it).  scale: finite.  Accumulation is fp32; bf16 inputs are
+ * multiplied on bf16 matrix cores with the probabilities rounded to bf16.
+ * workspace: tsa_workspace_size(TSA_OP_ATTENTION_FWD) bytes (currently 0; may
+ * be NULL when 0). */
+tsa_status_t tsa_attention_fwd(const tsa_problem_t* p,
+                               const void* q, const void* k, const void* v,
+                               const uint32_t* mask_bits, float scale,
+                               void* o, float* lse,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Mask compaction (FG-Attn abstract: one skip decision per M x N tile): every
+ * bitmap row (b,h,i) becomes the ascending list of its kept key tiles j < T_k.
+ * row_ptr: [B*H*T_q + 1] int64, rows in (b,h,i) row-major order, row_ptr[0]=0,
+ * always written in full.  col_idx: int32 key-tile indices; entries at
+ * positions >= col_capacity are not written, so the caller checks
+ * row_ptr[B*H*T_q] <= col_capacity.  p->d, p->dtype are ignored.
+ * workspace: tsa_workspace_size(TSA_OP_MASK_COMPACT) bytes. */
+tsa_status_t tsa_mask_compact(const tsa_problem_t* p, const uint32_t* mask_bits,
+                              int64_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Tile-mask predictor from pooled queries and keys.  The FG-Attn abstract
+ * takes the tile mask as an input; this call produces one: Qbar_i = mean of
+ * the (valid) rows of query tile i, Kbar_j = mean of the keys of key tile j,
+ * s_ij = Qbar_i . Kbar_j in fp32, and row i keeps its
+ * k = T_k - 1 - floor(sparsity_percent * (T_k - 1) / 100) highest-scoring
+ * tiles, equal scores going to the smaller j.  With distinct scores these are
+ * the tiles strictly above the row's linearly interpolated
+ * sparsity_percent-th percentile.  q, k: [B,H,L,d]; 0 <= sparsity_percent < 100.
+ * mask_out: [B,H,T_q,W] uint32, written in full (padding bits zero).
+ * workspace: tsa_workspace_size(TSA_OP_PREDICT_MASK) bytes. */
+tsa_status_t tsa_predict_mask(const tsa_problem_t* p, const void* q, const void* k,
+                              int32_t sparsity_percent, uint32_t* mask_out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* tsa_status_string(tsa_status_t s);
+
+/* Detail text of the calling thread's last failed call ("" if none). */
+const char* tsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSA_H_ */

@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+symbol the headers declare, sizes workspaces and rejects bad arguments
+before enqueuing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tile_sparse_attention_amd as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(T.LIB_PATH),
+                                reason="libtsa.so not built (python tile_sparse_attention_amd/build.py)")
+
+
+def _declared():
+    names = set()
+    for h in ("tsa.h", "tsa_workload.h"):
+        txt = open(os.path.join(ROOT, "include", h)).read()
+        names |= set(re.findall(r"\b(tsa_[a-z0-9_]+)\s*\(", txt))
+    return names
+
+
+def test_exports_every_declared_symbol():
+    lib = T.lib()
+    declared = _declared()
+    assert declared == set(T.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_row_words():
+    assert T.mask_row_words(32760, 8) == 128
+    assert T.mask_row_words(75600, 1) == 2363
+    assert T.mask_row_words(118800, 16) == 233
+    assert T.mask_row_words(512, 16) == 1
+    assert T.mask_row_words(0, 8) == 0 and T.mask_row_words(10, 0) == 0
+
+
+def test_workspace_sizes():
+    pr = T.problem(1, 40, 32760, 128, 16, 8)
+    assert T.workspace_size(T.OP_ATTENTION_FWD, pr) == 0
+    assert T.workspace_size(T.OP_MASK_COMPACT, pr) >= 40 * 2048 * 4
+    pp = T.problem(1, 24, 118800, 128, 16, 16)
+    ws = T.workspace_size(T.OP_PREDICT_MASK, pp)
+    assert 2 * 24 * 7425 * 128 * 4 < ws < 2 * 24 * 7425 * 128 * 4 + (600 << 20)
+    with pytest.raises(T.TsaError) as e:
+        T.workspace_size(7, pr)
+    assert e.value.status == T.ERR_INVALID_ARGUMENT
+
+
+def _attn(pr, q=1, k=1, v=1, m=1, o=2, scale=1.0):
+    # non-null fake addresses: validation must reject before any use of them
+    def p(x):
+        return ctypes.c_void_p(0x10000 * x) if x else ctypes.c_void_p(0)
+    return T.lib().tsa_attention_fwd(ctypes.byref(pr), p(q), p(k), p(v), p(m),
+                                     ctypes.c_float(scale), p(o), None, None, 0, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("M", 8, T.ERR_UNSUPPORTED), ("M", 48, T.ERR_UNSUPPORTED), ("N", 3, T.ERR_UNSUPPORTED),
+    ("N", 128, T.ERR_UNSUPPORTED), ("d", 96, T.ERR_UNSUPPORTED), ("dtype", 5, T.ERR_UNSUPPORTED),
+    ("L", 0, T.ERR_INVALID_ARGUMENT), ("B", -1, T.ERR_INVALID_ARGUMENT),
+    ("L", (1 << 26) + 1, T.ERR_UNSUPPORTED), ("H", 1 << 21, T.ERR_UNSUPPORTED),
+])
+def test_attention_rejects_bad_problem(field, value, status):
+    pr = T.problem(1, 2, 512, 64, 16, 16)
+    setattr(pr, field, value)
+    assert _attn(pr) == status
+    assert T.last_error() != ""
+
+
+def test_attention_rejects_bad_pointers_and_scale():
+    pr = T.problem(1, 2, 512, 64, 16, 16, T.DTYPE_F32)
+    assert _attn(pr, q=0) == T.ERR_INVALID_ARGUMENT
+    assert _attn(pr, m=0) == T.ERR_INVALID_ARGUMENT
+    assert _attn(pr, o=0) == T.ERR_INVALID_ARGUMENT
+    assert _attn(pr, o=1) == T.ERR_INVALID_ARGUMENT          # aliases q
+    assert _attn(pr, scale=float("inf")) == T.ERR_INVALID_ARGUMENT
+    assert _attn(pr, scale=float("nan")) == T.ERR_INVALID_ARGUMENT
+    lib = T.lib()
+    st = lib.tsa_attention_fwd(ctypes.byref(pr), ctypes.c_void_p(0x10008), ctypes.c_void_p(0x20000),
+                               ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000),
+                               ctypes.c_float(1.0), ctypes.c_void_p(0x50000), None, None, 0, None)
+    assert st == T.ERR_INVALID_ARGUMENT and "align" in T.last_error()
+
+
+def test_compact_and_predict_validation():
+    lib = T.lib()
+    pr = T.problem(1, 2, 512, 64, 16, 16)
+    need = T.workspace_size(T.OP_MASK_COMPACT, pr)
+    st = lib.tsa_mask_compact(ctypes.byref(pr), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000),
+                              ctypes.c_void_p(0x3000), 10, ctypes.c_void_p(0x4000), need - 1, None)
+    assert st == T.ERR_WORKSPACE_TOO_SMALL
+    st = lib.tsa_mask_compact(ctypes.byref(pr), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000),
+                              None, 10, ctypes.c_void_p(0x4000), need, None)
+    assert st == T.ERR_INVALID_ARGUMENT
+    st = lib.tsa_mask_compact(ctypes.byref(pr), None, ctypes.c_void_p(0x2000),
+                              ctypes.c_void_p(0x3000), 10, ctypes.c_void_p(0x4000), need, None)
+    assert st == T.ERR_INVALID_ARGUMENT
+    pw = T.workspace_size(T.OP_PREDICT_MASK, pr)
+    for sp in (-1, 100):
+        st = lib.tsa_predict_mask(ctypes.byref(pr), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000),
+                                  sp, ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000), pw, None)
+        assert st == T.ERR_INVALID_ARGUMENT
+    st = lib.tsa_predict_mask(ctypes.byref(pr), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000),
+                              85, ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000), pw - 1, None)
+    assert st == T.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_maskgen_validation():
+    lib = T.lib()
+    pr = T.problem(1, 2, 512, 64, 16, 16)
+    g = T.MaskgenParams(1, (1 << 24) + 1, 0, 0, 0, 1)
+    assert lib.tsa_maskgen_hash(ctypes.byref(pr), ctypes.byref(g), ctypes.c_void_p(0x1000),
+                                None) == T.ERR_INVALID_ARGUMENT
+    assert lib.tsa_maskgen_hash(ctypes.byref(pr), None, ctypes.c_void_p(0x1000),
+                                None) == T.ERR_INVALID_ARGUMENT
+
+
+def test_status_strings():
+    assert T.status_string(T.OK) == "success"
+    assert T.status_string(T.ERR_HIP) == "HIP runtime error"
+    assert T.status_string(99) == "unknown status"
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(T, "_lib", None)
+    monkeypatch.setattr(T, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        T.lib()

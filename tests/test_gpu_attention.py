@@ -1,0 +1,114 @@
+"""GPU parity of the tile-sparse attention forward kernel against the fp64
+CPU oracle, through the C ABI, on seeded synthetic inputs."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import (compare, full_compare, gpu_attention, say, small_workload, to_dev_mask,
+                      torch_or_skip)
+
+pytestmark = pytest.mark.gpu
+
+
+def _hash_bits(w):
+    return W.mask_bits(w)
+
+
+def test_tiny_config_full():
+    torch_or_skip()
+    w = W.get("tiny")
+    full_compare(w, W.mask_bits(w), "tiny fp32 16x16 (full)")
+
+
+@pytest.mark.parametrize("M", [16, 32, 64])
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 16, 32, 64])
+def test_bf16_tile_grid_ragged(M, N):
+    torch_or_skip()
+    # L = 1000 leaves a partial last query tile for every M and a partial last
+    # key tile for N in {16, 32, 64}; 1000 is not a multiple of the key chunk.
+    w = small_workload(f"grid_{M}x{N}", 1000, 128, M, N, p=0.3, seed=100 + M + N)
+    full_compare(w, _hash_bits(w), f"bf16 d128 {M}x{N} L=1000")
+
+
+@pytest.mark.parametrize("dtype,d,N", [("f32", 128, 8), ("f32", 64, 1), ("f32", 64, 4),
+                                       ("bf16", 64, 8), ("bf16", 64, 1), ("f32", 128, 64)])
+def test_dtype_and_head_dim(dtype, d, N):
+    torch_or_skip()
+    w = small_workload(f"dt_{dtype}_{d}_{N}", 777, d, 16, N, dtype=dtype, p=0.4, seed=5 + d + N)
+    full_compare(w, _hash_bits(w), f"{dtype} d{d} 16x{N} L=777")
+
+
+@pytest.mark.parametrize("L", [1, 15, 17, 130, 257])
+def test_short_sequences(L):
+    torch_or_skip()
+    w = small_workload(f"short_{L}", L, 128, 16, 4, p=0.5, seed=L)
+    full_compare(w, _hash_bits(w), f"bf16 16x4 L={L}")
+
+
+def test_empty_mask_gives_zero_and_minus_inf():
+    torch = torch_or_skip()
+    w = small_workload("empty", 300, 128, 16, 8)
+    say("empty mask bf16 16x8 L=300")
+    q, k, v = W.make_qkv(w)
+    bits = np.zeros((1, 2, w.T_q, w.words), dtype=np.uint32)
+    o, lse = gpu_attention(q.cuda(), k.cuda(), v.cuda(), to_dev_mask(bits), 16, 8, w.scale)
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_padding_bits_are_ignored():
+    torch_or_skip()
+    w = small_workload("pad", 1000, 128, 16, 8, p=0.3, seed=3)     # T_k = 125: 3 padding bits
+    bits = W.mask_bits(w)
+    bits[..., -1] |= np.uint32(0xE0000000)
+    full_compare(w, bits, "bf16 16x8 padding bits set")
+
+
+def test_all_ones_and_diagonal_only():
+    torch_or_skip()
+    w = small_workload("ones", 700, 128, 16, 8, seed=11)
+    full_compare(w, W.pack_bits(np.ones((1, 2, w.T_q, w.T_k), dtype=bool)), "bf16 all-ones")
+    wd = w.replace(mask=W.MaskRecipe("diag_only"))
+    full_compare(wd, W.mask_bits(wd), "bf16 diagonal-only")
+
+
+def test_single_tile_rows_and_last_partial_tile():
+    torch_or_skip()
+    w = small_workload("single", 1000, 128, 16, 16, seed=13)
+    rng = np.random.default_rng(0)
+    keep = np.zeros((1, 2, w.T_q, w.T_k), dtype=bool)
+    for h in range(2):
+        for i in range(w.T_q):
+            keep[0, h, i, rng.integers(w.T_k)] = True
+        keep[0, h, ::3, w.T_k - 1] = True       # partial last key tile (8 keys)
+    full_compare(w, W.pack_bits(keep), "bf16 one tile per row + last partial key tile")
+
+
+def test_large_logits_are_stable():
+    torch = torch_or_skip()
+    w = small_workload("big", 600, 128, 16, 8, p=0.5, seed=17)
+    say("bf16 16x8 L=600 with Q scaled x8 (large logits)")
+    q, k, v = W.make_qkv(w)
+    q = (q.float() * 8).to(torch.bfloat16)
+    bits = W.mask_bits(w)
+    o, lse = gpu_attention(q.cuda(), k.cuda(), v.cuda(), to_dev_mask(bits), 16, 8, w.scale)
+    ro, rl = oracle.attention(q, k, v, bits, 16, 8, w.scale)
+    compare("large logits", o.float().cpu().numpy(), ro, "bf16", lse.cpu().numpy(), rl)
+
+
+def test_determinism():
+    torch = torch_or_skip()
+    w = small_workload("det", 2000, 128, 16, 8, p=0.3, seed=19)
+    say("determinism bf16 16x8 L=2000")
+    q, k, v = (x.cuda() for x in W.make_qkv(w))
+    m = to_dev_mask(W.mask_bits(w))
+    o1, l1 = gpu_attention(q, k, v, m, 16, 8, w.scale)
+    o2, l2 = gpu_attention(q, k, v, m, 16, 8, w.scale)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_multi_batch_heads():
+    torch_or_skip()
+    w = W.Workload("bh", 2, 3, 500, 128, 16, 8, "bf16",
+                   W.MaskRecipe("hash", p_near=0.35, p_far=0.35), 23)
+    full_compare(w, W.mask_bits(w), "bf16 B=2 H=3 16x8 L=500")

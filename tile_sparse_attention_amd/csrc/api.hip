@@ -1,0 +1,198 @@
+// C ABI of the tile-sparse attention library: argument validation, workspace
+// sizing, dispatch to the kernel launchers, and error reporting.  Nothing is
+// enqueued unless every check passes; no exception or abort crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+#include "tsa.h"
+#include "tsa_workload.h"
+
+namespace tsa {
+hipError_t launch_mask_compact(const tsa_problem_t* p, const uint32_t* mask, int64_t* row_ptr,
+                               int32_t* col_idx, int64_t col_capacity, void* workspace,
+                               hipStream_t stream);
+size_t mask_compact_workspace(const tsa_problem_t* p);
+hipError_t launch_predict_mask(const tsa_problem_t* p, const void* q, const void* k,
+                               int sparsity_percent, uint32_t* mask_out, void* workspace,
+                               hipStream_t stream);
+size_t predict_workspace(const tsa_problem_t* p);
+hipError_t launch_maskgen_hash(const tsa_problem_t* p, const tsa_maskgen_params_t* g,
+                               uint32_t* out, hipStream_t stream);
+}  // namespace tsa
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+tsa_status_t fail(tsa_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+tsa_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(TSA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+constexpr int kMaxL = 1 << 26;
+constexpr long long kMaxBH = 1 << 20;
+constexpr long long kMaxGrid = 0x7fffffffLL;
+
+// Shape checks common to every call.  need_d: check d and dtype.
+tsa_status_t check_problem(const tsa_problem_t* p, bool need_d) {
+  if (p == nullptr) return fail(TSA_ERR_INVALID_ARGUMENT, "problem is NULL");
+  if (p->B < 1 || p->H < 1 || p->L < 1 || p->M < 1 || p->N < 1 || (need_d && p->d < 1))
+    return fail(TSA_ERR_INVALID_ARGUMENT, "sizes must be positive (B=%d H=%d L=%d d=%d M=%d N=%d)",
+                p->B, p->H, p->L, p->d, p->M, p->N);
+  if (p->L > kMaxL) return fail(TSA_ERR_UNSUPPORTED, "L=%d exceeds %d", p->L, kMaxL);
+  if ((long long)p->B * p->H > kMaxBH)
+    return fail(TSA_ERR_UNSUPPORTED, "B*H=%lld exceeds %lld", (long long)p->B * p->H, kMaxBH);
+  if (!(p->M == 16 || p->M == 32 || p->M == 64))
+    return fail(TSA_ERR_UNSUPPORTED, "M=%d not in {16, 32, 64}", p->M);
+  if (!pow2_in(p->N, 1, 64))
+    return fail(TSA_ERR_UNSUPPORTED, "N=%d not in {1, 2, 4, 8, 16, 32, 64}", p->N);
+  if (need_d) {
+    if (!(p->d == 64 || p->d == 128)) return fail(TSA_ERR_UNSUPPORTED, "d=%d not in {64, 128}", p->d);
+    if (!(p->dtype == TSA_DTYPE_F32 || p->dtype == TSA_DTYPE_BF16))
+      return fail(TSA_ERR_UNSUPPORTED, "dtype=%d not supported", (int)p->dtype);
+  }
+  return TSA_OK;
+}
+
+long long n_rows(const tsa_problem_t* p) {
+  return (long long)p->B * p->H * ((p->L + p->M - 1) / p->M);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t tsa_mask_row_words(int32_t L, int32_t N) {
+  if (L < 1 || N < 1) return 0;
+  const int64_t T_k = ((int64_t)L + N - 1) / N;
+  return (T_k + 31) / 32;
+}
+
+tsa_status_t tsa_workspace_size(tsa_op_t op, const tsa_problem_t* p, size_t* bytes) {
+  if (bytes == nullptr) return fail(TSA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  tsa_status_t s;
+  switch (op) {
+    case TSA_OP_ATTENTION_FWD:
+      if ((s = check_problem(p, true)) != TSA_OK) return s;
+      *bytes = 0;
+      return TSA_OK;
+    case TSA_OP_MASK_COMPACT:
+      if ((s = check_problem(p, false)) != TSA_OK) return s;
+      *bytes = tsa::mask_compact_workspace(p);
+      return TSA_OK;
+    case TSA_OP_PREDICT_MASK:
+      if ((s = check_problem(p, true)) != TSA_OK) return s;
+      *bytes = tsa::predict_workspace(p);
+      return TSA_OK;
+  }
+  return fail(TSA_ERR_INVALID_ARGUMENT, "unknown op %d", (int)op);
+}
+
+tsa_status_t tsa_attention_fwd(const tsa_problem_t* p, const void* q, const void* k, const void* v,
+                               const uint32_t* mask_bits, float scale, void* o, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  tsa_status_t s = check_problem(p, true);
+  if (s != TSA_OK) return s;
+  if (!q || !k || !v || !mask_bits || !o)
+    return fail(TSA_ERR_INVALID_ARGUMENT, "q, k, v, mask_bits and o must be non-NULL");
+  if (!std::isfinite(scale)) return fail(TSA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(mask_bits, 4) || (lse && !aligned(lse, 4)))
+    return fail(TSA_ERR_INVALID_ARGUMENT, "q/k/v/o need 16-byte, mask/lse 4-byte alignment");
+  if (o == q || o == k || o == v) return fail(TSA_ERR_INVALID_ARGUMENT, "o aliases an input");
+  const long long blocks = (long long)p->B * p->H * ((p->L + 63) / 64);
+  if (blocks > kMaxGrid) return fail(TSA_ERR_UNSUPPORTED, "grid too large");
+  tsa::AttnLaunch a{p, q, k, v, mask_bits, scale, o, lse, static_cast<hipStream_t>(stream)};
+  const hipError_t e = p->dtype == TSA_DTYPE_BF16 ? tsa::launch_attention_bf16(a)
+                                                  : tsa::launch_attention_f32(a);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  return TSA_OK;
+}
+
+tsa_status_t tsa_mask_compact(const tsa_problem_t* p, const uint32_t* mask_bits, int64_t* row_ptr,
+                              int32_t* col_idx, int64_t col_capacity, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  tsa_status_t s = check_problem(p, false);
+  if (s != TSA_OK) return s;
+  if (!mask_bits || !row_ptr) return fail(TSA_ERR_INVALID_ARGUMENT, "mask_bits and row_ptr must be non-NULL");
+  if (col_capacity < 0) return fail(TSA_ERR_INVALID_ARGUMENT, "col_capacity < 0");
+  if (col_capacity > 0 && !col_idx) return fail(TSA_ERR_INVALID_ARGUMENT, "col_idx is NULL");
+  if (!aligned(mask_bits, 4) || !aligned(row_ptr, 8) || (col_idx && !aligned(col_idx, 4)))
+    return fail(TSA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+  if ((n_rows(p) + 3) / 4 > kMaxGrid) return fail(TSA_ERR_UNSUPPORTED, "too many rows");
+  const size_t need = tsa::mask_compact_workspace(p);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(TSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, 256-byte aligned (got %zu)",
+                need, workspace_bytes);
+  const hipError_t e = tsa::launch_mask_compact(p, mask_bits, row_ptr, col_idx, col_capacity,
+                                                 workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "compaction kernel launch");
+  return TSA_OK;
+}
+
+tsa_status_t tsa_predict_mask(const tsa_problem_t* p, const void* q, const void* k,
+                              int32_t sparsity_percent, uint32_t* mask_out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  tsa_status_t s = check_problem(p, true);
+  if (s != TSA_OK) return s;
+  if (!q || !k || !mask_out) return fail(TSA_ERR_INVALID_ARGUMENT, "q, k and mask_out must be non-NULL");
+  if (sparsity_percent < 0 || sparsity_percent >= 100)
+    return fail(TSA_ERR_INVALID_ARGUMENT, "sparsity_percent=%d outside [0, 100)", sparsity_percent);
+  if (!aligned(q, 4) || !aligned(k, 4) || !aligned(mask_out, 4))
+    return fail(TSA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+  const size_t need = tsa::predict_workspace(p);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(TSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, 256-byte aligned (got %zu)",
+                need, workspace_bytes);
+  const hipError_t e = tsa::launch_predict_mask(p, q, k, sparsity_percent, mask_out, workspace,
+                                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "predictor kernel launch");
+  return TSA_OK;
+}
+
+tsa_status_t tsa_maskgen_hash(const tsa_problem_t* p, const tsa_maskgen_params_t* g,
+                              uint32_t* mask_out, void* stream) {
+  tsa_status_t s = check_problem(p, false);
+  if (s != TSA_OK) return s;
+  if (!g || !mask_out) return fail(TSA_ERR_INVALID_ARGUMENT, "params and mask_out must be non-NULL");
+  if (g->frame_tokens < 0 || g->frame_radius < 0 || g->thr_near > (1u << 24) || g->thr_far > (1u << 24))
+    return fail(TSA_ERR_INVALID_ARGUMENT, "bad generator parameters");
+  const long long words = n_rows(p) * tsa_mask_row_words(p->L, p->N);
+  if ((words + 255) / 256 > kMaxGrid) return fail(TSA_ERR_UNSUPPORTED, "bitmap too large");
+  const hipError_t e = tsa::launch_maskgen_hash(p, g, mask_out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mask generator launch");
+  return TSA_OK;
+}
+
+const char* tsa_status_string(tsa_status_t s) {
+  switch (s) {
+    case TSA_OK: return "success";
+    case TSA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case TSA_ERR_UNSUPPORTED: return "unsupported problem";
+    case TSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case TSA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* tsa_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Instantiation table of the attention kernel for one element type.
+#pragma once
+
+#include "attention_fwd_impl.h"
+#include "launch.h"
+
+namespace tsa {
+
+template <typename T, int D, int N, int KC, int W>
+hipError_t launch_attn_cfg(const AttnLaunch& a) {
+  const tsa_problem_t& pr = *a.p;
+  AttnParams p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.mask = a.mask;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.H = pr.H;
+  p.L = pr.L;
+  p.M = pr.M;
+  p.T_q = (pr.L + pr.M - 1) / pr.M;
+  p.T_k = (pr.L + pr.N - 1) / pr.N;
+  p.words = (p.T_k + 31) / 32;
+  p.n_qblocks = (pr.L + 16 * W - 1) / (16 * W);
+  p.scale_log2 = a.scale * 1.4426950408889634f;
+  const long long blocks = (long long)pr.B * pr.H * p.n_qblocks;
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, N, KC, W>), dim3((unsigned)blocks), dim3(64 * W), 0,
+                     a.stream, p);
+  return hipGetLastError();
+}
+
+// Chunk size KC and waves per work-group W per (element type, head dim):
+// both keep the double-buffered K and V^T chunks within the 160 KB of LDS.
+template <typename T, int D> struct AttnShape;
+template <> struct AttnShape<bf16_t, 128> { static constexpr int KC = 128, W = 8; };
+template <> struct AttnShape<bf16_t, 64> { static constexpr int KC = 128, W = 8; };
+template <> struct AttnShape<float, 128> { static constexpr int KC = 64, W = 8; };
+template <> struct AttnShape<float, 64> { static constexpr int KC = 64, W = 4; };
+
+template <typename T, int D>
+hipError_t launch_attn_d(const AttnLaunch& a) {
+  constexpr int KC = AttnShape<T, D>::KC, W = AttnShape<T, D>::W;
+  switch (a.p->N) {
+    case 1: return launch_attn_cfg<T, D, 1, KC, W>(a);
+    case 2: return launch_attn_cfg<T, D, 2, KC, W>(a);
+    case 4: return launch_attn_cfg<T, D, 4, KC, W>(a);
+    case 8: return launch_attn_cfg<T, D, 8, KC, W>(a);
+    case 16: return launch_attn_cfg<T, D, 16, KC, W>(a);
+    case 32: return launch_attn_cfg<T, D, 32, KC, W>(a);
+    case 64: return launch_attn_cfg<T, D, 64, KC, W>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t launch_attn_t(const AttnLaunch& a) {
+  switch (a.p->d) {
+    case 64: return launch_attn_d<T, 64>(a);
+    case 128: return launch_attn_d<T, 128>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tsa

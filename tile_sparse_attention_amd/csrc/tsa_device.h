@@ -1,0 +1,80 @@
+// Device-side helpers shared by the tile-sparse attention kernels (gfx950).
+//
+// Wave64 throughout.  Matrix-core operand layouts used here (CDNA3/CDNA4
+// MFMA, 16x16 output block): for lane l, let g = l / 16 and n = l % 16;
+//   A (16 x K): lane holds row n, k-elements of group g;
+//   B (K x 16): lane holds column n, k-elements of group g;
+//   D (16 x 16, fp32): lane holds D[4g + i][n], i = 0..3.
+// Which k-values a group holds only has to agree between A and B, so every
+// kernel picks the k order that makes its loads contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef uint16_t bf16_t;  // storage type of bf16 elements in memory
+
+__device__ __forceinline__ int lane_id() {
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// Number of set bits of `m` strictly below this lane (wave64 prefix count).
+__device__ __forceinline__ uint32_t prefix_count64(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Wave-level compaction of one 64-tile window of a keep-bitmap row.
+// `bits` is wave-uniform: bit t keeps tile (base + t).  Every lane t whose bit
+// is set stores (base + t) at position `offset + (set bits below t)` through
+// `store(pos, value)`.  Returns the number of set bits.  The result list is
+// ascending because positions follow bit order.
+template <typename Store>
+__device__ __forceinline__ uint32_t wave_compact64(uint64_t bits, int base, uint32_t offset,
+                                                   Store&& store) {
+  const int t = lane_id();
+  if ((bits >> t) & 1ull) store(offset + prefix_count64(bits), base + t);
+  return (uint32_t)__builtin_popcountll(bits);
+}
+
+// Bits [first, first + count) of a bitmap row as a 64-bit value (count <= 64,
+// `first` a multiple of `count`, count a power of two).  Bits at or beyond
+// `valid` (the row's real tile count) are cleared.
+// Only words holding at least one valid bit are read.
+__device__ __forceinline__ uint64_t row_bits(const uint32_t* __restrict__ row, int first, int count,
+                                             int valid) {
+  const int room = valid - first;
+  if (room <= 0) return 0ull;
+  uint64_t b;
+  if (count <= 32) {
+    const uint32_t w = row[first >> 5];
+    const uint64_t lo = (uint64_t)(w >> (first & 31));
+    b = count == 32 ? lo : (lo & ((1ull << count) - 1ull));
+  } else {
+    b = (uint64_t)row[first >> 5];
+    if (room > 32) b |= (uint64_t)row[(first >> 5) + 1] << 32;
+  }
+  if (room < count) b &= (1ull << room) - 1ull;
+  return b;
+}
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t x) {
+  return __uint_as_float(((uint32_t)x) << 16);
+}
+
+// Exchange with the lane whose index differs in bit 4 / bit 5 (ds_bpermute).
+__device__ __forceinline__ float xor_lane16(float x) { return __shfl_xor(x, 16); }
+__device__ __forceinline__ float xor_lane32(float x) { return __shfl_xor(x, 32); }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace tsa

@@ -235,6 +235,17 @@ def _hash_rows(w: Workload, rows: np.ndarray) -> np.ndarray:
     return out
 
 
+def hash_params(w: Workload) -> dict:
+    """Parameters of the counter-based mask recipe, as the GPU generator takes them."""
+    m = w.mask
+    if m.kind != "hash":
+        raise ValueError(f"mask recipe {m.kind!r} is not counter-based")
+    return dict(state0=w.seed * 8 + 3, thr_near=prob_threshold(m.p_near),
+                thr_far=prob_threshold(m.p_far), frame_tokens=m.frame_tokens,
+                frame_radius=m.frame_radius if m.frame_tokens > 0 else 0,
+                force_diag=m.force_diag)
+
+
 def mask_rows_bool(w: Workload, rows) -> np.ndarray:
     """Keep bits (bool [n, T_k]) of the given (b, h, i) rows, for recipes that
     can be evaluated row by row (hash, ones, diag_only)."""
