@@ -12,20 +12,29 @@
 //   * Keys are streamed in chunks of KC keys.  The work-group stages each
 //     chunk once in LDS (K as rows, V transposed to [d][key]) with
 //     double-buffered, coalesced 16-byte global loads; every wave then reuses
-//     it.  K/V are read from HBM/L2 once per work-group instead of once per
+//     it, so K/V are read from HBM/L2 once per work-group, not once per
 //     query tile.
 //   * Per chunk each wave compacts its own mask bits into the list of kept
-//     key tiles (wave prefix count of the bitmap, the same routine the
-//     compaction kernel uses) and packs the kept keys densely into 16-key
-//     "slots".  Matrix-core work is spent only on kept keys: a skipped tile
-//     costs nothing beyond its mask bit, and kept tiles of any width N share
-//     MFMA blocks instead of padding each tile to 16 keys.
+//     key tiles (wave prefix count of the bitmap, the routine the compaction
+//     kernel also uses) and packs the kept keys densely into 16-key "slots".
+//     Matrix-core work is spent only on kept keys: a skipped tile costs its
+//     mask bit, and kept tiles of any width N share MFMA blocks instead of
+//     each being padded to 16 keys.
 //   * Scores are formed transposed, S^T = K Q^T (A = gathered K rows from LDS,
 //     B = the wave's Q fragment held in registers), so each lane owns one
-//     query column; the online softmax (running max m and sum l, base-2
-//     exponent with scale*log2(e) folded in) is lane-local apart from a
-//     4-lane-group max.  The S^T accumulator layout is directly the B operand
-//     of O^T += V^T P^T, so probabilities never leave registers.
+//     query column and the S^T accumulator layout is directly the B operand of
+//     O^T += V^T P^T: probabilities never leave registers.
+//   * Padding slots need no per-score masking: for QK^T they read a kept key
+//     of the same row (so the running max only ever sees real kept scores),
+//     for PV they read zero columns of the LDS V^T tile.  Keys past L read as
+//     zero V columns as well.  The softmax denominator comes out of the
+//     matrix cores too: V^T carries one extra row of ones (zero past L and in
+//     the padding columns), so l = P . 1 accumulates with O.
+//   * Online softmax in base 2 with scale*log2(e) folded into one FMA per
+//     score; the reference max is raised (and O, l rescaled) only when some
+//     row's max grows by more than 2^8, a wave-uniform decision, so most
+//     passes do no rescaling.  The result O / l is unchanged by the choice of
+//     reference.
 //   * Normalisation O = O / l (0 for a row with nothing kept) and the store
 //     happen once at the end.
 #pragma once
@@ -59,7 +68,9 @@ struct AttnCfg {
   static constexpr int NSLAB = D / SLAB;
   static constexpr int NDB = D / 16;               // 16-wide d blocks of O^T
   static constexpr int KSTR = D + VEC;             // K row stride in LDS (+16 B against bank conflicts)
-  static constexpr int VSTR = KC + VEC;            // V^T row stride in LDS (+16 B)
+  static constexpr int VSTR = KC + VEC;            // V^T row stride in LDS; columns KC.. are zero
+  static constexpr int VROWS = D + 1;              // V^T rows: d = 0..D-1 and the ones row
+  static constexpr int ZCOL = KC;                  // first zero column of V^T
   static constexpr int NT = 64 * W;
   static constexpr int CPR = D / VEC;              // 16-byte chunks per K/V row
   static constexpr int K_ITEMS = KC * CPR;
@@ -69,11 +80,13 @@ struct AttnCfg {
   static constexpr int TPC = KC / N;               // key tiles per chunk
   static constexpr int WINT = TPC < 64 ? TPC : 64; // tiles per compaction window
   static constexpr int NWIN = TPC / WINT;
+  static constexpr int MW = TPC >= 32 ? TPC / 32 : 1;  // mask words per chunk
   static constexpr int LOG2N = ilog2(N);
-  static constexpr int PASS_SB = 4;                // 16-slot sub-blocks per softmax pass
+  static constexpr int MAXSB = KC / 16;            // 16-slot sub-blocks per chunk
   static_assert(D % SLAB == 0 && D % 16 == 0, "head dim");
-  static_assert(KC % N == 0 && KC % 64 == 0 && TPC <= 256, "chunk");
+  static_assert(KC % N == 0 && KC % 64 == 0 && TPC <= 256 && MW <= 4, "chunk");
   static_assert((1 << LOG2N) == N, "N must be a power of two");
+  static_assert(VEC >= 4, "zero columns must cover a quad of keys");
 };
 
 template <typename T> struct Mma;
@@ -98,67 +111,49 @@ template <> struct Mma<float> {
 };
 
 template <typename T, int D, int N, int KC, int W>
-__global__ __launch_bounds__(64 * W) void attn_fwd_kernel(AttnParams p) {
+struct AttnKernel {
   using C = AttnCfg<T, D, N, KC, W>;
-  constexpr int VEC = C::VEC;
+  static constexpr int VEC = C::VEC;
+  static constexpr float RESCALE_STEP = 8.f;  // log2 units a row max may grow before rescaling
 
-  __shared__ __attribute__((aligned(16))) T k_lds[2][KC * C::KSTR];
-  __shared__ __attribute__((aligned(16))) T vt_lds[2][D * C::VSTR];
-  __shared__ uint8_t tlist[W][C::TPC];
+  struct Smem {
+    T k[2][KC * C::KSTR];
+    T vt[2][C::VROWS * C::VSTR];
+    uint8_t tl[W][C::TPC];
+  };
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int g = lane >> 4;
-  const int n = lane & 15;
-  const int wave = wave_uniform(tid >> 6);
-
-  const int bh = blockIdx.x / p.n_qblocks;
-  const int qb = blockIdx.x - bh * p.n_qblocks;
-  const int L = p.L;
-  const size_t head_off = (size_t)bh * (size_t)L * D;
-  const T* __restrict__ qg = reinterpret_cast<const T*>(p.q) + head_off;
-  const T* __restrict__ kg = reinterpret_cast<const T*>(p.k) + head_off;
-  const T* __restrict__ vg = reinterpret_cast<const T*>(p.v) + head_off;
-
-  const int row0 = qb * (16 * W) + 16 * wave;  // first query row of this wave
-  const bool wave_active = row0 < L;
-  const int mrow = row0 / p.M;
-  const uint32_t* __restrict__ mask_row =
-      p.mask + ((size_t)bh * p.T_q + (size_t)(wave_active ? mrow : 0)) * p.words;
-
-  // ---- Q fragment: lane (g, n) holds Q[row0+n][SLAB*s + VEC*g .. +VEC) ----
+  // ---- per-wave state ----
+  const AttnParams& p;
+  Smem& sm;
+  int tid, lane, g, n, wave;
+  int L, bh, row0;
+  bool active;
+  const T* __restrict__ kg;
+  const T* __restrict__ vg;
+  const uint32_t* __restrict__ mask_row;
   u32x4 qf[C::NSLAB];
-  {
-    const int r = row0 + n;
-#pragma unroll
-    for (int s = 0; s < C::NSLAB; ++s) {
-      if (r < L)
-        qf[s] = *reinterpret_cast<const u32x4*>(qg + (size_t)r * D + C::SLAB * s + VEC * g);
-      else
-        qf[s] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
-  f32x4 oacc[C::NDB];
-#pragma unroll
-  for (int j = 0; j < C::NDB; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max of scaled (log2-domain) scores of query n
-  float l_run = 0.f;        // this lane group's share of the running sum
-
-  // ---- chunk staging: global -> registers -> LDS ----
+  f32x4 oacc[C::NDB + 1];  // O^T blocks and, last, the row sums l
+  float m_run;             // reference max (log2 domain) of query n
   u32x4 kreg[C::K_PER_T];
   u32x4 vreg[C::V_PER_T][4];
 
-  auto load_chunk = [&](int c) {
+  __device__ __forceinline__ AttnKernel(const AttnParams& pp, Smem& s) : p(pp), sm(s) {}
+
+  __device__ __forceinline__ int tl_at(int idx) const { return (int)sm.tl[wave][idx]; }
+
+  // Global -> registers for chunk c (K rows, V rows, this wave's mask words).
+  __device__ __forceinline__ void load_chunk(int c, uint32_t (&mreg)[C::MW]) {
     const int kbase = c * KC;
+    const bool full = kbase + KC <= L;
 #pragma unroll
     for (int u = 0; u < C::K_PER_T; ++u) {
       const int idx = tid + u * C::NT;
       if (C::K_ITEMS % C::NT == 0 || idx < C::K_ITEMS) {
         const int row = idx / C::CPR, ch = idx % C::CPR;
         const int key = kbase + row;
-        kreg[u] = key < L ? *reinterpret_cast<const u32x4*>(kg + (size_t)key * D + ch * VEC)
-                          : u32x4{0u, 0u, 0u, 0u};
+        const int kc = full ? key : (key < L ? key : L - 1);
+        kreg[u] = *reinterpret_cast<const u32x4*>(kg + (size_t)kc * D + ch * VEC);
+        if (!full && key >= L) kreg[u] = u32x4{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
@@ -169,20 +164,29 @@ __global__ __launch_bounds__(64 * W) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = kbase + 4 * rg + r;
-          vreg[u][r] = key < L ? *reinterpret_cast<const u32x4*>(vg + (size_t)key * D + ch * VEC)
-                               : u32x4{0u, 0u, 0u, 0u};
+          const int kc = full ? key : (key < L ? key : L - 1);
+          vreg[u][r] = *reinterpret_cast<const u32x4*>(vg + (size_t)kc * D + ch * VEC);
+          if (!full && key >= L) vreg[u][r] = u32x4{0u, 0u, 0u, 0u};
         }
       }
     }
-  };
+    // mask words holding key tiles [c*TPC, c*TPC + TPC) of this wave's row
+    const int w0 = (c * C::TPC) >> 5;
+#pragma unroll
+    for (int i = 0; i < C::MW; ++i) {
+      const int wi = w0 + i < p.words ? w0 + i : p.words - 1;
+      mreg[i] = mask_row[wi];
+    }
+  }
 
-  auto store_chunk = [&](int buf) {
+  // Registers -> LDS buffer `buf` for chunk c (V transposed; ones row).
+  __device__ __forceinline__ void store_chunk(int c, int buf) {
 #pragma unroll
     for (int u = 0; u < C::K_PER_T; ++u) {
       const int idx = tid + u * C::NT;
       if (C::K_ITEMS % C::NT == 0 || idx < C::K_ITEMS) {
         const int row = idx / C::CPR, ch = idx % C::CPR;
-        *reinterpret_cast<u32x4*>(&k_lds[buf][row * C::KSTR + ch * VEC]) = kreg[u];
+        *reinterpret_cast<u32x4*>(&sm.k[buf][row * C::KSTR + ch * VEC]) = kreg[u];
       }
     }
 #pragma unroll
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(64 * W) void attn_fwd_kernel(AttnParams p) {
       const int idx = tid + u * C::NT;
       if (C::V_ITEMS % C::NT == 0 || idx < C::V_ITEMS) {
         const int rg = idx / C::CPR, ch = idx % C::CPR;
-        T* dst = &vt_lds[buf][(ch * VEC) * C::VSTR + 4 * rg];
+        T* dst = &sm.vt[buf][(ch * VEC) * C::VSTR + 4 * rg];
         const u32x4 r0 = vreg[u][0], r1 = vreg[u][1], r2 = vreg[u][2], r3 = vreg[u][3];
         if constexpr (sizeof(T) == 2) {
           // word w of a row holds d = 2w (low half) and 2w+1 (high half)
@@ -209,215 +213,299 @@ __global__ __launch_bounds__(64 * W) void attn_fwd_kernel(AttnParams p) {
         }
       }
     }
-  };
-
-  // key offset (within the chunk) of packed slot s, given this wave's tile list
-  uint8_t* tl = tlist[wave];
-  auto slot_key = [&](int s) -> int {
-    if constexpr (N == 1) return (int)tl[s];
-    else return ((int)tl[s >> C::LOG2N] << C::LOG2N) | (s & (N - 1));
-  };
-
-  // Four consecutive slots s0..s0+3 of V^T row `vrow` (all valid slots or
-  // all dummies when N >= 4; dummies read key 0 and are multiplied by p = 0).
-  auto vt_quad = [&](const T* vrow, int s0, int nslots) -> u32x4 {
-    if constexpr (N >= 4) {
-      const int key = s0 < nslots ? slot_key(s0) : 0;
+    // ones row: 1 for keys < L, 0 past L
+    if (tid < KC / VEC) {
+      const int k0 = c * KC + tid * VEC;
+      u32x4 v;
       if constexpr (sizeof(T) == 2) {
-        const u32x2 x = *reinterpret_cast<const u32x2*>(vrow + key);
-        return u32x4{x[0], x[1], 0u, 0u};
-      } else {
-        return *reinterpret_cast<const u32x4*>(vrow + key);
-      }
-    } else if constexpr (N == 2) {
-      const int k0 = s0 < nslots ? slot_key(s0) : 0;
-      const int k1 = s0 + 2 < nslots ? slot_key(s0 + 2) : 0;
-      if constexpr (sizeof(T) == 2) {
-        return u32x4{*reinterpret_cast<const uint32_t*>(vrow + k0),
-                     *reinterpret_cast<const uint32_t*>(vrow + k1), 0u, 0u};
-      } else {
-        const u32x2 a = *reinterpret_cast<const u32x2*>(vrow + k0);
-        const u32x2 b = *reinterpret_cast<const u32x2*>(vrow + k1);
-        return u32x4{a[0], a[1], b[0], b[1]};
-      }
-    } else {
-      int kk[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) kk[e] = s0 + e < nslots ? slot_key(s0 + e) : 0;
-      if constexpr (sizeof(T) == 2) {
-        const uint32_t e0 = reinterpret_cast<const uint16_t*>(vrow)[kk[0]];
-        const uint32_t e1 = reinterpret_cast<const uint16_t*>(vrow)[kk[1]];
-        const uint32_t e2 = reinterpret_cast<const uint16_t*>(vrow)[kk[2]];
-        const uint32_t e3 = reinterpret_cast<const uint16_t*>(vrow)[kk[3]];
-        return u32x4{e0 | (e1 << 16), e2 | (e3 << 16), 0u, 0u};
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t lo = k0 + 2 * w < L ? 0x3f80u : 0u;
+          const uint32_t hi = k0 + 2 * w + 1 < L ? 0x3f800000u : 0u;
+          v[w] = lo | hi;
+        }
       } else {
-        const uint32_t* vr = reinterpret_cast<const uint32_t*>(vrow);
-        return u32x4{vr[kk[0]], vr[kk[1]], vr[kk[2]], vr[kk[3]]};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) v[w] = k0 + w < L ? 0x3f800000u : 0u;
+      }
+      *reinterpret_cast<u32x4*>(&sm.vt[buf][D * C::VSTR + tid * VEC]) = v;
+    }
+  }
+
+  // Zero the V^T padding columns (read by padding slots) of both buffers.
+  __device__ __forceinline__ void zero_pad_columns() {
+    for (int r = tid; r < 2 * C::VROWS; r += C::NT) {
+      const int buf = r / C::VROWS, row = r % C::VROWS;
+      *reinterpret_cast<u32x4*>(&sm.vt[buf][row * C::VSTR + KC]) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // Four consecutive V^T elements for slots s0..s0+3 (N >= 4: one read).
+  __device__ __forceinline__ u32x2 vt_quad_b16(const T* vrow, int s0, int nslots) const {
+    if constexpr (N >= 4) {
+      const int s = s0 < nslots ? s0 : 0;
+      const int kk = (tl_at(s >> C::LOG2N) << C::LOG2N) | (s & (N - 1));
+      return *reinterpret_cast<const u32x2*>(vrow + (s0 < nslots ? kk : C::ZCOL));
+    } else if constexpr (N == 2) {
+      int kk[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int s = s0 + 2 * e;
+        const int t = tl_at(s < nslots ? (s >> 1) : 0) << 1;
+        kk[e] = s < nslots ? t : C::ZCOL;
+      }
+      return u32x2{*reinterpret_cast<const uint32_t*>(vrow + kk[0]),
+                   *reinterpret_cast<const uint32_t*>(vrow + kk[1])};
+    } else {
+      uint32_t e4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = s0 + e;
+        const int t = tl_at(s < nslots ? s : 0);
+        e4[e] = reinterpret_cast<const uint16_t*>(vrow)[s < nslots ? t : C::ZCOL];
+      }
+      return u32x2{e4[0] | (e4[1] << 16), e4[2] | (e4[3] << 16)};
+    }
+  }
+
+  __device__ __forceinline__ u32x4 vt_quad_f32(const T* vrow, int s0, int nslots) const {
+    if constexpr (N >= 4) {
+      const int s = s0 < nslots ? s0 : 0;
+      const int kk = (tl_at(s >> C::LOG2N) << C::LOG2N) | (s & (N - 1));
+      return *reinterpret_cast<const u32x4*>(vrow + (s0 < nslots ? kk : C::ZCOL));
+    } else if constexpr (N == 2) {
+      u32x2 a[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int s = s0 + 2 * e;
+        const int t = tl_at(s < nslots ? (s >> 1) : 0) << 1;
+        a[e] = *reinterpret_cast<const u32x2*>(vrow + (s < nslots ? t : C::ZCOL));
+      }
+      return u32x4{a[0][0], a[0][1], a[1][0], a[1][1]};
+    } else {
+      u32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = s0 + e;
+        const int t = tl_at(s < nslots ? s : 0);
+        r[e] = reinterpret_cast<const uint32_t*>(vrow)[s < nslots ? t : C::ZCOL];
+      }
+      return r;
+    }
+  }
+
+  // One softmax pass over NSB sub-blocks of 16 slots starting at sub-block sb0.
+  template <int NSB>
+  __device__ __forceinline__ void pass(const T* kl, const T* vl, int sb0, int nslots, int lim,
+                                       int key0) {
+    // QK^T A rows: a padding slot reads the first kept key; a key past L the
+    // start of its (kept) tile.  Either way the score is a real kept score.
+    int ka[NSB];
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+      const int slot = 16 * (sb0 + sb) + n;
+      const int sc = slot < nslots ? slot : 0;
+      const int t = tl_at(sc >> C::LOG2N) << C::LOG2N;
+      int key = t | (sc & (N - 1));
+      key = key < lim ? key : t;
+      key = slot < nslots ? key : key0;
+      ka[sb] = key * C::KSTR + VEC * g;
+    }
+    f32x4 s[NSB];
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sl = 0; sl < C::NSLAB; ++sl) {
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kl + ka[sb] + C::SLAB * sl);
+        if constexpr (sizeof(T) == 2) s[sb] = Mma<bf16_t>::mac8(a, qf[sl], s[sb]);
+        else s[sb] = Mma<float>::mac4(a, qf[sl], s[sb]);
       }
     }
-  };
+    // running max in the log2 domain (scale may be negative)
+    const float c = p.scale_log2;
+    float mr = s[0][0];
+    if (c >= 0.f) {
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mr = fmaxf(mr, s[sb][i]);
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mr = fminf(mr, s[sb][i]);
+    }
+    float mx = c * mr;
+    mx = fmaxf(mx, xor_lane16(mx));
+    mx = fmaxf(mx, xor_lane32(mx));
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_STEP) != 0ull) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2_fast(m_run - m_new);  // 0 on the first pass
+      m_run = m_new;
+#pragma unroll
+      for (int j = 0; j <= C::NDB; ++j) oacc[j] *= alpha;
+    }
+    const float nm = -m_run;
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[sb][i] = exp2_fast(__builtin_fmaf(s[sb][i], c, nm));
+    // O^T += V^T P^T (and l += P . 1 through the ones row)
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int pp = 0; pp < (NSB + 1) / 2; ++pp) {
+        const int a0 = 2 * pp, a1 = 2 * pp + 1;
+        bf16x8 pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[i] = (__bf16)s[a0][i];
+          pb[4 + i] = a1 < NSB ? (__bf16)s[a1 < NSB ? a1 : a0][i] : (__bf16)0.f;
+        }
+        const u32x4 bop = __builtin_bit_cast(u32x4, pb);
+        const int sA = 16 * (sb0 + a0) + 4 * g;
+        const int sB = a1 < NSB ? 16 * (sb0 + a1) + 4 * g : nslots;
+#pragma unroll
+        for (int j = 0; j <= C::NDB; ++j) {
+          const T* vrow = vl + (j < C::NDB ? 16 * j + n : D) * C::VSTR;
+          const u32x2 x0 = vt_quad_b16(vrow, sA, nslots);
+          const u32x2 x1 = vt_quad_b16(vrow, sB, nslots);
+          oacc[j] = Mma<bf16_t>::mac8(u32x4{x0[0], x0[1], x1[0], x1[1]}, bop, oacc[j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+        const u32x4 bop = __builtin_bit_cast(u32x4, s[sb]);
+        const int sA = 16 * (sb0 + sb) + 4 * g;
+#pragma unroll
+        for (int j = 0; j <= C::NDB; ++j) {
+          const T* vrow = vl + (j < C::NDB ? 16 * j + n : D) * C::VSTR;
+          oacc[j] = Mma<float>::mac4(vt_quad_f32(vrow, sA, nslots), bop, oacc[j]);
+        }
+      }
+    }
+  }
 
-  auto compute_chunk = [&](int c, int buf) {
+  __device__ __forceinline__ void compute_chunk(int c, int buf, const uint32_t (&mreg)[C::MW]) {
     // -- compaction of this wave's mask bits for the chunk's key tiles --
+    const int first = c * C::TPC;
     uint32_t nk = 0;
 #pragma unroll
     for (int win = 0; win < C::NWIN; ++win) {
-      const uint64_t bits = row_bits(mask_row, c * C::TPC + win * C::WINT, C::WINT, p.T_k);
+      uint64_t bits;
+      if constexpr (C::WINT == 64) {
+        bits = (uint64_t)uniform_u32(mreg[2 * win]) | ((uint64_t)uniform_u32(mreg[2 * win + 1]) << 32);
+      } else {
+        const uint32_t w = uniform_u32(mreg[0]) >> (first & 31);
+        bits = C::WINT == 32 ? (uint64_t)w : (uint64_t)(w & ((1u << C::WINT) - 1u));
+      }
+      const int room = p.T_k - first - win * C::WINT;  // valid tiles left in the row
+      if (room < C::WINT) bits = room <= 0 ? 0ull : (bits & ((1ull << room) - 1ull));
       nk += wave_compact64(bits, win * C::WINT, nk,
-                           [&](uint32_t pos, int val) { tl[pos] = (uint8_t)val; });
+                           [&](uint32_t pos, int val) { sm.tl[wave][pos] = (uint8_t)val; });
     }
-    const int nslots = wave_uniform((int)nk * N);
+    const int nslots = (int)nk * N;
     if (nslots == 0) return;
     __builtin_amdgcn_wave_barrier();
-
-    const T* kl = k_lds[buf];
-    const T* vl = vt_lds[buf];
-    const int kbase = c * KC;
+    const T* kl = sm.k[buf];
+    const T* vl = sm.vt[buf];
+    const int lim = L - c * KC;              // keys of this chunk that exist
+    const int key0 = tl_at(0) << C::LOG2N;   // first kept key of the chunk
     const int nsb = (nslots + 15) >> 4;
+    int sb0 = 0;
+    for (; sb0 + 4 <= nsb; sb0 += 4) pass<4>(kl, vl, sb0, nslots, lim, key0);
+    const int rem = nsb - sb0;
+    if (rem == 3) pass<3>(kl, vl, sb0, nslots, lim, key0);
+    else if (rem == 2) pass<2>(kl, vl, sb0, nslots, lim, key0);
+    else if (rem == 1) pass<1>(kl, vl, sb0, nslots, lim, key0);
+  }
 
-    for (int p0 = 0; p0 < nsb; p0 += C::PASS_SB) {
-      const int nsbp = nsb - p0 < C::PASS_SB ? nsb - p0 : C::PASS_SB;
-      f32x4 s[C::PASS_SB];
-      // -- S^T = K Q^T for up to PASS_SB blocks of 16 slots --
+  __device__ __forceinline__ void run() {
+    tid = threadIdx.x;
+    lane = tid & 63;
+    g = lane >> 4;
+    n = lane & 15;
+    wave = wave_uniform(tid >> 6);
+    bh = blockIdx.x / p.n_qblocks;
+    const int qb = blockIdx.x - bh * p.n_qblocks;
+    L = p.L;
+    const size_t head_off = (size_t)bh * (size_t)L * D;
+    const T* __restrict__ qg = reinterpret_cast<const T*>(p.q) + head_off;
+    kg = reinterpret_cast<const T*>(p.k) + head_off;
+    vg = reinterpret_cast<const T*>(p.v) + head_off;
+    row0 = qb * (16 * W) + 16 * wave;
+    active = row0 < L;
+    const int mrow = active ? row0 / p.M : 0;
+    mask_row = p.mask + ((size_t)bh * p.T_q + (size_t)mrow) * p.words;
+
+    // Q fragment: lane (g, n) holds Q[row0+n][SLAB*s + VEC*g .. +VEC)
+    {
+      const int r = row0 + n < L ? row0 + n : L - 1;
 #pragma unroll
-      for (int sb = 0; sb < C::PASS_SB; ++sb) {
-        s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (sb < nsbp) {
-          const int slot = (p0 + sb) * 16 + n;
-          const int key = slot < nslots ? slot_key(slot) : 0;
-          const T* krow = kl + key * C::KSTR + VEC * g;
+      for (int s = 0; s < C::NSLAB; ++s)
+        qf[s] = *reinterpret_cast<const u32x4*>(qg + (size_t)r * D + C::SLAB * s + VEC * g);
+      if (row0 + n >= L)
 #pragma unroll
-          for (int sl = 0; sl < C::NSLAB; ++sl) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(krow + C::SLAB * sl);
-            if constexpr (sizeof(T) == 2) s[sb] = Mma<bf16_t>::mac8(a, qf[sl], s[sb]);
-            else s[sb] = Mma<float>::mac4(a, qf[sl], s[sb]);
-          }
-        }
-      }
-      // -- mask, scale to log2 domain, running max --
-      float mx = -INFINITY;
-#pragma unroll
-      for (int sb = 0; sb < C::PASS_SB; ++sb) {
-        if (sb < nsbp) {
-          const int s0 = (p0 + sb) * 16 + 4 * g;
-          // keys left in the sequence after this quad's first key (<= 0: none)
-          const int room = N >= 4 ? (s0 < nslots ? L - kbase - slot_key(s0) : 0) : 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            bool ok;
-            if constexpr (N >= 4) {
-              ok = i < room;
-            } else {
-              ok = s0 + i < nslots && kbase + slot_key(s0 + i) < L;
-            }
-            const float t = ok ? s[sb][i] * p.scale_log2 : -INFINITY;
-            s[sb][i] = t;
-            mx = fmaxf(mx, t);
-          }
-        }
-      }
-      mx = fmaxf(mx, xor_lane16(mx));
-      mx = fmaxf(mx, xor_lane32(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int j = 0; j < C::NDB; ++j) oacc[j] *= alpha;
-#pragma unroll
-      for (int sb = 0; sb < C::PASS_SB; ++sb) {
-        if (sb < nsbp) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float e = exp2_fast(s[sb][i] - m_use);
-            s[sb][i] = e;
-            l_run += e;
-          }
-        }
-      }
-      // -- O^T += V^T P^T --
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int pp = 0; pp < C::PASS_SB / 2; ++pp) {
-          const int sb0 = 2 * pp, sb1 = 2 * pp + 1;
-          if (sb0 < nsbp) {
-            const bool has1 = sb1 < nsbp;
-            bf16x8 pb;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              pb[i] = (__bf16)s[sb0][i];
-              pb[4 + i] = (__bf16)(has1 ? s[sb1][i] : 0.f);
-            }
-            const u32x4 bop = __builtin_bit_cast(u32x4, pb);
-            const int sA = (p0 + sb0) * 16 + 4 * g;
-            const int sB = has1 ? (p0 + sb1) * 16 + 4 * g : nslots;  // dummy when absent
-#pragma unroll
-            for (int j = 0; j < C::NDB; ++j) {
-              const T* vrow = vl + (16 * j + n) * C::VSTR;
-              const u32x4 x0 = vt_quad(vrow, sA, nslots);
-              const u32x4 x1 = vt_quad(vrow, sB, nslots);
-              const u32x4 a = {x0[0], x0[1], x1[0], x1[1]};
-              oacc[j] = Mma<bf16_t>::mac8(a, bop, oacc[j]);
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int sb = 0; sb < C::PASS_SB; ++sb) {
-          if (sb < nsbp) {
-            const u32x4 bop = __builtin_bit_cast(u32x4, s[sb]);
-            const int sA = (p0 + sb) * 16 + 4 * g;
-#pragma unroll
-            for (int j = 0; j < C::NDB; ++j) {
-              const T* vrow = vl + (16 * j + n) * C::VSTR;
-              oacc[j] = Mma<float>::mac4(vt_quad(vrow, sA, nslots), bop, oacc[j]);
-            }
-          }
-        }
-      }
+        for (int s = 0; s < C::NSLAB; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
     }
-  };
+#pragma unroll
+    for (int j = 0; j <= C::NDB; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
 
-  // ---- main loop over key chunks (double-buffered LDS) ----
-  const int n_chunks = (L + KC - 1) / KC;
-  load_chunk(0);
-  store_chunk(0);
-  __syncthreads();
-  for (int c = 0; c < n_chunks; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < n_chunks;
-    if (more) load_chunk(c + 1);
-    if (wave_active) compute_chunk(c, buf);
-    if (more) store_chunk(buf ^ 1);
+    zero_pad_columns();
+    const int n_chunks = (L + KC - 1) / KC;
+    uint32_t mcur[C::MW], mnext[C::MW];
+    load_chunk(0, mcur);
+    store_chunk(0, 0);
     __syncthreads();
-  }
+    for (int c = 0; c < n_chunks; ++c) {
+      const int buf = c & 1;
+      const bool more = c + 1 < n_chunks;
+      if (more) load_chunk(c + 1, mnext);
+      if (active) compute_chunk(c, buf, mcur);
+      if (more) {
+        store_chunk(c + 1, buf ^ 1);
+#pragma unroll
+        for (int i = 0; i < C::MW; ++i) mcur[i] = mnext[i];
+      }
+      __syncthreads();
+    }
 
-  // ---- normalise and store ----
-  if (!wave_active) return;
-  float l_tot = l_run + xor_lane16(l_run);
-  l_tot += xor_lane32(l_tot);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const int r = row0 + n;
-  if (r < L) {
-    T* og = reinterpret_cast<T*>(p.o) + head_off + (size_t)r * D;
+    // normalise and store
+    if (!active) return;
+    const float l_tot = oacc[C::NDB][0];
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int r = row0 + n;
+    if (r < L) {
+      T* og = reinterpret_cast<T*>(p.o) + head_off + (size_t)r * D;
 #pragma unroll
-    for (int j = 0; j < C::NDB; ++j) {
-      const f32x4 val = oacc[j] * inv;
-      if constexpr (sizeof(T) == 2) {
-        bf16x4 ob;
+      for (int j = 0; j < C::NDB; ++j) {
+        const f32x4 val = oacc[j] * inv;
+        if constexpr (sizeof(T) == 2) {
+          bf16x4 ob;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ob[i] = (__bf16)val[i];
-        *reinterpret_cast<u32x2*>(og + 16 * j + 4 * g) = __builtin_bit_cast(u32x2, ob);
-      } else {
-        *reinterpret_cast<f32x4*>(og + 16 * j + 4 * g) = val;
+          for (int i = 0; i < 4; ++i) ob[i] = (__bf16)val[i];
+          *reinterpret_cast<u32x2*>(og + 16 * j + 4 * g) = __builtin_bit_cast(u32x2, ob);
+        } else {
+          *reinterpret_cast<f32x4*>(og + 16 * j + 4 * g) = val;
+        }
+      }
+      if (p.lse != nullptr && g == 0) {
+        p.lse[(size_t)bh * L + r] =
+            l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
       }
     }
-    if (p.lse != nullptr && g == 0) {
-      p.lse[(size_t)bh * L + r] =
-          l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-    }
   }
+};
+
+template <typename T, int D, int N, int KC, int W>
+__global__ __launch_bounds__(64 * W) void attn_fwd_kernel(AttnParams p) {
+  using K = AttnKernel<T, D, N, KC, W>;
+  __shared__ __attribute__((aligned(16))) typename K::Smem sm;
+  K k(p, sm);
+  k.run();
 }
 
 }  // namespace tsa

@@ -33,6 +33,11 @@ __device__ __forceinline__ uint32_t prefix_count64(uint64_t m) {
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Lane 0's value of a 32-bit word, zero-extended (readfirstlane is int-typed).
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+
 // Wave-level compaction of one 64-tile window of a keep-bitmap row.
 // `bits` is wave-uniform: bit t keeps tile (base + t).  Every lane t whose bit
 // is set stores (base + t) at position `offset + (set bits below t)` through
