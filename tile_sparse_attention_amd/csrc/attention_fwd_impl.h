@@ -68,7 +68,8 @@ struct AttnCfg {
   static constexpr int NSLAB = D / SLAB;
   static constexpr int NDB = D / 16;               // 16-wide d blocks of O^T
   static constexpr int KSTR = D + VEC;             // K row stride in LDS (+16 B against bank conflicts)
-  static constexpr int VSTR = KC + VEC;            // V^T row stride in LDS; columns KC.. are zero
+  static constexpr int VPAD = 4;                   // zero columns after the KC keys of a V^T row
+  static constexpr int VSTR = KC + VPAD;           // V^T row stride: 264 B (bf16) / 272 B (fp32)
   static constexpr int VROWS = D + 1;              // V^T rows: d = 0..D-1 and the ones row
   static constexpr int ZCOL = KC;                  // first zero column of V^T
   static constexpr int NT = 64 * W;
@@ -86,7 +87,9 @@ struct AttnCfg {
   static_assert(D % SLAB == 0 && D % 16 == 0, "head dim");
   static_assert(KC % N == 0 && KC % 64 == 0 && TPC <= 256 && MW <= 4, "chunk");
   static_assert((1 << LOG2N) == N, "N must be a power of two");
-  static_assert(VEC >= 4, "zero columns must cover a quad of keys");
+  // V staging: a wave covers 16 consecutive key quads x 4 16-byte d chunks
+  static constexpr int VQ = KC / 4;                // key quads per chunk
+  static_assert(VQ % 16 == 0 && CPR % 4 == 0, "V staging tile");
 };
 
 template <typename T> struct Mma;
@@ -141,32 +144,65 @@ struct AttnKernel {
 
   __device__ __forceinline__ int tl_at(int idx) const { return (int)sm.tl[wave][idx]; }
 
+  // V staging item -> (key quad rg, 16-byte d chunk ch).  Lane l of a wave
+  // takes quad (l % 16) and chunk (l / 16) of the wave's 16 x 4 block, so the
+  // 16 lanes writing one V^T row write 128 contiguous bytes.
+  __device__ __forceinline__ void v_item(int idx, int& rg, int& ch) const {
+    const int l = idx & 63, blk = idx >> 6;
+    constexpr int QB = C::VQ / 16;                 // 16-quad blocks per chunk
+    rg = (blk % QB) * 16 + (l & 15);
+    ch = (blk / QB) * 4 + (l >> 4);
+  }
+
   // Global -> registers for chunk c (K rows, V rows, this wave's mask words).
+  // Full chunks address from a uniform chunk base plus a per-thread constant;
+  // the last, partial chunk clamps to row L-1 and zero-fills keys past L.
   __device__ __forceinline__ void load_chunk(int c, uint32_t (&mreg)[C::MW]) {
     const int kbase = c * KC;
-    const bool full = kbase + KC <= L;
+    const T* kc_base = kg + (size_t)kbase * D;
+    const T* vc_base = vg + (size_t)kbase * D;
+    if (kbase + KC <= L) {
 #pragma unroll
-    for (int u = 0; u < C::K_PER_T; ++u) {
-      const int idx = tid + u * C::NT;
-      if (C::K_ITEMS % C::NT == 0 || idx < C::K_ITEMS) {
-        const int row = idx / C::CPR, ch = idx % C::CPR;
-        const int key = kbase + row;
-        const int kc = full ? key : (key < L ? key : L - 1);
-        kreg[u] = *reinterpret_cast<const u32x4*>(kg + (size_t)kc * D + ch * VEC);
-        if (!full && key >= L) kreg[u] = u32x4{0u, 0u, 0u, 0u};
+      for (int u = 0; u < C::K_PER_T; ++u) {
+        const int idx = tid + u * C::NT;
+        if (C::K_ITEMS % C::NT == 0 || idx < C::K_ITEMS)
+          kreg[u] = *reinterpret_cast<const u32x4*>(kc_base + (idx / C::CPR) * D + (idx % C::CPR) * VEC);
       }
-    }
 #pragma unroll
-    for (int u = 0; u < C::V_PER_T; ++u) {
-      const int idx = tid + u * C::NT;
-      if (C::V_ITEMS % C::NT == 0 || idx < C::V_ITEMS) {
-        const int rg = idx / C::CPR, ch = idx % C::CPR;
+      for (int u = 0; u < C::V_PER_T; ++u) {
+        const int idx = tid + u * C::NT;
+        if (C::V_ITEMS % C::NT == 0 || idx < C::V_ITEMS) {
+          int rg, ch;
+          v_item(idx, rg, ch);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kbase + 4 * rg + r;
-          const int kc = full ? key : (key < L ? key : L - 1);
-          vreg[u][r] = *reinterpret_cast<const u32x4*>(vg + (size_t)kc * D + ch * VEC);
-          if (!full && key >= L) vreg[u][r] = u32x4{0u, 0u, 0u, 0u};
+          for (int r = 0; r < 4; ++r)
+            vreg[u][r] = *reinterpret_cast<const u32x4*>(vc_base + (4 * rg + r) * D + ch * VEC);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < C::K_PER_T; ++u) {
+        const int idx = tid + u * C::NT;
+        if (C::K_ITEMS % C::NT == 0 || idx < C::K_ITEMS) {
+          const int row = idx / C::CPR, ch = idx % C::CPR;
+          const int rc = kbase + row < L ? row : L - 1 - kbase;
+          kreg[u] = *reinterpret_cast<const u32x4*>(kc_base + rc * D + ch * VEC);
+          if (kbase + row >= L) kreg[u] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < C::V_PER_T; ++u) {
+        const int idx = tid + u * C::NT;
+        if (C::V_ITEMS % C::NT == 0 || idx < C::V_ITEMS) {
+          int rg, ch;
+          v_item(idx, rg, ch);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 4 * rg + r;
+            const int rc = kbase + row < L ? row : L - 1 - kbase;
+            vreg[u][r] = *reinterpret_cast<const u32x4*>(vc_base + rc * D + ch * VEC);
+            if (kbase + row >= L) vreg[u][r] = u32x4{0u, 0u, 0u, 0u};
+          }
         }
       }
     }
@@ -193,7 +229,8 @@ struct AttnKernel {
     for (int u = 0; u < C::V_PER_T; ++u) {
       const int idx = tid + u * C::NT;
       if (C::V_ITEMS % C::NT == 0 || idx < C::V_ITEMS) {
-        const int rg = idx / C::CPR, ch = idx % C::CPR;
+        int rg, ch;
+        v_item(idx, rg, ch);
         T* dst = &sm.vt[buf][(ch * VEC) * C::VSTR + 4 * rg];
         const u32x4 r0 = vreg[u][0], r1 = vreg[u][1], r2 = vreg[u][2], r3 = vreg[u][3];
         if constexpr (sizeof(T) == 2) {
@@ -236,12 +273,17 @@ struct AttnKernel {
   __device__ __forceinline__ void zero_pad_columns() {
     for (int r = tid; r < 2 * C::VROWS; r += C::NT) {
       const int buf = r / C::VROWS, row = r % C::VROWS;
-      *reinterpret_cast<u32x4*>(&sm.vt[buf][row * C::VSTR + KC]) = u32x4{0u, 0u, 0u, 0u};
+      T* dst = &sm.vt[buf][row * C::VSTR + KC];
+      if constexpr (sizeof(T) == 2) *reinterpret_cast<u32x2*>(dst) = u32x2{0u, 0u};
+      else *reinterpret_cast<u32x4*>(dst) = u32x4{0u, 0u, 0u, 0u};
     }
   }
 
   // Four consecutive V^T elements for slots s0..s0+3 (N >= 4: one read).
+  // FULL: every slot is known to be < nslots.
+  template <bool FULL>
   __device__ __forceinline__ u32x2 vt_quad_b16(const T* vrow, int s0, int nslots) const {
+    if constexpr (FULL) nslots = 0x7fffffff;
     if constexpr (N >= 4) {
       const int s = s0 < nslots ? s0 : 0;
       const int kk = (tl_at(s >> C::LOG2N) << C::LOG2N) | (s & (N - 1));
@@ -268,7 +310,9 @@ struct AttnKernel {
     }
   }
 
+  template <bool FULL>
   __device__ __forceinline__ u32x4 vt_quad_f32(const T* vrow, int s0, int nslots) const {
+    if constexpr (FULL) nslots = 0x7fffffff;
     if constexpr (N >= 4) {
       const int s = s0 < nslots ? s0 : 0;
       const int kk = (tl_at(s >> C::LOG2N) << C::LOG2N) | (s & (N - 1));
@@ -295,9 +339,14 @@ struct AttnKernel {
   }
 
   // One softmax pass over NSB sub-blocks of 16 slots starting at sub-block sb0.
-  template <int NSB>
+  // FULL: all slots of the pass are < nslots and every key of the chunk is < L.
+  template <int NSB, bool FULL>
   __device__ __forceinline__ void pass(const T* kl, const T* vl, int sb0, int nslots, int lim,
                                        int key0) {
+    if constexpr (FULL) {
+      nslots = 0x7fffffff;
+      lim = 0x7fffffff;
+    }
     // QK^T A rows: a padding slot reads the first kept key; a key past L the
     // start of its (kept) tile.  Either way the score is a real kept score.
     int ka[NSB];
@@ -365,12 +414,13 @@ struct AttnKernel {
         }
         const u32x4 bop = __builtin_bit_cast(u32x4, pb);
         const int sA = 16 * (sb0 + a0) + 4 * g;
-        const int sB = a1 < NSB ? 16 * (sb0 + a1) + 4 * g : nslots;
+        const int sB = 16 * (sb0 + a1) + 4 * g;
 #pragma unroll
         for (int j = 0; j <= C::NDB; ++j) {
           const T* vrow = vl + (j < C::NDB ? 16 * j + n : D) * C::VSTR;
-          const u32x2 x0 = vt_quad_b16(vrow, sA, nslots);
-          const u32x2 x1 = vt_quad_b16(vrow, sB, nslots);
+          const u32x2 x0 = vt_quad_b16<FULL>(vrow, sA, nslots);
+          const u32x2 x1 = a1 < NSB ? vt_quad_b16<FULL>(vrow, sB, nslots)
+                                    : *reinterpret_cast<const u32x2*>(vrow + C::ZCOL);
           oacc[j] = Mma<bf16_t>::mac8(u32x4{x0[0], x0[1], x1[0], x1[1]}, bop, oacc[j]);
         }
       }
@@ -382,7 +432,7 @@ struct AttnKernel {
 #pragma unroll
         for (int j = 0; j <= C::NDB; ++j) {
           const T* vrow = vl + (j < C::NDB ? 16 * j + n : D) * C::VSTR;
-          oacc[j] = Mma<float>::mac4(vt_quad_f32(vrow, sA, nslots), bop, oacc[j]);
+          oacc[j] = Mma<float>::mac4(vt_quad_f32<FULL>(vrow, sA, nslots), bop, oacc[j]);
         }
       }
     }
@@ -414,12 +464,24 @@ struct AttnKernel {
     const int lim = L - c * KC;              // keys of this chunk that exist
     const int key0 = tl_at(0) << C::LOG2N;   // first kept key of the chunk
     const int nsb = (nslots + 15) >> 4;
+    const bool full_chunk = lim >= KC;
     int sb0 = 0;
-    for (; sb0 + 4 <= nsb; sb0 += 4) pass<4>(kl, vl, sb0, nslots, lim, key0);
+    for (; sb0 + 4 <= nsb; sb0 += 4) {
+      if (full_chunk && 16 * (sb0 + 4) <= nslots) pass<4, true>(kl, vl, sb0, nslots, lim, key0);
+      else pass<4, false>(kl, vl, sb0, nslots, lim, key0);
+    }
     const int rem = nsb - sb0;
-    if (rem == 3) pass<3>(kl, vl, sb0, nslots, lim, key0);
-    else if (rem == 2) pass<2>(kl, vl, sb0, nslots, lim, key0);
-    else if (rem == 1) pass<1>(kl, vl, sb0, nslots, lim, key0);
+    const bool full_tail = full_chunk && (nslots & 15) == 0;
+    if (rem == 3) {
+      if (full_tail) pass<3, true>(kl, vl, sb0, nslots, lim, key0);
+      else pass<3, false>(kl, vl, sb0, nslots, lim, key0);
+    } else if (rem == 2) {
+      if (full_tail) pass<2, true>(kl, vl, sb0, nslots, lim, key0);
+      else pass<2, false>(kl, vl, sb0, nslots, lim, key0);
+    } else if (rem == 1) {
+      if (full_tail) pass<1, true>(kl, vl, sb0, nslots, lim, key0);
+      else pass<1, false>(kl, vl, sb0, nslots, lim, key0);
+    }
   }
 
   __device__ __forceinline__ void run() {
