@@ -161,12 +161,16 @@ def main():
     mask = make_mask(w, qd, kd)
     torch.cuda.synchronize()
     out = torch.empty_like(qd)
+    ws = torch.empty(T.workspace_size(T.OP_ATTENTION_FWD, T.problem(w.B, w.H, w.L, w.d, w.M, w.N,
+                                                                    T.DTYPE_BF16 if w.dtype == "bf16"
+                                                                    else T.DTYPE_F32)),
+                     dtype=torch.uint8, device="cuda")
     flops = kept_flops_device(w, mask)
     dense_flops = 4 * w.B * w.H * w.L * w.L * w.d
     log(f"kept FLOPs {flops:.4e} ({flops / dense_flops:.4f} of dense)")
 
     def step():
-        T.attention_fwd(qd, kd, vd, mask, w.M, w.N, w.scale, out=out)
+        T.attention_fwd(qd, kd, vd, mask, w.M, w.N, w.scale, out=out, workspace=ws)
 
     ms_step, ms_kernel, ms_min = time_calls(step, args.steps, args.warmup)
     tflops = flops / (ms_step * 1e-3) / 1e12
@@ -182,7 +186,7 @@ def main():
         out2 = torch.empty_like(qd)
 
         def dense_step():
-            T.attention_fwd(qd, kd, vd, ones, w.M, w.N, w.scale, out=out2)
+            T.attention_fwd(qd, kd, vd, ones, w.M, w.N, w.scale, out=out2, workspace=ws)
         d_step, d_kernel, _ = time_calls(dense_step, max(3, args.steps // 4), 1)
         cfg["all_ones_ms"] = round(d_step, 4)
         cfg["all_ones_tflops"] = round(dense_flops / (d_step * 1e-3) / 1e12, 2)

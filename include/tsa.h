@@ -27,7 +27,7 @@
  *     failure.
  *
  * Supported problem set: dtype in {F32, BF16}; d in {64, 128}; M in {16, 32, 64};
- * N in {1, 2, 4, 8, 16, 32, 64}; 1 <= L <= 2^26; B*H <= 2^20.  Other values
+ * N in {1, 2, 4, 8, 16, 32, 64}; 1 <= L <= 2^22; B*H <= 2^20.  Other values
  * return TSA_ERR_UNSUPPORTED.
  */
 #ifndef TSA_H_
@@ -79,8 +79,10 @@ tsa_status_t tsa_workspace_size(tsa_op_t op, const tsa_problem_t* p, size_t* byt
  * lse: optional [B,H,L] fp32 natural-log sum-exp of the kept scaled scores
  * (NULL skips it).  scale: finite.  Accumulation is fp32; bf16 inputs are
  * multiplied on bf16 matrix cores with the probabilities rounded to bf16.
- * workspace: tsa_workspace_size(TSA_OP_ATTENTION_FWD) bytes (currently 0; may
- * be NULL when 0). */
+ * workspace: tsa_workspace_size(TSA_OP_ATTENTION_FWD) bytes, 256-byte aligned;
+ * the call packs V transposed into it (B*H*(d+1)*ceil(L/128)*128 elements)
+ * before the attention kernel reads it.  Its contents are not needed after
+ * the call returns control of the stream. */
 tsa_status_t tsa_attention_fwd(const tsa_problem_t* p,
                                const void* q, const void* k, const void* v,
                                const uint32_t* mask_bits, float scale,

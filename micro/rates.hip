@@ -1,0 +1,152 @@
+// Per-CU throughput microbenchmarks for the resources the tile-sparse
+// attention kernel depends on (gfx950): LDS reads (b128, b64, transposing
+// b64), bf16 16x16x32 MFMA, v_exp_f32 and fp32 FMA.  Every kernel is
+// in-bounds and exits after a fixed number of iterations.
+//
+//   hipcc --offload-arch=gfx950 -O3 micro/rates.hip -o micro_rates && ./micro_rates
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+
+#define CHECK(x)                                                                  \
+  do {                                                                            \
+    hipError_t e_ = (x);                                                          \
+    if (e_ != hipSuccess) {                                                       \
+      fprintf(stderr, "%s failed: %s\n", #x, hipGetErrorString(e_));              \
+      exit(1);                                                                    \
+    }                                                                             \
+  } while (0)
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kIters = 4096;
+
+// Each lane reads 16 bytes at lane*16 + ((it*1024) mod 32 KB): consecutive
+// lanes, consecutive 16-byte slots (conflict-free).
+__global__ __launch_bounds__(kThreads) void lds_b128(unsigned* out) {
+  __shared__ __attribute__((aligned(16))) unsigned lds[16384];  // 64 KB
+  for (int i = threadIdx.x; i < 16384; i += kThreads) lds[i] = i;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  u32x4 acc = {0, 0, 0, 0};
+  for (int it = 0; it < kIters; ++it) {
+    const int off = (lane * 16 + ((it * 1024 + (threadIdx.x >> 6) * 4096) & 32767)) >> 2;
+    acc ^= *reinterpret_cast<const u32x4*>(&lds[off]);
+  }
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x12345678u) out[0] = 1;
+}
+
+__global__ __launch_bounds__(kThreads) void lds_b64(unsigned* out) {
+  __shared__ __attribute__((aligned(16))) unsigned lds[16384];
+  for (int i = threadIdx.x; i < 16384; i += kThreads) lds[i] = i;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  u32x2 acc = {0, 0};
+  for (int it = 0; it < kIters; ++it) {
+    const int off = (lane * 8 + ((it * 512 + (threadIdx.x >> 6) * 4096) & 32767)) >> 2;
+    acc ^= *reinterpret_cast<const u32x2*>(&lds[off]);
+  }
+  if ((acc.x ^ acc.y) == 0x12345678u) out[0] = 1;
+}
+
+// Transposing read: lanes 4j..4j+3 of each 16-lane block read row j (4 rows of
+// 32 bytes per block, rows 272 bytes apart), as an MFMA operand gather would.
+__global__ __launch_bounds__(kThreads) void lds_tr16(unsigned* out) {
+  __shared__ __attribute__((aligned(16))) unsigned short lds[32768];
+  for (int i = threadIdx.x; i < 32768; i += kThreads) lds[i] = (unsigned short)i;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int blk = lane >> 4, j = (lane >> 2) & 3, c = lane & 3;
+  i16x4 acc = {0, 0, 0, 0};
+  for (int it = 0; it < kIters; ++it) {
+    const int row = (blk * 4 + j + (it & 15) * 16 + (threadIdx.x >> 6) * 4) & 127;
+    const int off = row * 136 + c * 4 + ((it >> 4) & 7) * 16;
+    acc ^= __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(lds + off));
+  }
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x1234) out[0] = 1;
+}
+
+__global__ __launch_bounds__(kThreads) void mfma_bf16(unsigned* out, float seed) {
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) { a[i] = (__bf16)(seed * i); b[i] = (__bf16)(seed + i); }
+  f32x4 c0 = {0, 0, 0, 0}, c1 = c0, c2 = c0, c3 = c0;
+  for (int it = 0; it < kIters / 4; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c3, 0, 0, 0);
+  }
+  const f32x4 s = c0 + c1 + c2 + c3;
+  if (s.x + s.y + s.z + s.w == 1.2345f) out[0] = 1;
+}
+
+__global__ __launch_bounds__(kThreads) void valu_exp(unsigned* out, float seed) {
+  float x0 = seed * threadIdx.x, x1 = x0 + 1.f, x2 = x0 + 2.f, x3 = x0 + 3.f;
+  for (int it = 0; it < kIters / 4; ++it) {
+    x0 = __builtin_amdgcn_exp2f(x0); x1 = __builtin_amdgcn_exp2f(x1);
+    x2 = __builtin_amdgcn_exp2f(x2); x3 = __builtin_amdgcn_exp2f(x3);
+  }
+  if (x0 + x1 + x2 + x3 == 1.2345f) out[0] = 1;
+}
+
+__global__ __launch_bounds__(kThreads) void valu_fma(unsigned* out, float seed) {
+  float x0 = seed * threadIdx.x, x1 = x0 + 1.f, x2 = x0 + 2.f, x3 = x0 + 3.f;
+  for (int it = 0; it < kIters / 4; ++it) {
+    x0 = __builtin_fmaf(x0, 0.999f, 0.5f); x1 = __builtin_fmaf(x1, 0.999f, 0.5f);
+    x2 = __builtin_fmaf(x2, 0.999f, 0.5f); x3 = __builtin_fmaf(x3, 0.999f, 0.5f);
+  }
+  if (x0 + x1 + x2 + x3 == 1.2345f) out[0] = 1;
+}
+
+template <typename F>
+float time_ms(F launch) {
+  hipEvent_t a, b;
+  CHECK(hipEventCreate(&a));
+  CHECK(hipEventCreate(&b));
+  launch();
+  CHECK(hipDeviceSynchronize());
+  CHECK(hipEventRecord(a));
+  for (int r = 0; r < 5; ++r) launch();
+  CHECK(hipEventRecord(b));
+  CHECK(hipEventSynchronize(b));
+  float ms;
+  CHECK(hipEventElapsedTime(&ms, a, b));
+  return ms / 5;
+}
+
+int main() {
+  hipDeviceProp_t prop;
+  CHECK(hipGetDeviceProperties(&prop, 0));
+  const int cus = prop.multiProcessorCount;
+  const double clk = 2.4e9;  // peak engine clock of MI355X
+  unsigned* out;
+  CHECK(hipMalloc(&out, 64));
+  const int blocks = cus * 8;
+  const double waves = (double)blocks * kThreads / 64;
+  printf("device %s, %d CUs, %d blocks x %d threads, %d iterations\n", prop.name, cus, blocks,
+         kThreads, kIters);
+  auto per_cu_clk = [&](double total, float ms) { return total / (ms * 1e-3) / clk / cus; };
+  float t;
+  t = time_ms([&] { hipLaunchKernelGGL(lds_b128, dim3(blocks), dim3(kThreads), 0, 0, out); });
+  printf("ds_read_b128      : %7.1f B/clk/CU (%.3f ms)\n", per_cu_clk(waves * 64 * 16 * kIters, t), t);
+  t = time_ms([&] { hipLaunchKernelGGL(lds_b64, dim3(blocks), dim3(kThreads), 0, 0, out); });
+  printf("ds_read_b64       : %7.1f B/clk/CU (%.3f ms)\n", per_cu_clk(waves * 64 * 8 * kIters, t), t);
+  t = time_ms([&] { hipLaunchKernelGGL(lds_tr16, dim3(blocks), dim3(kThreads), 0, 0, out); });
+  printf("ds_read_b64_tr_b16: %7.1f B/clk/CU (%.3f ms)\n", per_cu_clk(waves * 64 * 8 * kIters, t), t);
+  t = time_ms([&] { hipLaunchKernelGGL(mfma_bf16, dim3(blocks), dim3(kThreads), 0, 0, out, 0.5f); });
+  printf("mfma 16x16x32 bf16: %7.1f FLOP/clk/CU (%.3f ms)\n",
+         per_cu_clk(waves * kIters * 16.0 * 16 * 32 * 2, t), t);
+  t = time_ms([&] { hipLaunchKernelGGL(valu_exp, dim3(blocks), dim3(kThreads), 0, 0, out, 0.01f); });
+  printf("v_exp_f32         : %7.1f lane-ops/clk/CU (%.3f ms)\n", per_cu_clk(waves * 64 * kIters, t), t);
+  t = time_ms([&] { hipLaunchKernelGGL(valu_fma, dim3(blocks), dim3(kThreads), 0, 0, out, 0.01f); });
+  printf("v_fma_f32         : %7.1f lane-ops/clk/CU (%.3f ms)\n", per_cu_clk(waves * 64 * kIters, t), t);
+  CHECK(hipFree(out));
+  return 0;
+}

@@ -41,7 +41,7 @@ def test_row_words():
 
 def test_workspace_sizes():
     pr = T.problem(1, 40, 32760, 128, 16, 8)
-    assert T.workspace_size(T.OP_ATTENTION_FWD, pr) == 0
+    assert T.workspace_size(T.OP_ATTENTION_FWD, pr) == 40 * 129 * 32768 * 2
     assert T.workspace_size(T.OP_MASK_COMPACT, pr) >= 40 * 2048 * 4
     pp = T.problem(1, 24, 118800, 128, 16, 16)
     ws = T.workspace_size(T.OP_PREDICT_MASK, pp)
@@ -63,7 +63,7 @@ def _attn(pr, q=1, k=1, v=1, m=1, o=2, scale=1.0):
     ("M", 8, T.ERR_UNSUPPORTED), ("M", 48, T.ERR_UNSUPPORTED), ("N", 3, T.ERR_UNSUPPORTED),
     ("N", 128, T.ERR_UNSUPPORTED), ("d", 96, T.ERR_UNSUPPORTED), ("dtype", 5, T.ERR_UNSUPPORTED),
     ("L", 0, T.ERR_INVALID_ARGUMENT), ("B", -1, T.ERR_INVALID_ARGUMENT),
-    ("L", (1 << 26) + 1, T.ERR_UNSUPPORTED), ("H", 1 << 21, T.ERR_UNSUPPORTED),
+    ("L", (1 << 22) + 1, T.ERR_UNSUPPORTED), ("H", 1 << 21, T.ERR_UNSUPPORTED),
 ])
 def test_attention_rejects_bad_problem(field, value, status):
     pr = T.problem(1, 2, 512, 64, 16, 16)
@@ -85,6 +85,7 @@ def test_attention_rejects_bad_pointers_and_scale():
                                ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000),
                                ctypes.c_float(1.0), ctypes.c_void_p(0x50000), None, None, 0, None)
     assert st == T.ERR_INVALID_ARGUMENT and "align" in T.last_error()
+    assert _attn(pr) == T.ERR_WORKSPACE_TOO_SMALL            # no workspace given
 
 
 def test_compact_and_predict_validation():

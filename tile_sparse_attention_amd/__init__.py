@@ -131,8 +131,12 @@ def _workspace(op: int, pr: Problem, device):
 
 
 def attention_fwd(q, k, v, mask_bits, M: int, N: int, scale: float | None = None, *,
-                  out=None, return_lse: bool = False):
-    """O (and optionally LSE) of tile-sparse attention; q, k, v: [B, H, L, d]."""
+                  out=None, return_lse: bool = False, workspace=None):
+    """O (and optionally LSE) of tile-sparse attention; q, k, v: [B, H, L, d].
+
+    `workspace` (uint8 GPU tensor of at least workspace_size(OP_ATTENTION_FWD)
+    bytes) is allocated per call when not given.
+    """
     torch = _torch()
     B, H, L, d = q.shape
     if scale is None:
@@ -150,7 +154,11 @@ def attention_fwd(q, k, v, mask_bits, M: int, N: int, scale: float | None = None
             tuple(mask_bits.shape) != (B, H, T_q, mask_row_words(L, N)):
         raise TsaError(ERR_INVALID_ARGUMENT, "mask_bits must be int32/uint32 [B, H, T_q, words]")
     pr = Problem(B, H, L, d, M, N, _dtype_code(q))
-    ws, nws = _workspace(OP_ATTENTION_FWD, pr, q.device)
+    if workspace is None:
+        ws, nws = _workspace(OP_ATTENTION_FWD, pr, q.device)
+    else:
+        _need_cuda(workspace)
+        ws, nws = workspace, workspace.numel() * workspace.element_size()
     _check(lib().tsa_attention_fwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(mask_bits),
                                    ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(ws), nws,
                                    _stream()))

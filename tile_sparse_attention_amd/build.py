@@ -43,12 +43,46 @@ def _compile(src: str) -> str:
     return obj
 
 
+SPILL_CHECKED = ("attention_fwd_bf16.hip", "attention_fwd_f32.hip")
+
+
+def _check_no_spills(src: str) -> None:
+    """Fail the build if a kernel of `src` spills registers to scratch memory.
+
+    (SGPR spills into VGPR lanes cost no memory traffic and are allowed.)
+    The attention kernels are tuned to fit the register file at two waves per
+    SIMD; a spill means a change pushed them over, which costs both speed and
+    (through scratch traffic interleaved with the LDS-DMA pipeline) has been
+    seen to produce wrong results, so it is treated as a build error.
+    """
+    asm = os.path.join(BUILD, os.path.basename(src)[:-4] + ".s")
+    cmd = [HIPCC, *CFLAGS, "--offload-device-only", "-S", src, "-o", asm]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr}")
+    spills = []
+    name = None
+    with open(asm) as f:
+        for line in f:
+            t = line.strip()
+            if t.startswith(".name:"):
+                name = t.split(None, 1)[1]
+            elif t.startswith((".vgpr_spill_count:", ".private_segment_fixed_size:")):
+                n = int(t.split()[1])
+                if n:
+                    spills.append(f"{name}: {t}")
+    if spills:
+        raise RuntimeError("register spills in " + src + ":\n  " + "\n  ".join(spills))
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    checked = [x for x in srcs if os.path.basename(x) in SPILL_CHECKED]
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))
+        list(ex.map(_check_no_spills, checked))
     tmp = LIB + ".tmp"
     r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
                        capture_output=True, text=True)

@@ -45,7 +45,7 @@ bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1))
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
-constexpr int kMaxL = 1 << 26;
+constexpr int kMaxL = 1 << 22;
 constexpr long long kMaxBH = 1 << 20;
 constexpr long long kMaxGrid = 0x7fffffffLL;
 
@@ -90,7 +90,7 @@ tsa_status_t tsa_workspace_size(tsa_op_t op, const tsa_problem_t* p, size_t* byt
   switch (op) {
     case TSA_OP_ATTENTION_FWD:
       if ((s = check_problem(p, true)) != TSA_OK) return s;
-      *bytes = 0;
+      *bytes = tsa::attention_vt_bytes(p);
       return TSA_OK;
     case TSA_OP_MASK_COMPACT:
       if ((s = check_problem(p, false)) != TSA_OK) return s;
@@ -107,8 +107,6 @@ tsa_status_t tsa_workspace_size(tsa_op_t op, const tsa_problem_t* p, size_t* byt
 tsa_status_t tsa_attention_fwd(const tsa_problem_t* p, const void* q, const void* k, const void* v,
                                const uint32_t* mask_bits, float scale, void* o, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   tsa_status_t s = check_problem(p, true);
   if (s != TSA_OK) return s;
   if (!q || !k || !v || !mask_bits || !o)
@@ -118,9 +116,14 @@ tsa_status_t tsa_attention_fwd(const tsa_problem_t* p, const void* q, const void
       !aligned(mask_bits, 4) || (lse && !aligned(lse, 4)))
     return fail(TSA_ERR_INVALID_ARGUMENT, "q/k/v/o need 16-byte, mask/lse 4-byte alignment");
   if (o == q || o == k || o == v) return fail(TSA_ERR_INVALID_ARGUMENT, "o aliases an input");
+  const size_t need = tsa::attention_vt_bytes(p);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(TSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, 256-byte aligned (got %zu)",
+                need, workspace_bytes);
   const long long blocks = (long long)p->B * p->H * ((p->L + 63) / 64);
   if (blocks > kMaxGrid) return fail(TSA_ERR_UNSUPPORTED, "grid too large");
-  tsa::AttnLaunch a{p, q, k, v, mask_bits, scale, o, lse, static_cast<hipStream_t>(stream)};
+  tsa::AttnLaunch a{p, q, k, v, mask_bits, scale, o, lse, workspace,
+                    static_cast<hipStream_t>(stream)};
   const hipError_t e = p->dtype == TSA_DTYPE_BF16 ? tsa::launch_attention_bf16(a)
                                                   : tsa::launch_attention_f32(a);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");

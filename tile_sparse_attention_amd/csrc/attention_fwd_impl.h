@@ -6,24 +6,30 @@
 // softmax.  O = softmax(scale * Q K^T restricted to kept tiles) V.
 //
 // Work decomposition
-//   * A work-group owns 16*W consecutive query rows of one (b, h); each wave
-//     owns 16 of them (one 16-row slice of a mask row, since M is a multiple
-//     of 16).
+//   * A work-group owns 32*W consecutive query rows of one (b, h); each wave
+//     owns 32 of them as two 16-row query tiles (M is a multiple of 16, so a
+//     16-row tile lies inside one mask row).
 //   * Keys are streamed in chunks of KC keys.  The work-group stages each
 //     chunk once in LDS (K as rows, V transposed to [d][key]) with
-//     double-buffered, coalesced 16-byte global loads; every wave then reuses
-//     it, so K/V are read from HBM/L2 once per work-group, not once per
-//     query tile.
-//   * Per chunk each wave compacts its own mask bits into the list of kept
-//     key tiles (wave prefix count of the bitmap, the routine the compaction
-//     kernel also uses) and packs the kept keys densely into 16-key "slots".
-//     Matrix-core work is spent only on kept keys: a skipped tile costs its
-//     mask bit, and kept tiles of any width N share MFMA blocks instead of
-//     each being padded to 16 keys.
+//     double-buffered buffer loads whose chunk offset is a uniform value; all
+//     waves then reuse it, so each K/V element crosses from L2 once per
+//     32*W query rows.  Chunks are visited in a per-work-group rotated order
+//     so that neighbouring work-groups (same XCD, same L2) do not all miss on
+//     the same lines at the same time.
+//   * Per chunk each wave compacts its mask bits into the list of kept key
+//     tiles (wave prefix count of the bitmap, the routine the compaction
+//     kernel also uses) and packs the kept keys densely into 16-key "slots":
+//     matrix-core work is spent only on kept keys, and kept tiles of any
+//     width N share MFMA blocks instead of each being padded to 16 keys.
+//     When M >= 32 both query tiles of a wave lie in the same mask row and
+//     share one compacted list.
 //   * Scores are formed transposed, S^T = K Q^T (A = gathered K rows from LDS,
-//     B = the wave's Q fragment held in registers), so each lane owns one
+//     B = the tile's Q fragment held in registers), so each lane owns one
 //     query column and the S^T accumulator layout is directly the B operand of
-//     O^T += V^T P^T: probabilities never leave registers.
+//     O^T += V^T P^T: probabilities never leave registers.  For N >= 8 the
+//     rows of each pair of 16-slot blocks are assigned to slots so that every
+//     lane's eight PV k-values are eight consecutive keys: one 16-byte LDS
+//     read per MFMA operand.
 //   * Padding slots need no per-score masking: for QK^T they read a kept key
 //     of the same row (so the running max only ever sees real kept scores),
 //     for PV they read zero columns of the LDS V^T tile.  Keys past L read as
@@ -31,10 +37,10 @@
 //     matrix cores too: V^T carries one extra row of ones (zero past L and in
 //     the padding columns), so l = P . 1 accumulates with O.
 //   * Online softmax in base 2 with scale*log2(e) folded into one FMA per
-//     score; the reference max is raised (and O, l rescaled) only when some
-//     row's max grows by more than 2^8, a wave-uniform decision, so most
-//     passes do no rescaling.  The result O / l is unchanged by the choice of
-//     reference.
+//     score.  The reference max is raised (and O, l rescaled) only when some
+//     lane's scores exceed it by more than 2^8, a wave-uniform ballot, so most
+//     passes do neither a cross-lane reduction nor a rescale.  The result
+//     O / l does not depend on the choice of reference.
 //   * Normalisation O = O / l (0 for a row with nothing kept) and the store
 //     happen once at the end.
 #pragma once
@@ -46,11 +52,12 @@ namespace tsa {
 struct AttnParams {
   const void* q;
   const void* k;
-  const void* v;
+  const void* vt;        // packed V^T: [B*H][d + 1][L_pad], row d = ones (keys < L)
   const uint32_t* mask;
   void* o;
   float* lse;
   int H, L, M, T_q, T_k, words;
+  int L_pad;             // row length of the packed V^T (multiple of 128)
   int n_qblocks;
   float scale_log2;  // scale * log2(e)
 };
@@ -61,6 +68,9 @@ template <> struct ElemTraits<bf16_t> { static constexpr int VEC = 8; };
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 
+// Fourth word of a raw (unformatted, unswizzled) buffer resource on gfx9.
+constexpr int kBufferFlags = 0x00020000;
+
 template <typename T, int D, int N, int KC, int W>
 struct AttnCfg {
   static constexpr int VEC = ElemTraits<T>::VEC;   // elements per 16 bytes
@@ -68,28 +78,36 @@ struct AttnCfg {
   static constexpr int NSLAB = D / SLAB;
   static constexpr int NDB = D / 16;               // 16-wide d blocks of O^T
   static constexpr int KSTR = D + VEC;             // K row stride in LDS (+16 B against bank conflicts)
-  static constexpr int VPAD = 4;                   // zero columns after the KC keys of a V^T row
-  static constexpr int VSTR = KC + VPAD;           // V^T row stride: 264 B (bf16) / 272 B (fp32)
+  static constexpr int VPAD = VEC;                 // zero columns after the KC keys of a V^T row
+  static constexpr int VSTR = KC + VPAD;           // V^T row stride (272 B for bf16, KC = 128)
   static constexpr int VROWS = D + 1;              // V^T rows: d = 0..D-1 and the ones row
   static constexpr int ZCOL = KC;                  // first zero column of V^T
   static constexpr int NT = 64 * W;
+  static constexpr int ROWS = 32 * W;              // query rows per work-group
   static constexpr int CPR = D / VEC;              // 16-byte chunks per K/V row
-  static constexpr int K_ITEMS = KC * CPR;
-  static constexpr int V_ITEMS = (KC / 4) * CPR;   // groups of 4 rows x 16 bytes
-  static constexpr int K_PER_T = (K_ITEMS + NT - 1) / NT;
-  static constexpr int V_PER_T = (V_ITEMS + NT - 1) / NT;
   static constexpr int TPC = KC / N;               // key tiles per chunk
   static constexpr int WINT = TPC < 64 ? TPC : 64; // tiles per compaction window
   static constexpr int NWIN = TPC / WINT;
   static constexpr int MW = TPC >= 32 ? TPC / 32 : 1;  // mask words per chunk
   static constexpr int LOG2N = ilog2(N);
-  static constexpr int MAXSB = KC / 16;            // 16-slot sub-blocks per chunk
+  // bf16 with N >= 8: pairs of 16-slot blocks use the octet slot order
+  static constexpr bool OCT = sizeof(T) == 2 && N >= 8;
+  // LDS tiles are filled by direct global->LDS loads: one wave instruction
+  // writes 1 KB (16 bytes per lane) contiguously, so a tile of padded rows is
+  // covered by whole 1-KB instructions; lanes that land on row padding (or
+  // past the last row) read out of range and write zeros.
+  static constexpr int KRB = D * (int)sizeof(T);          // K row bytes in memory
+  static constexpr int KRS = KSTR * (int)sizeof(T);       // K row stride in LDS
+  static constexpr int VRB = KC * (int)sizeof(T);         // V^T row bytes per chunk
+  static constexpr int VRS = VSTR * (int)sizeof(T);       // V^T row stride in LDS
+  static constexpr int NI_K = (KC * KRS + 1023) / 1024;   // 1-KB loads per K tile
+  static constexpr int NI_V = (VROWS * VRS + 1023) / 1024;
+  static constexpr int NI = NI_K + NI_V;
+  static constexpr int NI_W = (NI + W - 1) / W;           // loads per wave per chunk
   static_assert(D % SLAB == 0 && D % 16 == 0, "head dim");
   static_assert(KC % N == 0 && KC % 64 == 0 && TPC <= 256 && MW <= 4, "chunk");
   static_assert((1 << LOG2N) == N, "N must be a power of two");
-  // V staging: a wave covers 16 consecutive key quads x 4 16-byte d chunks
-  static constexpr int VQ = KC / 4;                // key quads per chunk
-  static_assert(VQ % 16 == 0 && CPR % 4 == 0, "V staging tile");
+  static_assert(KRS == KRB + 16 && VRS == VRB + 16, "one 16-byte padding slot per row");
 };
 
 template <typename T> struct Mma;
@@ -120,259 +138,148 @@ struct AttnKernel {
   static constexpr float RESCALE_STEP = 8.f;  // log2 units a row max may grow before rescaling
 
   struct Smem {
-    T k[2][KC * C::KSTR];
-    T vt[2][C::VROWS * C::VSTR];
-    uint8_t tl[W][C::TPC];
+    __attribute__((aligned(16))) T k[2][C::NI_K * 1024 / sizeof(T)];
+    __attribute__((aligned(16))) T vt[2][C::NI_V * 1024 / sizeof(T)];
+    uint8_t tl[W][2][C::TPC];
   };
 
-  // ---- per-wave state ----
+  // per-tile state (a wave owns two 16-row query tiles)
+  struct Tile {
+    u32x4 qf[C::NSLAB];       // Q fragment: lane (g, n) holds Q[row+n][SLAB*s + VEC*g .. +VEC)
+    f32x4 oacc[C::NDB + 1];   // O^T blocks and, last, the row sums l
+    float m_run;              // reference max (log2 domain) of query n
+  };
+
   const AttnParams& p;
   Smem& sm;
   int tid, lane, g, n, wave;
   int L, bh, row0;
-  bool active;
   const T* __restrict__ kg;
-  const T* __restrict__ vg;
-  const uint32_t* __restrict__ mask_row;
-  u32x4 qf[C::NSLAB];
-  f32x4 oacc[C::NDB + 1];  // O^T blocks and, last, the row sums l
-  float m_run;             // reference max (log2 domain) of query n
-  u32x4 kreg[C::K_PER_T];
-  u32x4 vreg[C::V_PER_T][4];
+  const T* __restrict__ vtg;
+  const uint32_t* __restrict__ mask_row[2];
+  Tile tile[2];
 
   __device__ __forceinline__ AttnKernel(const AttnParams& pp, Smem& s) : p(pp), sm(s) {}
 
-  __device__ __forceinline__ int tl_at(int idx) const { return (int)sm.tl[wave][idx]; }
-
-  // V staging item -> (key quad rg, 16-byte d chunk ch).  Lane l of a wave
-  // takes quad (l % 16) and chunk (l / 16) of the wave's 16 x 4 block, so the
-  // 16 lanes writing one V^T row write 128 contiguous bytes.
-  __device__ __forceinline__ void v_item(int idx, int& rg, int& ch) const {
-    const int l = idx & 63, blk = idx >> 6;
-    constexpr int QB = C::VQ / 16;                 // 16-quad blocks per chunk
-    rg = (blk % QB) * 16 + (l & 15);
-    ch = (blk / QB) * 4 + (l >> 4);
+  __device__ __forceinline__ int tl_at(int list, int idx) const {
+    return (int)sm.tl[wave][list][idx];
   }
 
-  // Global -> registers for chunk c (K rows, V rows, this wave's mask words).
-  // Full chunks address from a uniform chunk base plus a per-thread constant;
-  // the last, partial chunk clamps to row L-1 and zero-fills keys past L.
-  __device__ __forceinline__ void load_chunk(int c, uint32_t (&mreg)[C::MW]) {
+  // Byte offset (relative to the chunk's resource base) that lane `ln` of
+  // tile load `I` reads, or an out-of-range offset for padding slots.
+  __device__ __forceinline__ uint32_t dma_offset(int I, int ln) const {
+    constexpr uint32_t OOB = 0x80000000u;
+    if (I < C::NI_K) {
+      const int pos = I * 1024 + 16 * ln;
+      const int row = pos / C::KRS, cb = pos - row * C::KRS;
+      return row < KC && cb < C::KRB ? (uint32_t)(row * C::KRB + cb) : OOB;
+    }
+    const int pos = (I - C::NI_K) * 1024 + 16 * ln;
+    const int row = pos / C::VRS, cb = pos - row * C::VRS;
+    return row < C::VROWS && cb < C::VRB ? (uint32_t)(row * p.L_pad * (int)sizeof(T) + cb) : OOB;
+  }
+
+  // Issue the direct global->LDS loads of chunk c into buffer `buf` (this
+  // wave's share) and the loads of both tiles' mask words for it.  Nothing
+  // waits here: the caller waits for the vector-memory counter and syncs the
+  // work-group before the buffer is read.
+  __device__ __forceinline__ void issue_chunk(int c, int buf, uint32_t (&mreg)[2][C::MW]) {
     const int kbase = c * KC;
-    const T* kc_base = kg + (size_t)kbase * D;
-    const T* vc_base = vg + (size_t)kbase * D;
-    if (kbase + KC <= L) {
+    const int rows = L - kbase < KC ? L - kbase : KC;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kg + (size_t)kbase * D), (short)0, rows * C::KRB, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vtg + kbase), (short)0, (C::VROWS * p.L_pad - kbase) * (int)sizeof(T), kBufferFlags);
 #pragma unroll
-      for (int u = 0; u < C::K_PER_T; ++u) {
-        const int idx = tid + u * C::NT;
-        if (C::K_ITEMS % C::NT == 0 || idx < C::K_ITEMS)
-          kreg[u] = *reinterpret_cast<const u32x4*>(kc_base + (idx / C::CPR) * D + (idx % C::CPR) * VEC);
-      }
-#pragma unroll
-      for (int u = 0; u < C::V_PER_T; ++u) {
-        const int idx = tid + u * C::NT;
-        if (C::V_ITEMS % C::NT == 0 || idx < C::V_ITEMS) {
-          int rg, ch;
-          v_item(idx, rg, ch);
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            vreg[u][r] = *reinterpret_cast<const u32x4*>(vc_base + (4 * rg + r) * D + ch * VEC);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < C::K_PER_T; ++u) {
-        const int idx = tid + u * C::NT;
-        if (C::K_ITEMS % C::NT == 0 || idx < C::K_ITEMS) {
-          const int row = idx / C::CPR, ch = idx % C::CPR;
-          const int rc = kbase + row < L ? row : L - 1 - kbase;
-          kreg[u] = *reinterpret_cast<const u32x4*>(kc_base + rc * D + ch * VEC);
-          if (kbase + row >= L) kreg[u] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < C::V_PER_T; ++u) {
-        const int idx = tid + u * C::NT;
-        if (C::V_ITEMS % C::NT == 0 || idx < C::V_ITEMS) {
-          int rg, ch;
-          v_item(idx, rg, ch);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = 4 * rg + r;
-            const int rc = kbase + row < L ? row : L - 1 - kbase;
-            vreg[u][r] = *reinterpret_cast<const u32x4*>(vc_base + rc * D + ch * VEC);
-            if (kbase + row >= L) vreg[u][r] = u32x4{0u, 0u, 0u, 0u};
-          }
+    for (int u = 0; u < C::NI_W; ++u) {
+      const int I = wave + W * u;
+      if (C::NI % W == 0 || I < C::NI) {
+        if (I < C::NI_K) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rk, (__attribute__((address_space(3))) void*)((char*)sm.k[buf] + I * 1024), 16,
+              dma_offset(I, lane), 0, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rv, (__attribute__((address_space(3))) void*)((char*)sm.vt[buf] + (I - C::NI_K) * 1024),
+              16, dma_offset(I, lane), 0, 0, 0);
         }
       }
     }
-    // mask words holding key tiles [c*TPC, c*TPC + TPC) of this wave's row
+    // mask words holding key tiles [c*TPC, c*TPC + TPC) of each tile's row
     const int w0 = (c * C::TPC) >> 5;
 #pragma unroll
-    for (int i = 0; i < C::MW; ++i) {
-      const int wi = w0 + i < p.words ? w0 + i : p.words - 1;
-      mreg[i] = mask_row[wi];
-    }
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < C::MW; ++i) {
+        const int wi = w0 + i < p.words ? w0 + i : p.words - 1;
+        mreg[t][i] = mask_row[t][wi];
+      }
   }
 
-  // Registers -> LDS buffer `buf` for chunk c (V transposed; ones row).
-  __device__ __forceinline__ void store_chunk(int c, int buf) {
-#pragma unroll
-    for (int u = 0; u < C::K_PER_T; ++u) {
-      const int idx = tid + u * C::NT;
-      if (C::K_ITEMS % C::NT == 0 || idx < C::K_ITEMS) {
-        const int row = idx / C::CPR, ch = idx % C::CPR;
-        *reinterpret_cast<u32x4*>(&sm.k[buf][row * C::KSTR + ch * VEC]) = kreg[u];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < C::V_PER_T; ++u) {
-      const int idx = tid + u * C::NT;
-      if (C::V_ITEMS % C::NT == 0 || idx < C::V_ITEMS) {
-        int rg, ch;
-        v_item(idx, rg, ch);
-        T* dst = &sm.vt[buf][(ch * VEC) * C::VSTR + 4 * rg];
-        const u32x4 r0 = vreg[u][0], r1 = vreg[u][1], r2 = vreg[u][2], r3 = vreg[u][3];
-        if constexpr (sizeof(T) == 2) {
-          // word w of a row holds d = 2w (low half) and 2w+1 (high half)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const u32x2 lo = {(r0[w] & 0xffffu) | (r1[w] << 16), (r2[w] & 0xffffu) | (r3[w] << 16)};
-            const u32x2 hi = {(r0[w] >> 16) | (r1[w] & 0xffff0000u),
-                              (r2[w] >> 16) | (r3[w] & 0xffff0000u)};
-            *reinterpret_cast<u32x2*>(dst + (2 * w) * C::VSTR) = lo;
-            *reinterpret_cast<u32x2*>(dst + (2 * w + 1) * C::VSTR) = hi;
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            *reinterpret_cast<u32x4*>(dst + e * C::VSTR) = u32x4{r0[e], r1[e], r2[e], r3[e]};
-        }
-      }
-    }
-    // ones row: 1 for keys < L, 0 past L
-    if (tid < KC / VEC) {
-      const int k0 = c * KC + tid * VEC;
-      u32x4 v;
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t lo = k0 + 2 * w < L ? 0x3f80u : 0u;
-          const uint32_t hi = k0 + 2 * w + 1 < L ? 0x3f800000u : 0u;
-          v[w] = lo | hi;
-        }
-      } else {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) v[w] = k0 + w < L ? 0x3f800000u : 0u;
-      }
-      *reinterpret_cast<u32x4*>(&sm.vt[buf][D * C::VSTR + tid * VEC]) = v;
-    }
+  // key offset (in the chunk) of slot s of list `li`
+  __device__ __forceinline__ int slot_key(int li, int s) const {
+    if constexpr (N == 1) return tl_at(li, s);
+    else return (tl_at(li, s >> C::LOG2N) << C::LOG2N) | (s & (N - 1));
   }
 
-  // Zero the V^T padding columns (read by padding slots) of both buffers.
-  __device__ __forceinline__ void zero_pad_columns() {
-    for (int r = tid; r < 2 * C::VROWS; r += C::NT) {
-      const int buf = r / C::VROWS, row = r % C::VROWS;
-      T* dst = &sm.vt[buf][row * C::VSTR + KC];
-      if constexpr (sizeof(T) == 2) *reinterpret_cast<u32x2*>(dst) = u32x2{0u, 0u};
-      else *reinterpret_cast<u32x4*>(dst) = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
-  // Four consecutive V^T elements for slots s0..s0+3 (N >= 4: one read).
-  // FULL: every slot is known to be < nslots.
+  // Four consecutive slots s0..s0+3 of V^T row `vrow` as a 4-element quad
+  // (8 bytes for bf16, 16 bytes for fp32).  FULL: every slot is < nslots.
   template <bool FULL>
-  __device__ __forceinline__ u32x2 vt_quad_b16(const T* vrow, int s0, int nslots) const {
+  __device__ __forceinline__ u32x4 vt_quad(const T* vrow, int li, int s0, int nslots) const {
     if constexpr (FULL) nslots = 0x7fffffff;
     if constexpr (N >= 4) {
       const int s = s0 < nslots ? s0 : 0;
-      const int kk = (tl_at(s >> C::LOG2N) << C::LOG2N) | (s & (N - 1));
-      return *reinterpret_cast<const u32x2*>(vrow + (s0 < nslots ? kk : C::ZCOL));
+      const int col = s0 < nslots ? slot_key(li, s) : C::ZCOL;
+      if constexpr (sizeof(T) == 2) {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(vrow + col);
+        return u32x4{x[0], x[1], 0u, 0u};
+      } else {
+        return *reinterpret_cast<const u32x4*>(vrow + col);
+      }
     } else if constexpr (N == 2) {
-      int kk[2];
+      int col[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int s = s0 + 2 * e;
-        const int t = tl_at(s < nslots ? (s >> 1) : 0) << 1;
-        kk[e] = s < nslots ? t : C::ZCOL;
+        const int t = tl_at(li, s < nslots ? (s >> 1) : 0) << 1;
+        col[e] = s < nslots ? t : C::ZCOL;
       }
-      return u32x2{*reinterpret_cast<const uint32_t*>(vrow + kk[0]),
-                   *reinterpret_cast<const uint32_t*>(vrow + kk[1])};
+      if constexpr (sizeof(T) == 2) {
+        return u32x4{*reinterpret_cast<const uint32_t*>(vrow + col[0]),
+                     *reinterpret_cast<const uint32_t*>(vrow + col[1]), 0u, 0u};
+      } else {
+        const u32x2 a = *reinterpret_cast<const u32x2*>(vrow + col[0]);
+        const u32x2 b = *reinterpret_cast<const u32x2*>(vrow + col[1]);
+        return u32x4{a[0], a[1], b[0], b[1]};
+      }
     } else {
       uint32_t e4[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int s = s0 + e;
-        const int t = tl_at(s < nslots ? s : 0);
-        e4[e] = reinterpret_cast<const uint16_t*>(vrow)[s < nslots ? t : C::ZCOL];
+        const int t = tl_at(li, s < nslots ? s : 0);
+        const int col = s < nslots ? t : C::ZCOL;
+        if constexpr (sizeof(T) == 2) e4[e] = reinterpret_cast<const uint16_t*>(vrow)[col];
+        else e4[e] = reinterpret_cast<const uint32_t*>(vrow)[col];
       }
-      return u32x2{e4[0] | (e4[1] << 16), e4[2] | (e4[3] << 16)};
+      if constexpr (sizeof(T) == 2) return u32x4{e4[0] | (e4[1] << 16), e4[2] | (e4[3] << 16), 0u, 0u};
+      else return u32x4{e4[0], e4[1], e4[2], e4[3]};
     }
   }
 
+  // Eight consecutive slots s0..s0+7 (octet order, N >= 8: one 16-byte read).
   template <bool FULL>
-  __device__ __forceinline__ u32x4 vt_quad_f32(const T* vrow, int s0, int nslots) const {
+  __device__ __forceinline__ u32x4 vt_oct(const T* vrow, int li, int s0, int nslots) const {
     if constexpr (FULL) nslots = 0x7fffffff;
-    if constexpr (N >= 4) {
-      const int s = s0 < nslots ? s0 : 0;
-      const int kk = (tl_at(s >> C::LOG2N) << C::LOG2N) | (s & (N - 1));
-      return *reinterpret_cast<const u32x4*>(vrow + (s0 < nslots ? kk : C::ZCOL));
-    } else if constexpr (N == 2) {
-      u32x2 a[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int s = s0 + 2 * e;
-        const int t = tl_at(s < nslots ? (s >> 1) : 0) << 1;
-        a[e] = *reinterpret_cast<const u32x2*>(vrow + (s < nslots ? t : C::ZCOL));
-      }
-      return u32x4{a[0][0], a[0][1], a[1][0], a[1][1]};
-    } else {
-      u32x4 r;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int s = s0 + e;
-        const int t = tl_at(s < nslots ? s : 0);
-        r[e] = reinterpret_cast<const uint32_t*>(vrow)[s < nslots ? t : C::ZCOL];
-      }
-      return r;
-    }
+    const int s = s0 < nslots ? s0 : 0;
+    const int col = s0 < nslots ? slot_key(li, s) : C::ZCOL;
+    return *reinterpret_cast<const u32x4*>(vrow + col);
   }
 
-  // One softmax pass over NSB sub-blocks of 16 slots starting at sub-block sb0.
-  // FULL: all slots of the pass are < nslots and every key of the chunk is < L.
-  template <int NSB, bool FULL>
-  __device__ __forceinline__ void pass(const T* kl, const T* vl, int sb0, int nslots, int lim,
-                                       int key0) {
-    if constexpr (FULL) {
-      nslots = 0x7fffffff;
-      lim = 0x7fffffff;
-    }
-    // QK^T A rows: a padding slot reads the first kept key; a key past L the
-    // start of its (kept) tile.  Either way the score is a real kept score.
-    int ka[NSB];
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
-      const int slot = 16 * (sb0 + sb) + n;
-      const int sc = slot < nslots ? slot : 0;
-      const int t = tl_at(sc >> C::LOG2N) << C::LOG2N;
-      int key = t | (sc & (N - 1));
-      key = key < lim ? key : t;
-      key = slot < nslots ? key : key0;
-      ka[sb] = key * C::KSTR + VEC * g;
-    }
-    f32x4 s[NSB];
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int sl = 0; sl < C::NSLAB; ++sl) {
-#pragma unroll
-      for (int sb = 0; sb < NSB; ++sb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kl + ka[sb] + C::SLAB * sl);
-        if constexpr (sizeof(T) == 2) s[sb] = Mma<bf16_t>::mac8(a, qf[sl], s[sb]);
-        else s[sb] = Mma<float>::mac4(a, qf[sl], s[sb]);
-      }
-    }
-    // running max in the log2 domain (scale may be negative)
+  // Running-max update for one tile from its NSB score blocks (raw units),
+  // then p = exp2(scale*log2(e)*s - m) in place.
+  template <int NSB>
+  __device__ __forceinline__ void softmax_tile(Tile& tt, f32x4 (&s)[NSB]) {
     const float c = p.scale_log2;
     float mr = s[0][0];
     if (c >= 0.f) {
@@ -386,21 +293,67 @@ struct AttnKernel {
 #pragma unroll
         for (int i = 0; i < 4; ++i) mr = fminf(mr, s[sb][i]);
     }
+    // Rescale only if some lane's scores exceed its reference by more than
+    // RESCALE_STEP; the new reference is then the row max across the lane
+    // groups holding the same query.
     float mx = c * mr;
-    mx = fmaxf(mx, xor_lane16(mx));
-    mx = fmaxf(mx, xor_lane32(mx));
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_STEP) != 0ull) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2_fast(m_run - m_new);  // 0 on the first pass
-      m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(mx > tt.m_run + RESCALE_STEP) != 0ull) {
+      mx = fmaxf(mx, xor_lane16(mx));
+      mx = fmaxf(mx, xor_lane32(mx));
+      const float m_new = fmaxf(tt.m_run, mx);
+      const float alpha = exp2_fast(tt.m_run - m_new);  // 0 on the first pass
+      tt.m_run = m_new;
 #pragma unroll
-      for (int j = 0; j <= C::NDB; ++j) oacc[j] *= alpha;
+      for (int j = 0; j <= C::NDB; ++j) tt.oacc[j] *= alpha;
     }
-    const float nm = -m_run;
+    const float nm = -tt.m_run;
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[sb][i] = exp2_fast(__builtin_fmaf(s[sb][i], c, nm));
+  }
+
+  // One pass of tile TA over NSB 16-slot blocks of list `li` starting at
+  // block sb0.  FULL: all slots of the pass are < nslots and every key of the
+  // chunk is < L.
+  template <int NSB, bool FULL, int TA>
+  __device__ __forceinline__ void pass(const T* kl, const T* vl, int li, int sb0, int nslots,
+                                       int lim, int key0) {
+    if constexpr (FULL) {
+      nslots = 0x7fffffff;
+      lim = 0x7fffffff;
+    }
+    constexpr int NPAIR = C::OCT ? NSB / 2 : 0;   // blocks 0..2*NPAIR-1 use the octet order
+    const int base = 16 * sb0;
+    // QK^T A rows: a padding slot reads the first kept key; a key past L the
+    // start of its (kept) tile.  Either way the score is a real kept score.
+    int ka[NSB];
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+      int slot;
+      if (sb < 2 * NPAIR) slot = base + 32 * (sb >> 1) + 8 * (n >> 2) + 4 * (sb & 1) + (n & 3);
+      else slot = base + 16 * sb + n;
+      const int sc = slot < nslots ? slot : 0;
+      const int t = tl_at(li, sc >> C::LOG2N) << C::LOG2N;
+      int key = t | (sc & (N - 1));
+      key = key < lim ? key : t;
+      key = slot < nslots ? key : key0;
+      ka[sb] = key * C::KSTR + VEC * g;
+    }
+    Tile& tt = tile[TA];
+    f32x4 s[NSB];
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sl = 0; sl < C::NSLAB; ++sl) {
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kl + ka[sb] + C::SLAB * sl);
+        if constexpr (sizeof(T) == 2) s[sb] = Mma<bf16_t>::mac8(a, tt.qf[sl], s[sb]);
+        else s[sb] = Mma<float>::mac4(a, tt.qf[sl], s[sb]);
+      }
+    }
+    softmax_tile<NSB>(tt, s);
     // O^T += V^T P^T (and l += P . 1 through the ones row)
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -413,75 +366,111 @@ struct AttnKernel {
           pb[4 + i] = a1 < NSB ? (__bf16)s[a1 < NSB ? a1 : a0][i] : (__bf16)0.f;
         }
         const u32x4 bop = __builtin_bit_cast(u32x4, pb);
-        const int sA = 16 * (sb0 + a0) + 4 * g;
-        const int sB = 16 * (sb0 + a1) + 4 * g;
+        const bool oct = pp < NPAIR;
+        const int sO = base + 32 * pp + 8 * g;          // octet order
+        const int sA = base + 16 * a0 + 4 * g;          // quad order
+        const int sB = base + 16 * a1 + 4 * g;
 #pragma unroll
         for (int j = 0; j <= C::NDB; ++j) {
           const T* vrow = vl + (j < C::NDB ? 16 * j + n : D) * C::VSTR;
-          const u32x2 x0 = vt_quad_b16<FULL>(vrow, sA, nslots);
-          const u32x2 x1 = a1 < NSB ? vt_quad_b16<FULL>(vrow, sB, nslots)
-                                    : *reinterpret_cast<const u32x2*>(vrow + C::ZCOL);
-          oacc[j] = Mma<bf16_t>::mac8(u32x4{x0[0], x0[1], x1[0], x1[1]}, bop, oacc[j]);
+          u32x4 av;
+          if (oct) {
+            av = vt_oct<FULL>(vrow, li, sO, nslots);
+          } else {
+            const u32x4 x0 = vt_quad<FULL>(vrow, li, sA, nslots);
+            u32x4 x1;
+            if (a1 < NSB) x1 = vt_quad<FULL>(vrow, li, sB, nslots);
+            else x1 = *reinterpret_cast<const u32x4*>(vrow + C::ZCOL);
+            av = u32x4{x0[0], x0[1], x1[0], x1[1]};
+          }
+          tt.oacc[j] = Mma<bf16_t>::mac8(av, bop, tt.oacc[j]);
         }
       }
     } else {
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb) {
-        const u32x4 bop = __builtin_bit_cast(u32x4, s[sb]);
-        const int sA = 16 * (sb0 + sb) + 4 * g;
+        const int sA = base + 16 * sb + 4 * g;
 #pragma unroll
         for (int j = 0; j <= C::NDB; ++j) {
           const T* vrow = vl + (j < C::NDB ? 16 * j + n : D) * C::VSTR;
-          oacc[j] = Mma<float>::mac4(vt_quad_f32<FULL>(vrow, sA, nslots), bop, oacc[j]);
+          const u32x4 av = vt_quad<FULL>(vrow, li, sA, nslots);
+          tt.oacc[j] = Mma<float>::mac4(av, __builtin_bit_cast(u32x4, s[sb]), tt.oacc[j]);
         }
       }
     }
   }
 
-  __device__ __forceinline__ void compute_chunk(int c, int buf, const uint32_t (&mreg)[C::MW]) {
-    // -- compaction of this wave's mask bits for the chunk's key tiles --
+  // Compact mask list `li` for chunk c from its mask words; returns slots.
+  __device__ __forceinline__ int compact(int li, int c, const uint32_t (&mw)[C::MW]) {
     const int first = c * C::TPC;
     uint32_t nk = 0;
 #pragma unroll
     for (int win = 0; win < C::NWIN; ++win) {
       uint64_t bits;
       if constexpr (C::WINT == 64) {
-        bits = (uint64_t)uniform_u32(mreg[2 * win]) | ((uint64_t)uniform_u32(mreg[2 * win + 1]) << 32);
+        bits = (uint64_t)uniform_u32(mw[2 * win]) | ((uint64_t)uniform_u32(mw[2 * win + 1]) << 32);
       } else {
-        const uint32_t w = uniform_u32(mreg[0]) >> (first & 31);
+        const uint32_t w = uniform_u32(mw[0]) >> (first & 31);
         bits = C::WINT == 32 ? (uint64_t)w : (uint64_t)(w & ((1u << C::WINT) - 1u));
       }
       const int room = p.T_k - first - win * C::WINT;  // valid tiles left in the row
       if (room < C::WINT) bits = room <= 0 ? 0ull : (bits & ((1ull << room) - 1ull));
       nk += wave_compact64(bits, win * C::WINT, nk,
-                           [&](uint32_t pos, int val) { sm.tl[wave][pos] = (uint8_t)val; });
+                           [&](uint32_t pos, int val) { sm.tl[wave][li][pos] = (uint8_t)val; });
     }
-    const int nslots = (int)nk * N;
-    if (nslots == 0) return;
     __builtin_amdgcn_wave_barrier();
-    const T* kl = sm.k[buf];
-    const T* vl = sm.vt[buf];
-    const int lim = L - c * KC;              // keys of this chunk that exist
-    const int key0 = tl_at(0) << C::LOG2N;   // first kept key of the chunk
+    return (int)nk * N;
+  }
+
+  // Passes of tile TA over the nslots slots of list `li`: blocks of PASS
+  // 16-slot sub-blocks, then one shorter pass for the rest.
+  template <int TA>
+  __device__ __forceinline__ void run_list(const T* kl, const T* vl, int li, int nslots, int lim) {
+    constexpr int PASS = 2;
+    const int key0 = tl_at(li, 0) << C::LOG2N;   // first kept key of the chunk
     const int nsb = (nslots + 15) >> 4;
     const bool full_chunk = lim >= KC;
     int sb0 = 0;
-    for (; sb0 + 4 <= nsb; sb0 += 4) {
-      if (full_chunk && 16 * (sb0 + 4) <= nslots) pass<4, true>(kl, vl, sb0, nslots, lim, key0);
-      else pass<4, false>(kl, vl, sb0, nslots, lim, key0);
+    for (; sb0 + PASS <= nsb; sb0 += PASS) {
+      if (full_chunk && 16 * (sb0 + PASS) <= nslots)
+        pass<PASS, true, TA>(kl, vl, li, sb0, nslots, lim, key0);
+      else
+        pass<PASS, false, TA>(kl, vl, li, sb0, nslots, lim, key0);
     }
     const int rem = nsb - sb0;
     const bool full_tail = full_chunk && (nslots & 15) == 0;
-    if (rem == 3) {
-      if (full_tail) pass<3, true>(kl, vl, sb0, nslots, lim, key0);
-      else pass<3, false>(kl, vl, sb0, nslots, lim, key0);
-    } else if (rem == 2) {
-      if (full_tail) pass<2, true>(kl, vl, sb0, nslots, lim, key0);
-      else pass<2, false>(kl, vl, sb0, nslots, lim, key0);
-    } else if (rem == 1) {
-      if (full_tail) pass<1, true>(kl, vl, sb0, nslots, lim, key0);
-      else pass<1, false>(kl, vl, sb0, nslots, lim, key0);
+    if constexpr (PASS > 3) {
+      if (rem == 3) {
+        if (full_tail) pass<3, true, TA>(kl, vl, li, sb0, nslots, lim, key0);
+        else pass<3, false, TA>(kl, vl, li, sb0, nslots, lim, key0);
+      }
     }
+    if constexpr (PASS > 2) {
+      if (rem == 2) {
+        if (full_tail) pass<2, true, TA>(kl, vl, li, sb0, nslots, lim, key0);
+        else pass<2, false, TA>(kl, vl, li, sb0, nslots, lim, key0);
+      }
+    }
+    if (rem == 1) {
+      if (full_tail) pass<1, true, TA>(kl, vl, li, sb0, nslots, lim, key0);
+      else pass<1, false, TA>(kl, vl, li, sb0, nslots, lim, key0);
+    }
+  }
+
+  // Both tiles of a wave lie in one mask row when M >= 32 (row0 is a
+  // multiple of 32), and then share one compacted list; the passes stay per
+  // tile (running both tiles through one pass needs more registers than two
+  // waves per SIMD leave).
+  __device__ __forceinline__ void compute_chunk(int c, int buf, const uint32_t (&mw)[2][C::MW],
+                                                bool same_row, bool act1) {
+    const T* kl = sm.k[buf];
+    const T* vl = sm.vt[buf];
+    const int lim = L - c * KC;  // keys of this chunk that exist
+    const int n0 = compact(0, c, mw[0]);
+    const int l1 = same_row ? 0 : 1;
+    const int n1 = !act1 ? 0 : same_row ? n0 : compact(1, c, mw[1]);
+    if (n0 > 0) run_list<0>(kl, vl, 0, n0, lim);
+    if (n1 > 0) run_list<1>(kl, vl, l1, n1, lim);
   }
 
   __device__ __forceinline__ void run() {
@@ -496,55 +485,66 @@ struct AttnKernel {
     const size_t head_off = (size_t)bh * (size_t)L * D;
     const T* __restrict__ qg = reinterpret_cast<const T*>(p.q) + head_off;
     kg = reinterpret_cast<const T*>(p.k) + head_off;
-    vg = reinterpret_cast<const T*>(p.v) + head_off;
-    row0 = qb * (16 * W) + 16 * wave;
-    active = row0 < L;
-    const int mrow = active ? row0 / p.M : 0;
-    mask_row = p.mask + ((size_t)bh * p.T_q + (size_t)mrow) * p.words;
+    vtg = reinterpret_cast<const T*>(p.vt) + (size_t)bh * C::VROWS * p.L_pad;
 
-    // Q fragment: lane (g, n) holds Q[row0+n][SLAB*s + VEC*g .. +VEC)
-    {
-      const int r = row0 + n < L ? row0 + n : L - 1;
+    row0 = qb * C::ROWS + 32 * wave;
+    const bool act0 = row0 < L, act1 = row0 + 16 < L;
+    const bool same_row = p.M >= 32;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r = row0 + 16 * t;
+      const int mrow = r < L ? r / p.M : 0;
+      mask_row[t] = p.mask + ((size_t)bh * p.T_q + (size_t)mrow) * p.words;
+      const int rq = r + n < L ? r + n : L - 1;
 #pragma unroll
       for (int s = 0; s < C::NSLAB; ++s)
-        qf[s] = *reinterpret_cast<const u32x4*>(qg + (size_t)r * D + C::SLAB * s + VEC * g);
-      if (row0 + n >= L)
+        tile[t].qf[s] = *reinterpret_cast<const u32x4*>(qg + (size_t)rq * D + C::SLAB * s + VEC * g);
+      if (r + n >= L)
 #pragma unroll
-        for (int s = 0; s < C::NSLAB; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
+        for (int s = 0; s < C::NSLAB; ++s) tile[t].qf[s] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j <= C::NDB; ++j) tile[t].oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      tile[t].m_run = -INFINITY;
     }
-#pragma unroll
-    for (int j = 0; j <= C::NDB; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_run = -INFINITY;
 
-    zero_pad_columns();
+    // Chunks are visited in a rotated order (the online softmax does not
+    // depend on the order): neighbouring work-groups share an XCD and its L2,
+    // and each starts one chunk behind the previous one.
     const int n_chunks = (L + KC - 1) / KC;
-    uint32_t mcur[C::MW], mnext[C::MW];
-    load_chunk(0, mcur);
-    store_chunk(0, 0);
+    const int rot = n_chunks - 1 - (int)((blockIdx.x >> 3) % (unsigned)n_chunks);
+    auto phys = [&](int c) { const int x = c + rot; return x >= n_chunks ? x - n_chunks : x; };
+    uint32_t mcur[2][C::MW], mnext[2][C::MW];
+    issue_chunk(phys(0), 0, mcur);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int c = 0; c < n_chunks; ++c) {
       const int buf = c & 1;
       const bool more = c + 1 < n_chunks;
-      if (more) load_chunk(c + 1, mnext);
-      if (active) compute_chunk(c, buf, mcur);
+      // buffer buf^1 was last read in iteration c-1, which every wave has left
+      if (more) issue_chunk(phys(c + 1), buf ^ 1, mnext);
+      if (act0) compute_chunk(phys(c), buf, mcur, same_row, act1);
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of chunk c+1 have landed
+      __syncthreads();                 // ... and every other wave's
       if (more) {
-        store_chunk(c + 1, buf ^ 1);
 #pragma unroll
-        for (int i = 0; i < C::MW; ++i) mcur[i] = mnext[i];
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < C::MW; ++i) mcur[t][i] = mnext[t][i];
       }
-      __syncthreads();
     }
 
     // normalise and store
-    if (!active) return;
-    const float l_tot = oacc[C::NDB][0];
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int r = row0 + n;
-    if (r < L) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r = row0 + 16 * t + n;
+      if (r >= L) continue;
+      Tile& tt = tile[t];
+      const float l_tot = tt.oacc[C::NDB][0];
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       T* og = reinterpret_cast<T*>(p.o) + head_off + (size_t)r * D;
 #pragma unroll
       for (int j = 0; j < C::NDB; ++j) {
-        const f32x4 val = oacc[j] * inv;
+        const f32x4 val = tt.oacc[j] * inv;
         if constexpr (sizeof(T) == 2) {
           bf16x4 ob;
 #pragma unroll
@@ -556,11 +556,55 @@ struct AttnKernel {
       }
       if (p.lse != nullptr && g == 0) {
         p.lse[(size_t)bh * L + r] =
-            l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+            l_tot > 0.f ? (tt.m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
       }
     }
   }
 };
+
+// Packs V [B*H][L][D] into V^T [B*H][D + 1][L_pad]: row d < D holds V[., d]
+// for keys < L and zeros up to L_pad; row D holds ones for keys < L and
+// zeros after (the softmax denominator is accumulated against it).  One
+// work-group per 64 keys of one (b, h): 16-byte coalesced reads of the rows,
+// a transpose through LDS, 16-byte coalesced writes of the columns.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void vt_pack_kernel(const T* __restrict__ v, T* __restrict__ vt,
+                                                      int L, int L_pad) {
+  constexpr int VEC = ElemTraits<T>::VEC;
+  constexpr int CPR = D / VEC;       // 16-byte chunks per V row
+  constexpr int TS = D + 2;          // LDS row stride (elements), odd word stride for bf16
+  __shared__ T tile[64 * TS];
+  const int bh = blockIdx.y;
+  const int k0 = blockIdx.x * 64;
+  const T* src = v + ((size_t)bh * L) * D;
+  for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
+    const int r = i / CPR, ch = i % CPR;
+    const int key = k0 + r;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (key < L) x = *reinterpret_cast<const u32x4*>(src + (size_t)key * D + ch * VEC);
+    const T* xe = reinterpret_cast<const T*>(&x);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) tile[r * TS + ch * VEC + e] = xe[e];
+  }
+  __syncthreads();
+  constexpr int GPR = 64 / VEC;      // 16-byte groups per output row segment
+  T* dst = vt + (size_t)bh * (D + 1) * L_pad + k0;
+  for (int i = threadIdx.x; i < (D + 1) * GPR; i += 256) {
+    const int d = i / GPR, kg = i % GPR;
+    T out[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const int r = kg * VEC + e;
+      if (d < D) {
+        out[e] = tile[r * TS + d];
+      } else {
+        if constexpr (sizeof(T) == 2) out[e] = (T)(k0 + r < L ? 0x3f80u : 0u);
+        else out[e] = k0 + r < L ? 1.f : 0.f;
+      }
+    }
+    *reinterpret_cast<u32x4*>(dst + (size_t)d * L_pad + kg * VEC) = *reinterpret_cast<const u32x4*>(out);
+  }
+}
 
 template <typename T, int D, int N, int KC, int W>
 __global__ __launch_bounds__(64 * W) void attn_fwd_kernel(AttnParams p) {

@@ -12,7 +12,7 @@ hipError_t launch_attn_cfg(const AttnLaunch& a) {
   AttnParams p;
   p.q = a.q;
   p.k = a.k;
-  p.v = a.v;
+  p.vt = a.workspace;
   p.mask = a.mask;
   p.o = a.o;
   p.lse = a.lse;
@@ -22,9 +22,13 @@ hipError_t launch_attn_cfg(const AttnLaunch& a) {
   p.T_q = (pr.L + pr.M - 1) / pr.M;
   p.T_k = (pr.L + pr.N - 1) / pr.N;
   p.words = (p.T_k + 31) / 32;
-  p.n_qblocks = (pr.L + 16 * W - 1) / (16 * W);
+  p.L_pad = attention_l_pad(pr.L);
+  p.n_qblocks = (pr.L + 32 * W - 1) / (32 * W);
   p.scale_log2 = a.scale * 1.4426950408889634f;
   const long long blocks = (long long)pr.B * pr.H * p.n_qblocks;
+  hipLaunchKernelGGL((vt_pack_kernel<T, D>), dim3((unsigned)(p.L_pad / 64), (unsigned)(pr.B * pr.H)),
+                     dim3(256), 0, a.stream, static_cast<const T*>(a.v), static_cast<T*>(a.workspace),
+                     pr.L, p.L_pad);
   hipLaunchKernelGGL((attn_fwd_kernel<T, D, N, KC, W>), dim3((unsigned)blocks), dim3(64 * W), 0,
                      a.stream, p);
   return hipGetLastError();
