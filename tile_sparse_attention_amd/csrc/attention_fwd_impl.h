@@ -71,7 +71,7 @@ constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 // Fourth word of a raw (unformatted, unswizzled) buffer resource on gfx9.
 constexpr int kBufferFlags = 0x00020000;
 
-template <typename T, int D, int N, int KC, int W>
+template <typename T, int D, int N, int KC, int W, int TPW>
 struct AttnCfg {
   static constexpr int VEC = ElemTraits<T>::VEC;   // elements per 16 bytes
   static constexpr int SLAB = 4 * VEC;             // d covered by one 16-byte read per lane group
@@ -83,7 +83,7 @@ struct AttnCfg {
   static constexpr int VROWS = D + 1;              // V^T rows: d = 0..D-1 and the ones row
   static constexpr int ZCOL = KC;                  // first zero column of V^T
   static constexpr int NT = 64 * W;
-  static constexpr int ROWS = 32 * W;              // query rows per work-group
+  static constexpr int ROWS = 16 * TPW * W;        // query rows per work-group
   static constexpr int CPR = D / VEC;              // 16-byte chunks per K/V row
   static constexpr int TPC = KC / N;               // key tiles per chunk
   static constexpr int WINT = TPC < 64 ? TPC : 64; // tiles per compaction window
@@ -131,19 +131,23 @@ template <> struct Mma<float> {
   }
 };
 
-template <typename T, int D, int N, int KC, int W>
+template <typename T, int D, int N, int KC, int W, int TPW>
 struct AttnKernel {
-  using C = AttnCfg<T, D, N, KC, W>;
+  using C = AttnCfg<T, D, N, KC, W, TPW>;
   static constexpr int VEC = C::VEC;
   static constexpr float RESCALE_STEP = 8.f;  // log2 units a row max may grow before rescaling
+  // With four waves per SIMD (one tile per wave) the register budget is 128:
+  // loads of a pass are then not all hoisted ahead of their MFMAs; the other
+  // waves hide the latency instead.
+  static constexpr bool LIMIT_ILP = TPW == 1;
 
   struct Smem {
     __attribute__((aligned(16))) T k[2][C::NI_K * 1024 / sizeof(T)];
     __attribute__((aligned(16))) T vt[2][C::NI_V * 1024 / sizeof(T)];
-    uint8_t tl[W][2][C::TPC];
+    uint8_t tl[W][TPW][C::TPC];
   };
 
-  // per-tile state (a wave owns two 16-row query tiles)
+  // per-tile state (a wave owns TPW 16-row query tiles)
   struct Tile {
     u32x4 qf[C::NSLAB];       // Q fragment: lane (g, n) holds Q[row+n][SLAB*s + VEC*g .. +VEC)
     f32x4 oacc[C::NDB + 1];   // O^T blocks and, last, the row sums l
@@ -156,8 +160,8 @@ struct AttnKernel {
   int L, bh, row0;
   const T* __restrict__ kg;
   const T* __restrict__ vtg;
-  const uint32_t* __restrict__ mask_row[2];
-  Tile tile[2];
+  const uint32_t* __restrict__ mask_row[TPW];
+  Tile tile[TPW];
 
   __device__ __forceinline__ AttnKernel(const AttnParams& pp, Smem& s) : p(pp), sm(s) {}
 
@@ -183,13 +187,17 @@ struct AttnKernel {
   // wave's share) and the loads of both tiles' mask words for it.  Nothing
   // waits here: the caller waits for the vector-memory counter and syncs the
   // work-group before the buffer is read.
-  __device__ __forceinline__ void issue_chunk(int c, int buf, uint32_t (&mreg)[2][C::MW]) {
+  __device__ __forceinline__ void issue_chunk(int c, int buf, uint32_t (&mreg)[TPW][C::MW]) {
     const int kbase = c * KC;
     const int rows = L - kbase < KC ? L - kbase : KC;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kg + (size_t)kbase * D), (short)0, rows * C::KRB, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vtg + kbase), (short)0, (C::VROWS * p.L_pad - kbase) * (int)sizeof(T), kBufferFlags);
+    // The per-lane offsets are loop-invariant; recomputing them (a few VALU
+    // per load) keeps them out of the register budget instead of holding or
+    // spilling them across the chunk loop.
+    const int ln = lane + opaque_zero();
 #pragma unroll
     for (int u = 0; u < C::NI_W; ++u) {
       const int I = wave + W * u;
@@ -197,18 +205,18 @@ struct AttnKernel {
         if (I < C::NI_K) {
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               rk, (__attribute__((address_space(3))) void*)((char*)sm.k[buf] + I * 1024), 16,
-              dma_offset(I, lane), 0, 0, 0);
+              dma_offset(I, ln), 0, 0, 0);
         } else {
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               rv, (__attribute__((address_space(3))) void*)((char*)sm.vt[buf] + (I - C::NI_K) * 1024),
-              16, dma_offset(I, lane), 0, 0, 0);
+              16, dma_offset(I, ln), 0, 0, 0);
         }
       }
     }
     // mask words holding key tiles [c*TPC, c*TPC + TPC) of each tile's row
     const int w0 = (c * C::TPC) >> 5;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
       for (int i = 0; i < C::MW; ++i) {
         const int wi = w0 + i < p.words ? w0 + i : p.words - 1;
@@ -352,6 +360,7 @@ struct AttnKernel {
         if constexpr (sizeof(T) == 2) s[sb] = Mma<bf16_t>::mac8(a, tt.qf[sl], s[sb]);
         else s[sb] = Mma<float>::mac4(a, tt.qf[sl], s[sb]);
       }
+      if constexpr (LIMIT_ILP) __builtin_amdgcn_sched_barrier(0);
     }
     softmax_tile<NSB>(tt, s);
     // O^T += V^T P^T (and l += P . 1 through the ones row)
@@ -384,6 +393,9 @@ struct AttnKernel {
             av = u32x4{x0[0], x0[1], x1[0], x1[1]};
           }
           tt.oacc[j] = Mma<bf16_t>::mac8(av, bop, tt.oacc[j]);
+          if constexpr (LIMIT_ILP) {
+            if (j % 3 == 2) __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
     } else {
@@ -457,20 +469,22 @@ struct AttnKernel {
     }
   }
 
-  // Both tiles of a wave lie in one mask row when M >= 32 (row0 is a
-  // multiple of 32), and then share one compacted list; the passes stay per
-  // tile (running both tiles through one pass needs more registers than two
-  // waves per SIMD leave).
-  __device__ __forceinline__ void compute_chunk(int c, int buf, const uint32_t (&mw)[2][C::MW],
+  // With two tiles per wave both lie in one mask row when M >= 32 (row0 is
+  // a multiple of 32) and share one compacted list; the passes stay per tile
+  // (running both tiles through one pass needs more registers than two waves
+  // per SIMD leave).
+  __device__ __forceinline__ void compute_chunk(int c, int buf, const uint32_t (&mw)[TPW][C::MW],
                                                 bool same_row, bool act1) {
     const T* kl = sm.k[buf];
     const T* vl = sm.vt[buf];
     const int lim = L - c * KC;  // keys of this chunk that exist
     const int n0 = compact(0, c, mw[0]);
-    const int l1 = same_row ? 0 : 1;
-    const int n1 = !act1 ? 0 : same_row ? n0 : compact(1, c, mw[1]);
     if (n0 > 0) run_list<0>(kl, vl, 0, n0, lim);
-    if (n1 > 0) run_list<1>(kl, vl, l1, n1, lim);
+    if constexpr (TPW == 2) {
+      const int l1 = same_row ? 0 : 1;
+      const int n1 = !act1 ? 0 : same_row ? n0 : compact(1, c, mw[1]);
+      if (n1 > 0) run_list<1>(kl, vl, l1, n1, lim);
+    }
   }
 
   __device__ __forceinline__ void run() {
@@ -487,11 +501,11 @@ struct AttnKernel {
     kg = reinterpret_cast<const T*>(p.k) + head_off;
     vtg = reinterpret_cast<const T*>(p.vt) + (size_t)bh * C::VROWS * p.L_pad;
 
-    row0 = qb * C::ROWS + 32 * wave;
-    const bool act0 = row0 < L, act1 = row0 + 16 < L;
+    row0 = qb * C::ROWS + 16 * TPW * wave;
+    const bool act0 = row0 < L, act1 = TPW == 2 && row0 + 16 < L;
     const bool same_row = p.M >= 32;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < TPW; ++t) {
       const int r = row0 + 16 * t;
       const int mrow = r < L ? r / p.M : 0;
       mask_row[t] = p.mask + ((size_t)bh * p.T_q + (size_t)mrow) * p.words;
@@ -513,7 +527,7 @@ struct AttnKernel {
     const int n_chunks = (L + KC - 1) / KC;
     const int rot = n_chunks - 1 - (int)((blockIdx.x >> 3) % (unsigned)n_chunks);
     auto phys = [&](int c) { const int x = c + rot; return x >= n_chunks ? x - n_chunks : x; };
-    uint32_t mcur[2][C::MW], mnext[2][C::MW];
+    uint32_t mcur[TPW][C::MW], mnext[TPW][C::MW];
     issue_chunk(phys(0), 0, mcur);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -527,7 +541,7 @@ struct AttnKernel {
       __syncthreads();                 // ... and every other wave's
       if (more) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < TPW; ++t)
 #pragma unroll
           for (int i = 0; i < C::MW; ++i) mcur[t][i] = mnext[t][i];
       }
@@ -535,7 +549,7 @@ struct AttnKernel {
 
     // normalise and store
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < TPW; ++t) {
       const int r = row0 + 16 * t + n;
       if (r >= L) continue;
       Tile& tt = tile[t];
@@ -606,9 +620,9 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const T* __restrict__ v, T
   }
 }
 
-template <typename T, int D, int N, int KC, int W>
+template <typename T, int D, int N, int KC, int W, int TPW>
 __global__ __launch_bounds__(64 * W) void attn_fwd_kernel(AttnParams p) {
-  using K = AttnKernel<T, D, N, KC, W>;
+  using K = AttnKernel<T, D, N, KC, W, TPW>;
   __shared__ __attribute__((aligned(16))) typename K::Smem sm;
   K k(p, sm);
   k.run();

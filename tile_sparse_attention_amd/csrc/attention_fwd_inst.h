@@ -6,7 +6,7 @@
 
 namespace tsa {
 
-template <typename T, int D, int N, int KC, int W>
+template <typename T, int D, int N, int KC, int W, int TPW>
 hipError_t launch_attn_cfg(const AttnLaunch& a) {
   const tsa_problem_t& pr = *a.p;
   AttnParams p;
@@ -23,36 +23,47 @@ hipError_t launch_attn_cfg(const AttnLaunch& a) {
   p.T_k = (pr.L + pr.N - 1) / pr.N;
   p.words = (p.T_k + 31) / 32;
   p.L_pad = attention_l_pad(pr.L);
-  p.n_qblocks = (pr.L + 32 * W - 1) / (32 * W);
+  p.n_qblocks = (pr.L + 16 * TPW * W - 1) / (16 * TPW * W);
   p.scale_log2 = a.scale * 1.4426950408889634f;
   const long long blocks = (long long)pr.B * pr.H * p.n_qblocks;
   hipLaunchKernelGGL((vt_pack_kernel<T, D>), dim3((unsigned)(p.L_pad / 64), (unsigned)(pr.B * pr.H)),
                      dim3(256), 0, a.stream, static_cast<const T*>(a.v), static_cast<T*>(a.workspace),
                      pr.L, p.L_pad);
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, N, KC, W>), dim3((unsigned)blocks), dim3(64 * W), 0,
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, N, KC, W, TPW>), dim3((unsigned)blocks), dim3(64 * W), 0,
                      a.stream, p);
   return hipGetLastError();
 }
 
-// Chunk size KC and waves per work-group W per (element type, head dim):
-// both keep the double-buffered K and V^T chunks within the 160 KB of LDS.
-template <typename T, int D> struct AttnShape;
-template <> struct AttnShape<bf16_t, 128> { static constexpr int KC = 128, W = 8; };
-template <> struct AttnShape<bf16_t, 64> { static constexpr int KC = 128, W = 8; };
-template <> struct AttnShape<float, 128> { static constexpr int KC = 64, W = 8; };
-template <> struct AttnShape<float, 64> { static constexpr int KC = 64, W = 4; };
+// Chunk size KC, waves per work-group W and 16-row tiles per wave TPW per
+// (element type, head dim, N): the double-buffered K and V^T chunks stay
+// within the 160 KB of LDS, and every variant fits the register file without
+// spilling (checked at build time).  Sixteen one-tile waves (four per SIMD)
+// hide latency best; the N < 4 gathers need the larger budget of eight
+// two-tile waves.
+template <typename T, int D, int N> struct AttnShape;
+template <int N> struct AttnShape<bf16_t, 128, N> {
+  static constexpr int KC = 128, W = N >= 4 ? 16 : 8, TPW = N >= 4 ? 1 : 2;
+};
+template <int N> struct AttnShape<bf16_t, 64, N> { static constexpr int KC = 128, W = 16, TPW = 1; };
+template <int N> struct AttnShape<float, 128, N> { static constexpr int KC = 64, W = 8, TPW = 2; };
+template <int N> struct AttnShape<float, 64, N> { static constexpr int KC = 64, W = 4, TPW = 2; };
+
+template <typename T, int D, int N>
+hipError_t launch_attn_n(const AttnLaunch& a) {
+  using S = AttnShape<T, D, N>;
+  return launch_attn_cfg<T, D, N, S::KC, S::W, S::TPW>(a);
+}
 
 template <typename T, int D>
 hipError_t launch_attn_d(const AttnLaunch& a) {
-  constexpr int KC = AttnShape<T, D>::KC, W = AttnShape<T, D>::W;
   switch (a.p->N) {
-    case 1: return launch_attn_cfg<T, D, 1, KC, W>(a);
-    case 2: return launch_attn_cfg<T, D, 2, KC, W>(a);
-    case 4: return launch_attn_cfg<T, D, 4, KC, W>(a);
-    case 8: return launch_attn_cfg<T, D, 8, KC, W>(a);
-    case 16: return launch_attn_cfg<T, D, 16, KC, W>(a);
-    case 32: return launch_attn_cfg<T, D, 32, KC, W>(a);
-    case 64: return launch_attn_cfg<T, D, 64, KC, W>(a);
+    case 1: return launch_attn_n<T, D, 1>(a);
+    case 2: return launch_attn_n<T, D, 2>(a);
+    case 4: return launch_attn_n<T, D, 4>(a);
+    case 8: return launch_attn_n<T, D, 8>(a);
+    case 16: return launch_attn_n<T, D, 16>(a);
+    case 32: return launch_attn_n<T, D, 32>(a);
+    case 64: return launch_attn_n<T, D, 64>(a);
     default: return hipErrorInvalidValue;
   }
 }

@@ -82,4 +82,12 @@ __device__ __forceinline__ float xor_lane32(float x) { return __shfl_xor(x, 32);
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A zero the compiler cannot see through: adding it to an index keeps a
+// loop-invariant computation inside the loop (recomputed, not kept live).
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+  return z;
+}
+
 }  // namespace tsa
