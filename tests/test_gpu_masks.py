@@ -1,0 +1,124 @@
+"""GPU mask generator and mask compaction against the host generator and the
+CPU oracle (bit-exact), through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import mask_to_np, say, to_dev_mask, torch_or_skip
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_mask(w):
+    import tile_sparse_attention_amd as T
+    return T.maskgen_hash(w.B, w.H, w.L, w.M, w.N, **W.hash_params(w))
+
+
+def _rows_of(bits_np, rows):
+    return np.stack([bits_np[b, h, i] for b, h, i in rows])
+
+
+@pytest.mark.parametrize("name", ["tiny", "wan480_fine", "wan720_n1"])
+def test_maskgen_matches_host_generator(name):
+    torch = torch_or_skip()
+    w = W.get(name)
+    say(f"maskgen {name}")
+    m = mask_to_np(_gpu_mask(w))
+    rng = np.random.default_rng(1)
+    rows = [(0, h, i) for h in range(w.H) for i in {0, w.T_q - 1, int(rng.integers(w.T_q))}]
+    host = W.pack_bits(W.mask_rows_bool(w, rows))
+    assert np.array_equal(_rows_of(m, rows), host)
+    # padding bits are zero
+    if w.T_k % 32:
+        assert np.all(m[..., -1] >> np.uint32(w.T_k % 32) == 0)
+    torch.cuda.synchronize()
+
+
+def test_maskgen_small_shapes_full():
+    torch_or_skip()
+    for L, M, N in [(1, 16, 1), (100, 16, 8), (1000, 32, 2), (777, 64, 64)]:
+        w = W.Workload("g", 2, 3, L, 64, M, N, "bf16",
+                       W.MaskRecipe("hash", p_near=0.37, p_far=0.11, frame_tokens=50,
+                                    frame_radius=1), 77)
+        say(f"maskgen full L={L} {M}x{N}")
+        assert np.array_equal(mask_to_np(_gpu_mask(w)), W.mask_bits(w))
+
+
+def _compact(bits_dev, w, cap=None):
+    import tile_sparse_attention_amd as T
+    rp, ci = T.mask_compact(bits_dev, w.L, w.M, w.N, col_capacity=cap)
+    return rp.cpu().numpy(), ci.cpu().numpy()
+
+
+@pytest.mark.parametrize("L,M,N", [(512, 16, 16), (1000, 16, 1), (1000, 16, 8), (3000, 64, 64),
+                                   (77, 16, 2), (1, 16, 4)])
+def test_compaction_bit_exact_small(L, M, N):
+    torch_or_skip()
+    w = W.Workload("c", 2, 3, L, 64, M, N, "bf16", W.MaskRecipe("hash", p_near=0.3, p_far=0.3), 5)
+    say(f"compaction L={L} {M}x{N}")
+    bits = W.mask_bits(w)
+    if w.T_k % 32:                                   # set the padding bits: they must be ignored
+        bits[..., -1] |= np.uint32(0xFFFFFFFF) << np.uint32(w.T_k % 32)
+    rp, ci = _compact(to_dev_mask(bits), w)
+    orp, oci = oracle.compact(bits, w.T_k)
+    assert np.array_equal(rp, orp) and np.array_equal(ci, oci)
+
+
+def test_compaction_capacity_clipping():
+    torch_or_skip()
+    w = W.Workload("c", 1, 2, 640, 64, 16, 8, "bf16", W.MaskRecipe("hash", p_near=0.4, p_far=0.4), 9)
+    say("compaction capacity clip")
+    bits = W.mask_bits(w)
+    orp, oci = oracle.compact(bits, w.T_k)
+    cap = int(orp[-1]) // 2
+    rp, ci = _compact(to_dev_mask(bits), w, cap=cap)
+    assert np.array_equal(rp, orp)
+    assert np.array_equal(ci[:cap], oci[:cap])
+
+
+def test_compaction_empty_and_full_rows():
+    torch_or_skip()
+    w = W.Workload("c", 1, 1, 300, 64, 16, 4, "bf16", W.MaskRecipe("ones"), 1)
+    bits = W.mask_bits(w)
+    bits[0, 0, ::2] = 0
+    say("compaction empty/full rows")
+    rp, ci = _compact(to_dev_mask(bits), w)
+    orp, oci = oracle.compact(bits, w.T_k)
+    assert np.array_equal(rp, orp) and np.array_equal(ci, oci)
+
+
+def test_compaction_wan480_fine_full():
+    """Every row of the 40-head 16x8 bitmap (host-generated), bit-exact."""
+    torch_or_skip()
+    w = W.get("wan480_fine")
+    say("compaction wan480_fine full (host mask)")
+    bits = W.mask_bits(w)
+    rp, ci = _compact(to_dev_mask(bits), w)
+    orp, oci = oracle.compact(bits, w.T_k)
+    assert np.array_equal(rp, orp) and np.array_equal(ci, oci)
+
+
+def test_compaction_wan720_n1_sampled_rows():
+    """16x1 on the 75600-token shape: the full lists (2.9e9 entries) are built
+    on the GPU; counts and lists of sampled rows are compared with the oracle
+    applied to the host generator's rows (equal to the GPU mask's rows, which
+    is asserted first)."""
+    torch = torch_or_skip()
+    w = W.get("wan720_n1")
+    say("compaction wan720_n1 sampled rows")
+    m = _gpu_mask(w)
+    rp_d, ci_d = __import__("tile_sparse_attention_amd").mask_compact(m, w.L, w.M, w.N)
+    tiles = W.sample_tiles(w, per_head=16)
+    rows = [(0, h, int(i)) for h in (0, 17, 39) for i in tiles[0, h]]
+    host = W.pack_bits(W.mask_rows_bool(w, rows))
+    assert np.array_equal(_rows_of(mask_to_np(m), rows), host)
+    rp = rp_d.cpu().numpy()
+    for (b, h, i), hr in zip(rows, host):
+        r = (b * w.H + h) * w.T_q + i
+        lst = ci_d[rp[r]:rp[r + 1]].cpu().numpy()
+        _, oci = oracle.compact(hr[None, None, None], w.T_k)
+        assert np.array_equal(lst, oci)
+    assert rp[0] == 0 and np.all(np.diff(rp) >= 0)
+    del ci_d
+    torch.cuda.empty_cache()

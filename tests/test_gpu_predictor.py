@@ -1,0 +1,84 @@
+"""GPU pooled-Q/pooled-K tile-mask predictor against the CPU oracle.
+
+The GPU scores in fp32 and the oracle in fp64, so decisions may differ only
+for scores within a small band around a row's threshold.  Checked per row:
+exactly k tiles kept; every tile whose oracle score is above the oracle's
+k-th largest score by more than delta is kept, every tile below it by more
+than delta is dropped, delta = 1e-4 * max|s| + 1e-6.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import mask_to_np, say, torch_or_skip
+from oracle import predictor as opred
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_rows(gpu_bits, scores, sp):
+    T_k = scores.shape[1]
+    k = opred.topk_count(T_k, sp)
+    keep = oracle.unpack_mask(gpu_bits, T_k)
+    assert np.all(keep.sum(axis=1) == k), "wrong number of kept tiles"
+    if k == 0:
+        return 0
+    srt = -np.sort(-scores, axis=1)
+    thr = srt[:, k - 1]
+    delta = 1e-4 * np.abs(scores).max(axis=1) + 1e-6
+    above = scores > (thr + delta)[:, None]
+    below = scores < (thr - delta)[:, None]
+    assert np.all(keep[above]), "a clearly-above tile was dropped"
+    assert not np.any(keep[below]), "a clearly-below tile was kept"
+    exact = oracle.unpack_mask(opred._pack(opred.predict_keep(scores, sp)), T_k)
+    return int((exact != keep).sum())
+
+
+def _run(q, k, M, N, sp):
+    import tile_sparse_attention_amd as T
+    return mask_to_np(T.predict_mask(q.cuda(), k.cuda(), M, N, sp))
+
+
+@pytest.mark.parametrize("dtype,d,L,M,N,sp", [
+    ("bf16", 128, 1000, 16, 16, 85), ("bf16", 128, 777, 16, 8, 70), ("f32", 64, 512, 16, 16, 50),
+    ("bf16", 64, 300, 32, 1, 90), ("bf16", 128, 16, 16, 16, 85), ("f32", 128, 2000, 64, 64, 0),
+    ("bf16", 128, 4100, 16, 4, 99)])
+def test_predictor_small(dtype, d, L, M, N, sp):
+    torch_or_skip()
+    w = W.Workload("p", 2, 2, L, d, M, N, dtype, W.MaskRecipe("predicted", sparsity_percent=sp),
+                   31 + L, offset_frame_tokens=max(1, L // 5), offset_sigma=0.5)
+    say(f"predictor {dtype} d={d} L={L} {M}x{N} sp={sp}")
+    q, k, _ = W.make_qkv(w)
+    bits = _run(q, k, M, N, sp)
+    for b in range(w.B):
+        for h in range(w.H):
+            s = opred.pooled_scores(q[b, h], k[b, h], M, N)
+            _check_rows(bits[b, h], s, sp)
+
+
+def test_predictor_ties_go_to_smaller_tile():
+    torch = torch_or_skip()
+    say("predictor ties")
+    L, d, M, N = 256, 64, 16, 16
+    q = torch.randn(1, 1, L, d).to(torch.bfloat16)
+    k = torch.randn(1, 1, N, d).repeat(1, 1, L // N, 1).to(torch.bfloat16)   # all key tiles equal
+    bits = _run(q, k, M, N, 50)
+    keep = oracle.unpack_mask(bits[0, 0], L // N)
+    kk = opred.topk_count(L // N, 50)
+    assert np.all(keep[:, :kk]) and not np.any(keep[:, kk:])
+
+
+def test_predictor_hunyuan_sampled_rows():
+    """The 24-head, 118800-token shape with per-frame offsets: sampled rows."""
+    torch_or_skip()
+    w = W.get("hunyuan720").replace(H=4)
+    say("predictor hunyuan720 (4 heads) sampled rows")
+    q, k, _ = W.make_qkv(w)
+    bits = _run(q, k, w.M, w.N, 85)
+    tiles = W.sample_tiles(w, per_head=64)
+    mism = 0
+    for h in range(w.H):
+        s = opred.pooled_scores(q[0, h], k[0, h], w.M, w.N, rows=tiles[0, h])
+        mism += _check_rows(bits[0, h, tiles[0, h]], s, 85)
+    print(f"[predictor] near-threshold decisions differing from fp64: {mism}", flush=True)
