@@ -91,33 +91,42 @@ def time_calls(fn, steps, warmup):
     return wall / steps, sum(per) / len(per), min(per)
 
 
-def cpu_baseline(w, q, k, v, mask, budget_s=15.0):
-    """fp64 oracle on a bounded sample of query tiles of head 0, same metric unit."""
+def cpu_baseline(w, q, k, v, mask, budget_s=20.0):
+    """fp64 oracle on a bounded sample of the workload, in the metric's unit: the
+    first `per_head` of each head's sampled query tiles (tile 0, the last tile and
+    random ones), over all heads, with `per_head` sized to the time budget."""
     import numpy as np
 
     import oracle
     import workloads as W
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    bits_h0 = mask[0, 0].cpu().numpy().view(np.uint32)
-    tiles = W.sample_tiles(w)[0, 0]
-    qh, kh, vh = q[0, 0].cpu(), k[0, 0].cpu(), v[0, 0].cpu()
-    # one probe group to size the sample to the time budget
-    t0 = time.perf_counter()
-    oracle.attention_rows(qh, kh, vh, bits_h0, w.M, w.N, w.scale, tiles[:8], group=8)
-    per_tile = (time.perf_counter() - t0) / 8
-    n = int(max(8, min(len(tiles), budget_s / max(per_tile, 1e-6))))
-    sample = tiles[:n]
-    t0 = time.perf_counter()
-    oracle.attention_rows(qh, kh, vh, bits_h0, w.M, w.N, w.scale, sample, group=16)
-    secs = time.perf_counter() - t0
-    # kept FLOPs of the sampled rows (the oracle itself does dense work)
-    keep = oracle.unpack_mask(bits_h0[sample], w.T_k)
-    m = np.minimum(w.M, w.L - sample * w.M)
+    tiles = W.sample_tiles(w)
+    bits = mask.cpu().numpy().view(np.uint32)
     nj = np.minimum(w.N, w.L - np.arange(w.T_k) * w.N)
-    kept = 4 * w.d * int((m[:, None] * keep * nj[None, :]).sum())
+
+    def run(b, h, sample):
+        oracle.attention_rows(q[b, h], k[b, h], v[b, h], bits[b, h], w.M, w.N, w.scale, sample,
+                              group=16)
+        keep = oracle.unpack_mask(bits[b, h][sample], w.T_k)
+        m = np.minimum(w.M, w.L - sample * w.M)
+        return 4 * w.d * int((m[:, None] * keep * nj[None, :]).sum())
+
+    run(0, 0, tiles[0, 0, :16])                  # warm-up, then a probe that sizes the sample
+    t0 = time.perf_counter()
+    run(0, 0, tiles[0, 0, :16])
+    per_tile = (time.perf_counter() - t0) / 16
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    per_head = int(max(4, min(tiles.shape[2], budget_s / max(per_tile, 1e-6) / len(heads))))
+    kept, secs = 0, 0.0
+    for b, h in heads:
+        t0 = time.perf_counter()
+        kept += run(b, h, tiles[b, h, :per_head])
+        secs += time.perf_counter() - t0
+    n = per_head * len(heads)
     return {"value": kept / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} sampled query tiles ({n * w.M} rows) of head 0, all {w.L} keys, fp64 "
-                      f"numpy, {secs:.1f} s; kept FLOPs of those rows / time"}
+            "sample": f"{per_head} sampled query tiles per head x {len(heads)} heads ({n} tiles, "
+                      f"{n * w.M} query rows) against all {w.L} keys, fp64 numpy, {secs:.1f} s; "
+                      f"kept FLOPs of those rows / time"}
 
 
 def traffic_for(workload: str, sha: str):
@@ -139,6 +148,9 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run one plain device copy of BYTES bytes (calibrates the HBM "
+                         "byte counters of a profiler run) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -151,6 +163,14 @@ def main():
 
     import tile_sparse_attention_amd as T
     import workloads as W
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe}), flush=True)
+        return
     name = args.workload or W.HEADLINE
     w = W.get(name)
     log(f"workload {name}: B={w.B} H={w.H} L={w.L} d={w.d} M={w.M} N={w.N} {w.dtype}")
