@@ -3,7 +3,8 @@
 // b64), bf16 16x16x32 MFMA, v_exp_f32 and fp32 FMA.  Every kernel is
 // in-bounds and exits after a fixed number of iterations.
 //
-//   hipcc --offload-arch=gfx950 -O3 micro/rates.hip -o micro_rates && ./micro_rates
+//   hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops micro/rates.hip -o micro_rates
+//   ./micro_rates
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -73,6 +74,84 @@ __global__ __launch_bounds__(kThreads) void lds_tr16(unsigned* out) {
   if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x1234) out[0] = 1;
 }
 
+
+// Eight independent reads in flight per wave, each result consumed by an
+// empty asm statement (no VALU work in the loop).  32 KB of LDS per
+// work-group, four work-groups (16 waves) per CU.  PAT 0: consecutive lanes
+// read consecutive 16-byte slots; PAT 1: the MFMA-operand pattern of the
+// attention kernel (lane (g, n) reads 16 bytes at byte 16*g of row n, rows
+// 272 bytes apart).
+template <int PAT>
+__global__ __launch_bounds__(kThreads) void lds_b128_ilp(unsigned* out) {
+  __shared__ __attribute__((aligned(16))) unsigned lds[8192];  // 32 KB
+  for (int i = threadIdx.x; i < 8192; i += kThreads) lds[i] = i;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int base = (PAT == 0 ? lane * 16 : (lane & 15) * 272 + (lane >> 4) * 16) + wv * 1024;
+  const char* lb = reinterpret_cast<const char*>(lds) + base;
+  for (int it = 0; it < kIters / 8; ++it) {
+    const char* p = lb + ((it * 2048) & 8191);
+    u32x4 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const u32x4*>(p + u * 1024);
+    asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]),
+                 "v"(x[7]));
+  }
+  if (lane == 64) out[0] = 1;
+}
+
+// LDS operand feed of the attention passes: every 16x16x32 MFMA takes one
+// operand from a 16-byte-per-lane LDS read (1 KB per MFMA), the other from
+// registers.  Reports the MFMA rate reached.
+__global__ __launch_bounds__(kThreads) void mix_lds_mfma(unsigned* out, float seed) {
+  __shared__ __attribute__((aligned(16))) unsigned lds[8192];  // 32 KB
+  for (int i = threadIdx.x; i < 8192; i += kThreads) lds[i] = 0x3f803f80u + (i & 7);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const char* lb = reinterpret_cast<const char*>(lds) + (lane & 15) * 272 + (lane >> 4) * 16 + wv * 1024;
+  bf16x8 b;
+  for (int i = 0; i < 8; ++i) b[i] = (__bf16)(seed + i);
+  f32x4 c0 = {0, 0, 0, 0}, c1 = c0, c2 = c0, c3 = c0;
+  for (int it = 0; it < kIters / 8; ++it) {
+    const char* p = lb + ((it * 2048) & 8191);
+#pragma unroll
+    for (int u = 0; u < 8; u += 4) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(p + u * 1024);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(p + u * 1024 + 1024);
+      const bf16x8 a2 = *reinterpret_cast<const bf16x8*>(p + u * 1024 + 2048);
+      const bf16x8 a3 = *reinterpret_cast<const bf16x8*>(p + u * 1024 + 3072);
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3, b, c3, 0, 0, 0);
+    }
+  }
+  const f32x4 s = c0 + c1 + c2 + c3;
+  if (s.x + s.y + s.z + s.w == 1.2345f) out[0] = 1;
+}
+
+// Vector-memory reads of an L1/L2-resident 16 KB block per work-group
+// (global_load_dwordx4, 8 independent loads in flight per wave).
+__global__ __launch_bounds__(kThreads) void l1_b128_ilp(const unsigned* __restrict__ src, unsigned* out) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const unsigned* blk = src + (blockIdx.x & 63) * 4096;  // 64 distinct 16 KB blocks
+  u32x4 acc[8];
+  for (int u = 0; u < 8; ++u) acc[u] = u32x4{0, 0, 0, 0};
+  for (int it = 0; it < kIters / 8; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int off = (lane * 16 + (((it * 8 + u) * 1024 + wv * 4096) & 16383)) >> 2;
+      acc[u] ^= *reinterpret_cast<const u32x4*>(&blk[off]);
+    }
+  }
+  u32x4 a = acc[0];
+  for (int u = 1; u < 8; ++u) a ^= acc[u];
+  if ((a.x ^ a.y ^ a.z ^ a.w) == 0x12345678u) out[0] = 1;
+}
+
 __global__ __launch_bounds__(kThreads) void mfma_bf16(unsigned* out, float seed) {
   bf16x8 a, b;
   for (int i = 0; i < 8; ++i) { a[i] = (__bf16)(seed * i); b[i] = (__bf16)(seed + i); }
@@ -82,6 +161,22 @@ __global__ __launch_bounds__(kThreads) void mfma_bf16(unsigned* out, float seed)
     c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c1, 0, 0, 0);
     c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c2, 0, 0, 0);
     c3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c3, 0, 0, 0);
+  }
+  const f32x4 s = c0 + c1 + c2 + c3;
+  if (s.x + s.y + s.z + s.w == 1.2345f) out[0] = 1;
+}
+
+
+__global__ __launch_bounds__(kThreads) void mfma_bf16_k16(unsigned* out, float seed) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 a, b;
+  for (int i = 0; i < 4; ++i) { a[i] = (__bf16)(seed * i); b[i] = (__bf16)(seed + i); }
+  f32x4 c0 = {0, 0, 0, 0}, c1 = c0, c2 = c0, c3 = c0;
+  for (int it = 0; it < kIters / 4; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c3, 0, 0, 0);
   }
   const f32x4 s = c0 + c1 + c2 + c3;
   if (s.x + s.y + s.z + s.w == 1.2345f) out[0] = 1;
@@ -140,9 +235,29 @@ int main() {
   printf("ds_read_b64       : %7.1f B/clk/CU (%.3f ms)\n", per_cu_clk(waves * 64 * 8 * kIters, t), t);
   t = time_ms([&] { hipLaunchKernelGGL(lds_tr16, dim3(blocks), dim3(kThreads), 0, 0, out); });
   printf("ds_read_b64_tr_b16: %7.1f B/clk/CU (%.3f ms)\n", per_cu_clk(waves * 64 * 8 * kIters, t), t);
+  t = time_ms([&] { hipLaunchKernelGGL(lds_b128_ilp<0>, dim3(blocks), dim3(kThreads), 0, 0, out); });
+  printf("ds_read_b128 x8   : %7.1f B/clk/CU (%.3f ms) consecutive slots\n",
+         per_cu_clk(waves * 64 * 16 * (kIters / 8) * 8, t), t);
+  t = time_ms([&] { hipLaunchKernelGGL(lds_b128_ilp<1>, dim3(blocks), dim3(kThreads), 0, 0, out); });
+  printf("ds_read_b128 x8   : %7.1f B/clk/CU (%.3f ms) MFMA operand rows, 272-byte stride\n",
+         per_cu_clk(waves * 64 * 16 * (kIters / 8) * 8, t), t);
+  t = time_ms([&] { hipLaunchKernelGGL(mix_lds_mfma, dim3(blocks), dim3(kThreads), 0, 0, out, 0.5f); });
+  printf("mfma + 1 KB LDS   : %7.1f FLOP/clk/CU (%.3f ms), %.1f B/clk/CU of LDS reads\n",
+         per_cu_clk(waves * (kIters / 8) * 8 * 16.0 * 16 * 32 * 2, t), t,
+         per_cu_clk(waves * (kIters / 8) * 8 * 1024.0, t));
+  unsigned* src;
+  CHECK(hipMalloc(&src, 64 * 16384));
+  CHECK(hipMemset(src, 1, 64 * 16384));
+  t = time_ms([&] { hipLaunchKernelGGL(l1_b128_ilp, dim3(blocks), dim3(kThreads), 0, 0, src, out); });
+  printf("global b128 x8    : %7.1f B/clk/CU (%.3f ms) cache-resident 16 KB blocks\n",
+         per_cu_clk(waves * 64 * 16 * (kIters / 8) * 8, t), t);
+  CHECK(hipFree(src));
   t = time_ms([&] { hipLaunchKernelGGL(mfma_bf16, dim3(blocks), dim3(kThreads), 0, 0, out, 0.5f); });
   printf("mfma 16x16x32 bf16: %7.1f FLOP/clk/CU (%.3f ms)\n",
          per_cu_clk(waves * kIters * 16.0 * 16 * 32 * 2, t), t);
+  t = time_ms([&] { hipLaunchKernelGGL(mfma_bf16_k16, dim3(blocks), dim3(kThreads), 0, 0, out, 0.5f); });
+  printf("mfma 16x16x16 bf16: %7.1f FLOP/clk/CU (%.3f ms)\n",
+         per_cu_clk(waves * kIters * 16.0 * 16 * 16 * 2, t), t);
   t = time_ms([&] { hipLaunchKernelGGL(valu_exp, dim3(blocks), dim3(kThreads), 0, 0, out, 0.01f); });
   printf("v_exp_f32         : %7.1f lane-ops/clk/CU (%.3f ms)\n", per_cu_clk(waves * 64 * kIters, t), t);
   t = time_ms([&] { hipLaunchKernelGGL(valu_fma, dim3(blocks), dim3(kThreads), 0, 0, out, 0.01f); });

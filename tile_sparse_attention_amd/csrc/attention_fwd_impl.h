@@ -13,9 +13,9 @@
 //     chunk once in LDS (K as rows, V transposed to [d][key]) with
 //     double-buffered buffer loads whose chunk offset is a uniform value; all
 //     waves then reuse it, so each K/V element crosses from L2 once per
-//     32*W query rows.  Chunks are visited in a per-work-group rotated order
-//     so that neighbouring work-groups (same XCD, same L2) do not all miss on
-//     the same lines at the same time.
+//     32*W query rows.  Blocks are renumbered so that the work-groups running
+//     together on one XCD belong to one head and stream the same K/V through
+//     that XCD's L2.
 //   * Per chunk each wave compacts its mask bits into the list of kept key
 //     tiles (wave prefix count of the bitmap, the routine the compaction
 //     kernel also uses) and packs the kept keys densely into 16-key "slots":
@@ -493,8 +493,9 @@ struct AttnKernel {
     g = lane >> 4;
     n = lane & 15;
     wave = wave_uniform(tid >> 6);
-    bh = blockIdx.x / p.n_qblocks;
-    const int qb = blockIdx.x - bh * p.n_qblocks;
+    const int lb = xcd_major_block((int)blockIdx.x, (int)gridDim.x);
+    bh = lb / p.n_qblocks;
+    const int qb = lb - bh * p.n_qblocks;
     L = p.L;
     const size_t head_off = (size_t)bh * (size_t)L * D;
     const T* __restrict__ qg = reinterpret_cast<const T*>(p.q) + head_off;
@@ -521,12 +522,12 @@ struct AttnKernel {
       tile[t].m_run = -INFINITY;
     }
 
-    // Chunks are visited in a rotated order (the online softmax does not
-    // depend on the order): neighbouring work-groups share an XCD and its L2,
-    // and each starts one chunk behind the previous one.
+    // All work-groups of an XCD walk the chunks of their head in the same
+    // order, so a chunk is fetched into that XCD's L2 once and read there by
+    // every work-group near the same time (staggered start chunks measured
+    // slower).
     const int n_chunks = (L + KC - 1) / KC;
-    const int rot = n_chunks - 1 - (int)((blockIdx.x >> 3) % (unsigned)n_chunks);
-    auto phys = [&](int c) { const int x = c + rot; return x >= n_chunks ? x - n_chunks : x; };
+    auto phys = [](int c) { return c; };
     uint32_t mcur[TPW][C::MW], mnext[TPW][C::MW];
     issue_chunk(phys(0), 0, mcur);
     __builtin_amdgcn_s_waitcnt(0);

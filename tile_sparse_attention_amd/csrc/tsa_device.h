@@ -80,6 +80,31 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t x) {
 __device__ __forceinline__ float xor_lane16(float x) { return __shfl_xor(x, 16); }
 __device__ __forceinline__ float xor_lane32(float x) { return __shfl_xor(x, 32); }
 
+// Work-groups of a 1-D grid are handed to the eight XCDs of the chip in
+// turn (block b to XCD b mod 8), and each XCD has an L2 of its own.  This
+// renumbering gives every XCD one contiguous range of logical blocks, in
+// dispatch order: blocks that run together on an XCD are consecutive logical
+// blocks (of the same head, for the attention grid) and share its L2.
+__device__ __forceinline__ int xcd_major_block(int b, int nb) {
+  constexpr int X = 8;
+  const int x = b % X, i = b / X;
+  const int q = nb / X, r = nb % X;
+  return x * q + (x < r ? x : r) + i;
+}
+
+// Three-way max / min of finite floats in one instruction (fmaxf/fminf
+// would first quiet possible signalling NaNs, two extra instructions each).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float min3f(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // A zero the compiler cannot see through: adding it to an index keeps a
