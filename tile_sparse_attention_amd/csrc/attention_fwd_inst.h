@@ -2,12 +2,12 @@
 #pragma once
 
 #include "attention_fwd_impl.h"
+#include "attention_fwd_octet.h"
 #include "launch.h"
 
 namespace tsa {
 
-template <typename T, int D, int N, int KC, int W, int TPW>
-hipError_t launch_attn_cfg(const AttnLaunch& a) {
+inline AttnParams attn_params(const AttnLaunch& a, int rows_per_block) {
   const tsa_problem_t& pr = *a.p;
   AttnParams p;
   p.q = a.q;
@@ -23,14 +23,36 @@ hipError_t launch_attn_cfg(const AttnLaunch& a) {
   p.T_k = (pr.L + pr.N - 1) / pr.N;
   p.words = (p.T_k + 31) / 32;
   p.L_pad = attention_l_pad(pr.L);
-  p.n_qblocks = (pr.L + 16 * TPW * W - 1) / (16 * TPW * W);
+  p.n_qblocks = (pr.L + rows_per_block - 1) / rows_per_block;
   p.scale_log2 = a.scale * 1.4426950408889634f;
-  const long long blocks = (long long)pr.B * pr.H * p.n_qblocks;
-  hipLaunchKernelGGL((vt_pack_kernel<T, D>), dim3((unsigned)(p.L_pad / 64), (unsigned)(pr.B * pr.H)),
+  return p;
+}
+
+template <typename T, int D>
+void launch_vt_pack(const AttnLaunch& a, const AttnParams& p) {
+  hipLaunchKernelGGL((vt_pack_kernel<T, D>), dim3((unsigned)(p.L_pad / 64), (unsigned)(a.p->B * a.p->H)),
                      dim3(256), 0, a.stream, static_cast<const T*>(a.v), static_cast<T*>(a.workspace),
-                     pr.L, p.L_pad);
+                     a.p->L, p.L_pad);
+}
+
+template <typename T, int D, int N, int KC, int W, int TPW>
+hipError_t launch_attn_cfg(const AttnLaunch& a) {
+  const AttnParams p = attn_params(a, 16 * TPW * W);
+  const long long blocks = (long long)a.p->B * a.p->H * p.n_qblocks;
+  launch_vt_pack<T, D>(a, p);
   hipLaunchKernelGGL((attn_fwd_kernel<T, D, N, KC, W, TPW>), dim3((unsigned)blocks), dim3(64 * W), 0,
                      a.stream, p);
+  return hipGetLastError();
+}
+
+// bf16 with key tiles of N >= 8: the octet-packing kernel.
+template <int D, int N>
+hipError_t launch_attn_oct(const AttnLaunch& a) {
+  using C = OctCfg<D, N>;
+  const AttnParams p = attn_params(a, C::ROWS);
+  const long long blocks = (long long)a.p->B * a.p->H * p.n_qblocks;
+  launch_vt_pack<bf16_t, D>(a, p);
+  hipLaunchKernelGGL((attn_oct_kernel<D, N>), dim3((unsigned)blocks), dim3(64 * C::W), 0, a.stream, p);
   return hipGetLastError();
 }
 
@@ -50,8 +72,12 @@ template <int N> struct AttnShape<float, 64, N> { static constexpr int KC = 64, 
 
 template <typename T, int D, int N>
 hipError_t launch_attn_n(const AttnLaunch& a) {
-  using S = AttnShape<T, D, N>;
-  return launch_attn_cfg<T, D, N, S::KC, S::W, S::TPW>(a);
+  if constexpr (sizeof(T) == 2 && N >= 8) {
+    return launch_attn_oct<D, N>(a);
+  } else {
+    using S = AttnShape<T, D, N>;
+    return launch_attn_cfg<T, D, N, S::KC, S::W, S::TPW>(a);
+  }
 }
 
 template <typename T, int D>

@@ -1,0 +1,282 @@
+// Tile-sparse attention forward kernel for bf16 and key tiles of N >= 8 keys
+// (gfx950, wave64, 16x16x32 bf16 MFMA).
+//
+// Operation: FG-Attn ("FG-Attn: Leveraging Fine-Grained Sparse Attention in
+// Video Diffusion Models", section Abstract): the query-key dot products of
+// every M x N tile whose keep bit is 0 are skipped and those scores take no
+// part in the softmax; O = softmax(scale * Q K^T over kept tiles) V.
+//
+// With N >= 8 every kept key tile is a whole number of "octets", runs of
+// eight consecutive keys starting at a multiple of 8.  The kernel packs kept
+// octets, four per pass, into the 32-key contraction of the matrix cores:
+//   * A work-group owns 256 consecutive query rows of one (b, h); each of its
+//     16 waves owns one 16-row query tile (inside one mask row, M being a
+//     multiple of 16) and keeps that tile's Q fragment, O^T accumulator and
+//     running max in registers.
+//   * Keys stream through LDS in chunks of 128 (K rows, and the V^T columns
+//     of the packed V^T workspace), double-buffered, filled by direct
+//     global-to-LDS loads issued by all waves; each chunk crosses from L2
+//     once per 256 query rows.
+//   * Per chunk a wave turns the mask bits of its row into the ascending list
+//     of kept octets with one ballot and one lane permutation (lane i of the
+//     list register holds the i-th kept octet).  A pass takes list entries
+//     4p..4p+3; a list shorter than a multiple of four is padded with the
+//     first kept octet for the score side (a real kept score, so the running
+//     max only sees real kept scores) and with the zero column of V^T for
+//     the value side, whose ones row is zero there as well.
+//   * Scores are formed transposed, S^T = K Q^T (A = K rows from LDS, B = the
+//     Q fragment), with key rows laid out so that the two 16-key score blocks
+//     of a pass leave lane group g holding all eight keys of octet 4p+g: that
+//     is exactly the B operand of O^T += V^T P^T, and the matching A operand
+//     is one 16-byte LDS read of the octet's eight V^T columns.
+//   * The softmax denominator l comes from the same MFMA pipeline: the V^T
+//     workspace carries a ones row (zero past L and in the padding column),
+//     read as a broadcast (one address per lane group).
+//   * Online softmax in base 2, scale*log2(e) folded into one FMA per score;
+//     the reference max is raised (and O, l rescaled) only when some score
+//     exceeds it by more than 2^8, decided by one wave-wide ballot.
+//   * Keys past L in the last octet read K row L-1 (the loads clamp the row)
+//     and zero V^T columns, so they add nothing.
+#pragma once
+
+#include "attention_fwd_impl.h"
+
+namespace tsa {
+
+template <int D, int N>
+struct OctCfg {
+  static constexpr int KC = 128;                   // keys per chunk
+  static constexpr int W = 16;                     // waves per work-group
+  static constexpr int ROWS = 16 * W;              // query rows per work-group
+  static constexpr int OPC = KC / 8;               // octets per chunk
+  static constexpr int TPC = KC / N;               // key tiles per chunk (<= 16)
+  static constexpr int LOG2R = ilog2(N / 8);       // octets per key tile, log2
+  static constexpr int NSLAB = D / 32;             // 32-wide d slabs of the QK^T contraction
+  static constexpr int NDB = D / 16;               // 16-wide d blocks of O^T
+  static constexpr int KRB = D * 2;                // K row bytes in memory
+  static constexpr int KRS = KRB + 16;             // K row stride in LDS
+  static constexpr int VRB = KC * 2;               // V^T row bytes of one chunk
+  static constexpr int VRS = VRB + 16;             // V^T row stride in LDS (+ zero octet)
+  static constexpr int VROWS = D + 1;              // V^T rows incl. the ones row
+  static constexpr int ZOCT = OPC;                 // octet index of the zero column
+  static constexpr int NI_K = (KC * KRS + 1023) / 1024;     // 1-KB loads per K chunk
+  static constexpr int NI_V = (VROWS * VRS + 1023) / 1024;  // 1-KB loads per V^T chunk
+  static constexpr int NI = NI_K + NI_V;
+  static constexpr int NI_W = (NI + W - 1) / W;
+  static_assert(N >= 8 && N <= 64 && (N & (N - 1)) == 0, "octet kernel: N in {8,16,32,64}");
+  static_assert(D % 32 == 0, "head dim");
+  static_assert(TPC <= 16, "tile bits of a chunk fit one mask word");
+};
+
+template <int D, int N>
+struct OctKernel {
+  using C = OctCfg<D, N>;
+  static constexpr float RESCALE_STEP = 8.f;  // log2 units the max may grow before rescaling
+
+  struct Smem {
+    __attribute__((aligned(16))) uint8_t k[2][C::NI_K * 1024];
+    __attribute__((aligned(16))) uint8_t vt[2][C::NI_V * 1024];
+  };
+
+  const AttnParams& p;
+  Smem& sm;
+  int lane, g, n, wave, L;
+  const bf16_t* __restrict__ kg;
+  const bf16_t* __restrict__ vtg;
+  const uint32_t* __restrict__ mrow;
+  u32x4 qf[C::NSLAB];
+  f32x4 oacc[C::NDB + 1];
+  float m_run;
+
+  __device__ __forceinline__ OctKernel(const AttnParams& pp, Smem& s) : p(pp), sm(s) {}
+
+  // Byte offset read by lane `ln` for 1-KB load `I` of a chunk with `rows`
+  // keys, relative to the chunk's resource base; out of range (reads zero)
+  // for the padding bytes of an LDS row.  K rows past the last key repeat it.
+  __device__ __forceinline__ uint32_t dma_offset(int I, int ln, int rows) const {
+    constexpr uint32_t OOB = 0x80000000u;
+    if (I < C::NI_K) {
+      const int pos = I * 1024 + 16 * ln;
+      const int row = pos / C::KRS, cb = pos - row * C::KRS;
+      const int r = row < rows ? row : rows - 1;
+      return row < C::KC && cb < C::KRB ? (uint32_t)(r * C::KRB + cb) : OOB;
+    }
+    const int pos = (I - C::NI_K) * 1024 + 16 * ln;
+    const int row = pos / C::VRS, cb = pos - row * C::VRS;
+    return row < C::VROWS && cb < C::VRB ? (uint32_t)(row * p.L_pad * 2 + cb) : OOB;
+  }
+
+  // This wave's share of the loads of chunk c into buffer `buf`, and the
+  // mask word of chunk c.  Nothing waits here.
+  __device__ __forceinline__ uint32_t issue_chunk(int c, int buf) {
+    const int kbase = c * C::KC;
+    const int rows = L - kbase < C::KC ? L - kbase : C::KC;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kg + (size_t)kbase * D), (short)0, rows * C::KRB, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vtg + kbase), (short)0, (C::VROWS * p.L_pad - kbase) * 2, kBufferFlags);
+    const int ln = lane + opaque_zero();
+#pragma unroll
+    for (int u = 0; u < C::NI_W; ++u) {
+      const int I = wave + C::W * u;
+      if (C::NI % C::W == 0 || I < C::NI) {
+        if (I < C::NI_K)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rk, (__attribute__((address_space(3))) void*)(sm.k[buf] + I * 1024), 16,
+              dma_offset(I, ln, rows), 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rv, (__attribute__((address_space(3))) void*)(sm.vt[buf] + (I - C::NI_K) * 1024), 16,
+              dma_offset(I, ln, rows), 0, 0, 0);
+      }
+    }
+    const int wi = (c * C::TPC) >> 5;
+    return mrow[wi < p.words ? wi : p.words - 1];
+  }
+
+  // One pass over octets oq (score side, per lane: the octet of key row n of
+  // this lane's 16-key blocks) and ov (value side: lane group g's octet).
+  __device__ __forceinline__ void pass(int buf, int oq, int ov) {
+    const float c = p.scale_log2;
+    const uint8_t* ka = sm.k[buf] + (oq * 8 + (n & 3)) * C::KRS + 16 * g;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+    for (int sl = 0; sl < C::NSLAB; ++sl) {
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(ka + 64 * sl);
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(ka + 4 * C::KRS + 64 * sl);
+      s0 = Mma<bf16_t>::mac8(a0, qf[sl], s0);
+      s1 = Mma<bf16_t>::mac8(a1, qf[sl], s1);
+    }
+    float mr;
+    // (built with NaNs assumed absent, these fold into three-way max/min
+    // instructions without operand quieting)
+    if (c >= 0.f)
+      mr = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                 fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+    else
+      mr = fminf(fminf(fminf(s0[0], s0[1]), fminf(s0[2], s0[3])),
+                 fminf(fminf(s1[0], s1[1]), fminf(s1[2], s1[3])));
+    float mx = c * mr;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_STEP) != 0ull) {
+      mx = fmaxf(mx, xor_lane16(mx));
+      mx = fmaxf(mx, xor_lane32(mx));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2_fast(m_run - m_new);  // 0 on the first pass
+      m_run = m_new;
+#pragma unroll
+      for (int j = 0; j <= C::NDB; ++j) oacc[j] *= alpha;
+    }
+    const float nm = -m_run;
+    bf16x8 pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pb[i] = (__bf16)exp2_fast(__builtin_fmaf(s0[i], c, nm));
+      pb[4 + i] = (__bf16)exp2_fast(__builtin_fmaf(s1[i], c, nm));
+    }
+    const u32x4 bop = __builtin_bit_cast(u32x4, pb);
+    const uint8_t* va = sm.vt[buf] + n * C::VRS + 16 * ov;
+#pragma unroll
+    for (int j = 0; j < C::NDB; ++j) {
+      const u32x4 av = *reinterpret_cast<const u32x4*>(va + 16 * j * C::VRS);
+      oacc[j] = Mma<bf16_t>::mac8(av, bop, oacc[j]);
+    }
+    // ones row: the same 16 bytes for all lanes of a group (broadcast read)
+    const u32x4 ones = *reinterpret_cast<const u32x4*>(sm.vt[buf] + D * C::VRS + 16 * ov);
+    oacc[C::NDB] = Mma<bf16_t>::mac8(ones, bop, oacc[C::NDB]);
+  }
+
+  __device__ __forceinline__ void compute_chunk(int c, int buf, uint32_t mword) {
+    const int kbase = c * C::KC;
+    uint32_t tb = uniform_u32(mword) >> ((c * C::TPC) & 31);
+    if constexpr (C::TPC < 32) tb &= (1u << C::TPC) - 1u;
+    const int left = L - kbase;                       // keys of this chunk that exist
+    const int nval = left >= C::KC ? C::OPC : (left + 7) >> 3;
+    const bool keep = lane < nval && ((tb >> ((lane & (C::OPC - 1)) >> C::LOG2R)) & 1u);
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+    if (bal == 0ull) return;
+    const int count = __builtin_popcountll(bal);
+    const int below = (int)prefix_count64(bal);
+    const int tgt = keep ? below : count + (lane - below);
+    const int lst = __builtin_amdgcn_ds_permute(tgt * 4, lane);
+    const int first = __builtin_ctzll(bal);
+    const int lq = lane < count ? lst : first;
+    const int lv = lane < count ? lst : C::ZOCT;
+    for (int q0 = 0; q0 < count; q0 += 4) {
+      const int oq = __builtin_amdgcn_ds_bpermute((q0 + (n >> 2)) * 4, lq);
+      const int ov = __builtin_amdgcn_ds_bpermute((q0 + g) * 4, lv);
+      pass(buf, oq, ov);
+    }
+  }
+
+  __device__ __forceinline__ void run() {
+    const int tid = threadIdx.x;
+    lane = tid & 63;
+    g = lane >> 4;
+    n = lane & 15;
+    wave = wave_uniform(tid >> 6);
+    const int lb = xcd_major_block((int)blockIdx.x, (int)gridDim.x);
+    const int bh = lb / p.n_qblocks;
+    const int qb = lb - bh * p.n_qblocks;
+    L = p.L;
+    const size_t head_off = (size_t)bh * (size_t)L * D;
+    const bf16_t* __restrict__ qg = reinterpret_cast<const bf16_t*>(p.q) + head_off;
+    kg = reinterpret_cast<const bf16_t*>(p.k) + head_off;
+    vtg = reinterpret_cast<const bf16_t*>(p.vt) + (size_t)bh * C::VROWS * p.L_pad;
+
+    const int row0 = qb * C::ROWS + 16 * wave;
+    const bool act = row0 < L;
+    mrow = p.mask + ((size_t)bh * p.T_q + (size_t)(act ? row0 / p.M : 0)) * p.words;
+    const int rq = row0 + n < L ? row0 + n : L - 1;
+#pragma unroll
+    for (int s = 0; s < C::NSLAB; ++s)
+      qf[s] = *reinterpret_cast<const u32x4*>(qg + (size_t)rq * D + 32 * s + 8 * g);
+    if (row0 + n >= L)
+#pragma unroll
+      for (int s = 0; s < C::NSLAB; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j <= C::NDB; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+
+    const int n_chunks = (L + C::KC - 1) / C::KC;
+    uint32_t mcur = issue_chunk(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int c = 0; c < n_chunks; ++c) {
+      const int buf = c & 1;
+      // buffer buf^1 was last read in iteration c-1, which every wave has left
+      const uint32_t mnext = c + 1 < n_chunks ? issue_chunk(c + 1, buf ^ 1) : 0u;
+      if (act) compute_chunk(c, buf, mcur);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c+1 have landed
+      __syncthreads();                // ... and every other wave's
+      mcur = mnext;
+    }
+
+    const int r = row0 + n;
+    if (r >= L) return;
+    const float l_tot = oacc[C::NDB][0];
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    bf16_t* og = reinterpret_cast<bf16_t*>(p.o) + head_off + (size_t)r * D;
+#pragma unroll
+    for (int j = 0; j < C::NDB; ++j) {
+      const f32x4 val = oacc[j] * inv;
+      bf16x4 ob;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ob[i] = (__bf16)val[i];
+      *reinterpret_cast<u32x2*>(og + 16 * j + 4 * g) = __builtin_bit_cast(u32x2, ob);
+    }
+    if (p.lse != nullptr && g == 0)
+      p.lse[(size_t)bh * L + r] =
+          l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+  }
+};
+
+template <int D, int N>
+__global__ __launch_bounds__(1024) void attn_oct_kernel(AttnParams p) {
+  static_assert(OctCfg<D, N>::W == 16, "launch bounds: 16 waves");
+  using K = OctKernel<D, N>;
+  __shared__ __attribute__((aligned(16))) typename K::Smem sm;
+  K k(p, sm);
+  k.run();
+}
+
+}  // namespace tsa

@@ -92,19 +92,6 @@ __device__ __forceinline__ int xcd_major_block(int b, int nb) {
   return x * q + (x < r ? x : r) + i;
 }
 
-// Three-way max / min of finite floats in one instruction (fmaxf/fminf
-// would first quiet possible signalling NaNs, two extra instructions each).
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-__device__ __forceinline__ float min3f(float a, float b, float c) {
-  float r;
-  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // A zero the compiler cannot see through: adding it to an index keeps a
