@@ -115,6 +115,7 @@ __global__ __launch_bounds__(kThreads) void mix_lds_mfma(unsigned* out, float se
   for (int i = 0; i < 8; ++i) b[i] = (__bf16)(seed + i);
   f32x4 c0 = {0, 0, 0, 0}, c1 = c0, c2 = c0, c3 = c0;
   for (int it = 0; it < kIters / 8; ++it) {
+    asm volatile("" ::: "memory");  // keeps the reads in the loop
     const char* p = lb + ((it * 2048) & 8191);
 #pragma unroll
     for (int u = 0; u < 8; u += 4) {
@@ -150,6 +151,40 @@ __global__ __launch_bounds__(kThreads) void l1_b128_ilp(const unsigned* __restri
   u32x4 a = acc[0];
   for (int u = 1; u < 8; ++u) a ^= acc[u];
   if ((a.x ^ a.y ^ a.z ^ a.w) == 0x12345678u) out[0] = 1;
+}
+
+
+// LDS read pattern probe: lane (g, n) = (lane >> gshift, lane & (2^gshift - 1))
+// reads W bytes at n*rstride + g*gstride (+ 256-byte multiples that keep the
+// bank mapping), eight reads in flight.  Profiled with the LDS bank-conflict
+// counter, it shows which operand layouts the LDS serves conflict-free.
+template <int W>
+__global__ __launch_bounds__(kThreads) void lds_pattern(unsigned* out, int rstride, int gstride,
+                                                        int gshift) {
+  __shared__ __attribute__((aligned(16))) unsigned lds[8192];  // 32 KB
+  for (int i = threadIdx.x; i < 8192; i += kThreads) lds[i] = i;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int n = lane & ((1 << gshift) - 1), g = lane >> gshift;
+  const char* lb = reinterpret_cast<const char*>(lds) + n * rstride + g * gstride + wv * 4096;
+  for (int it = 0; it < kIters / 8; ++it) {
+    asm volatile("" ::: "memory");
+    if constexpr (W == 16) {
+      u32x4 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const u32x4*>(lb + u * 256);
+      asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]),
+                   "v"(x[7]));
+    } else {
+      u32x2 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const u32x2*>(lb + u * 256);
+      asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]),
+                   "v"(x[7]));
+    }
+  }
+  if (lane == 64) out[0] = 1;
 }
 
 __global__ __launch_bounds__(kThreads) void mfma_bf16(unsigned* out, float seed) {
@@ -252,6 +287,31 @@ int main() {
   printf("global b128 x8    : %7.1f B/clk/CU (%.3f ms) cache-resident 16 KB blocks\n",
          per_cu_clk(waves * 64 * 16 * (kIters / 8) * 8, t), t);
   CHECK(hipFree(src));
+  {
+    struct Pat { int w, rs, gs, gsh; const char* what; };
+    const Pat pats[] = {
+        {16, 16, 0, 6, "b128 consecutive"},
+        {16, 272, 16, 4, "b128 rows 272 B apart, groups 16 B"},
+        {16, 256, 16, 4, "b128 rows 256 B apart, groups 16 B"},
+        {16, 272, 64, 4, "b128 rows 272 B apart, groups 64 B"},
+        {16, 288, 16, 4, "b128 rows 288 B apart, groups 16 B"},
+        {16, 264, 16, 4, "b128 rows 264 B apart, groups 16 B"},
+        {16, 16, 256, 3, "b128 8 rows x 16 B consecutive, groups 256 B"},
+        {16, 272, 16, 3, "b128 8 rows 272 B apart, groups 16 B"},
+        {8, 8, 0, 6, "b64 consecutive"},
+        {8, 272, 8, 4, "b64 rows 272 B apart, groups 8 B"},
+        {8, 272, 16, 4, "b64 rows 272 B apart, groups 16 B"},
+        {8, 264, 8, 4, "b64 rows 264 B apart, groups 8 B"},
+    };
+    for (const Pat& q : pats) {
+      if (q.w == 16)
+        t = time_ms([&] { hipLaunchKernelGGL(lds_pattern<16>, dim3(blocks), dim3(kThreads), 0, 0, out, q.rs, q.gs, q.gsh); });
+      else
+        t = time_ms([&] { hipLaunchKernelGGL(lds_pattern<8>, dim3(blocks), dim3(kThreads), 0, 0, out, q.rs, q.gs, q.gsh); });
+      printf("pattern %-48s: %7.1f B/clk/CU (%.3f ms)\n", q.what,
+             per_cu_clk(waves * 64.0 * q.w * (kIters / 8) * 8, t), t);
+    }
+  }
   t = time_ms([&] { hipLaunchKernelGGL(mfma_bf16, dim3(blocks), dim3(kThreads), 0, 0, out, 0.5f); });
   printf("mfma 16x16x32 bf16: %7.1f FLOP/clk/CU (%.3f ms)\n",
          per_cu_clk(waves * kIters * 16.0 * 16 * 32 * 2, t), t);

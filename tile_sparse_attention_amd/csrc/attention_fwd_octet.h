@@ -25,10 +25,11 @@
 //     max only sees real kept scores) and with the zero column of V^T for
 //     the value side, whose ones row is zero there as well.
 //   * Scores are formed transposed, S^T = K Q^T (A = K rows from LDS, B = the
-//     Q fragment), with key rows laid out so that the two 16-key score blocks
-//     of a pass leave lane group g holding all eight keys of octet 4p+g: that
-//     is exactly the B operand of O^T += V^T P^T, and the matching A operand
-//     is one 16-byte LDS read of the octet's eight V^T columns.
+//     Q fragment); a 16-key score block holds two whole octets.  The
+//     accumulators are directly the B operand of O^T += V^T P^T
+//     (probabilities never leave registers); the matching A operand is two
+//     8-byte LDS reads of V^T columns per lane.  Row strides are chosen so
+//     that both reads are free of LDS bank conflicts for any octets.
 //   * The softmax denominator l comes from the same MFMA pipeline: the V^T
 //     workspace carries a ones row (zero past L and in the padding column),
 //     read as a broadcast (one address per lane group).
@@ -54,7 +55,11 @@ struct OctCfg {
   static constexpr int NSLAB = D / 32;             // 32-wide d slabs of the QK^T contraction
   static constexpr int NDB = D / 16;               // 16-wide d blocks of O^T
   static constexpr int KRB = D * 2;                // K row bytes in memory
-  static constexpr int KRS = KRB + 16;             // K row stride in LDS
+  // K row stride in LDS: with 32 padding bytes, the 16 key rows of a score
+  // block (two octets, eight consecutive rows each) read 16 bytes per lane
+  // without bank conflicts whatever the octets; V^T rows take 16 padding
+  // bytes, which keeps their 8-byte column reads conflict-free.
+  static constexpr int KRS = KRB + 32;
   static constexpr int VRB = KC * 2;               // V^T row bytes of one chunk
   static constexpr int VRS = VRB + 16;             // V^T row stride in LDS (+ zero octet)
   static constexpr int VROWS = D + 1;              // V^T rows incl. the ones row
@@ -87,6 +92,7 @@ struct OctKernel {
   u32x4 qf[C::NSLAB];
   f32x4 oacc[C::NDB + 1];
   float m_run;
+  uint32_t doff[C::NI_W];  // per-lane load offsets of a full chunk (chunk-invariant)
 
   __device__ __forceinline__ OctKernel(const AttnParams& pp, Smem& s) : p(pp), sm(s) {}
 
@@ -115,7 +121,7 @@ struct OctKernel {
         (void*)(kg + (size_t)kbase * D), (short)0, rows * C::KRB, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vtg + kbase), (short)0, (C::VROWS * p.L_pad - kbase) * 2, kBufferFlags);
-    const int ln = lane + opaque_zero();
+    const bool full = rows == C::KC;
 #pragma unroll
     for (int u = 0; u < C::NI_W; ++u) {
       const int I = wave + C::W * u;
@@ -123,29 +129,56 @@ struct OctKernel {
         if (I < C::NI_K)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               rk, (__attribute__((address_space(3))) void*)(sm.k[buf] + I * 1024), 16,
-              dma_offset(I, ln, rows), 0, 0, 0);
+              full ? doff[u] : dma_offset(I, lane, rows), 0, 0, 0);
         else
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               rv, (__attribute__((address_space(3))) void*)(sm.vt[buf] + (I - C::NI_K) * 1024), 16,
-              dma_offset(I, ln, rows), 0, 0, 0);
+              doff[u], 0, 0, 0);
       }
     }
     const int wi = (c * C::TPC) >> 5;
     return mrow[wi < p.words ? wi : p.words - 1];
   }
 
-  // One pass over octets oq (score side, per lane: the octet of key row n of
-  // this lane's 16-key blocks) and ov (value side: lane group g's octet).
-  __device__ __forceinline__ void pass(int buf, int oq, int ov) {
+  // One pass over the four kept octets at list positions q0..q0+3.  Score
+  // block b (0, 1) holds the octets at positions q0+2b and q0+2b+1, eight key
+  // rows each: lane (g, n) reads row n&7 of octet oq[b] (oq[b] = the octet at
+  // position q0+2b+(n>>3)).  The score accumulators leave lane group g with
+  // keys 4(g&1)..4(g&1)+3 of octet ovx (position q0+(g>>1)) and of octet ovy
+  // (position q0+2+(g>>1)), so its PV operand is two 8-byte V^T reads.
+  __device__ __forceinline__ void pass(int buf, int oq0, int oq1, int ovx, int ovy) {
     const float c = p.scale_log2;
-    const uint8_t* ka = sm.k[buf] + (oq * 8 + (n & 3)) * C::KRS + 16 * g;
+    const uint8_t* kb = sm.k[buf] + (n & 7) * C::KRS + 16 * g;
+    const uint8_t* ka0 = kb + oq0 * (8 * C::KRS);
+    const uint8_t* ka1 = kb + oq1 * (8 * C::KRS);
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
     for (int sl = 0; sl < C::NSLAB; ++sl) {
-      const u32x4 a0 = *reinterpret_cast<const u32x4*>(ka + 64 * sl);
-      const u32x4 a1 = *reinterpret_cast<const u32x4*>(ka + 4 * C::KRS + 64 * sl);
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(ka0 + 64 * sl);
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(ka1 + 64 * sl);
       s0 = Mma<bf16_t>::mac8(a0, qf[sl], s0);
       s1 = Mma<bf16_t>::mac8(a1, qf[sl], s1);
+    }
+    // The first V^T operands (and the ones row, the same bytes for all lanes
+    // of a group) are read before the softmax so their latency overlaps it;
+    // the rest after, within the register budget.
+    constexpr int EARLY = C::NDB / 2 - 1;
+    const int half = 8 * (g & 1);
+    const uint8_t* vx = sm.vt[buf] + n * C::VRS + 16 * ovx + half;
+    const uint8_t* vy = sm.vt[buf] + n * C::VRS + 16 * ovy + half;
+    u32x4 av[C::NDB + 1];
+    auto vread = [&](int off) {
+      const u32x2 x = *reinterpret_cast<const u32x2*>(vx + off);
+      const u32x2 y = *reinterpret_cast<const u32x2*>(vy + off);
+      return u32x4{x[0], x[1], y[0], y[1]};
+    };
+#pragma unroll
+    for (int j = 0; j < EARLY; ++j) av[j] = vread(16 * j * C::VRS);
+    {
+      const uint8_t* o1 = sm.vt[buf] + D * C::VRS + half;
+      const u32x2 x = *reinterpret_cast<const u32x2*>(o1 + 16 * ovx);
+      const u32x2 y = *reinterpret_cast<const u32x2*>(o1 + 16 * ovy);
+      av[C::NDB] = u32x4{x[0], x[1], y[0], y[1]};
     }
     float mr;
     // (built with NaNs assumed absent, these fold into three-way max/min
@@ -174,17 +207,15 @@ struct OctKernel {
       pb[4 + i] = (__bf16)exp2_fast(__builtin_fmaf(s1[i], c, nm));
     }
     const u32x4 bop = __builtin_bit_cast(u32x4, pb);
-    const uint8_t* va = sm.vt[buf] + n * C::VRS + 16 * ov;
 #pragma unroll
-    for (int j = 0; j < C::NDB; ++j) {
-      const u32x4 av = *reinterpret_cast<const u32x4*>(va + 16 * j * C::VRS);
-      oacc[j] = Mma<bf16_t>::mac8(av, bop, oacc[j]);
-    }
-    // ones row: the same 16 bytes for all lanes of a group (broadcast read)
-    const u32x4 ones = *reinterpret_cast<const u32x4*>(sm.vt[buf] + D * C::VRS + 16 * ov);
-    oacc[C::NDB] = Mma<bf16_t>::mac8(ones, bop, oacc[C::NDB]);
+    for (int j = EARLY; j < C::NDB; ++j) av[j] = vread(16 * j * C::VRS);
+#pragma unroll
+    for (int j = 0; j <= C::NDB; ++j) oacc[j] = Mma<bf16_t>::mac8(av[j], bop, oacc[j]);
   }
 
+  // Kept octets of chunk c as a lane-indexed list (ascending), then padding
+  // after the `count` kept entries: the first kept octet for the score side,
+  // the zero column of V^T for the value side.
   __device__ __forceinline__ void compute_chunk(int c, int buf, uint32_t mword) {
     const int kbase = c * C::KC;
     uint32_t tb = uniform_u32(mword) >> ((c * C::TPC) & 31);
@@ -201,10 +232,26 @@ struct OctKernel {
     const int first = __builtin_ctzll(bal);
     const int lq = lane < count ? lst : first;
     const int lv = lane < count ? lst : C::ZOCT;
+    // Lane p of pq / pv packs list entries 4p..4p+3 (one byte each); a pass
+    // reads its word as a wave-uniform value and every lane extracts the
+    // bytes it needs, which keeps the per-pass list lookups off the LDS.
+    const int comb = lq | (lv << 8);
+    uint32_t pq = 0u, pv = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t x = (uint32_t)__builtin_amdgcn_ds_bpermute(((4 * lane + k) & 63) * 4, comb);
+      pq |= (x & 0xffu) << (8 * k);
+      pv |= ((x >> 8) & 0xffu) << (8 * k);
+    }
+    const uint32_t shq = 8u * (uint32_t)(n >> 3), shv = 8u * (uint32_t)(g >> 1);
     for (int q0 = 0; q0 < count; q0 += 4) {
-      const int oq = __builtin_amdgcn_ds_bpermute((q0 + (n >> 2)) * 4, lq);
-      const int ov = __builtin_amdgcn_ds_bpermute((q0 + g) * 4, lv);
-      pass(buf, oq, ov);
+      const uint32_t wq = (uint32_t)__builtin_amdgcn_readlane((int)pq, q0 >> 2);
+      const uint32_t wv = (uint32_t)__builtin_amdgcn_readlane((int)pv, q0 >> 2);
+      const int oq0 = (int)__builtin_amdgcn_ubfe(wq, shq, 8);
+      const int oq1 = (int)__builtin_amdgcn_ubfe(wq, shq + 16u, 8);
+      const int ovx = (int)__builtin_amdgcn_ubfe(wv, shv, 8);
+      const int ovy = (int)__builtin_amdgcn_ubfe(wv, shv + 16u, 8);
+      pass(buf, oq0, oq1, ovx, ovy);
     }
   }
 
@@ -237,6 +284,11 @@ struct OctKernel {
     for (int j = 0; j <= C::NDB; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run = -INFINITY;
 
+#pragma unroll
+    for (int u = 0; u < C::NI_W; ++u) {
+      const int I = wave + C::W * u;
+      doff[u] = I < C::NI ? dma_offset(I, lane, C::KC) : 0u;
+    }
     const int n_chunks = (L + C::KC - 1) / C::KC;
     uint32_t mcur = issue_chunk(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
