@@ -128,6 +128,14 @@ int main() {
   const int cus = prop.multiProcessorCount;
   const double clk = 2.4e9;
   std::vector<Case> cases;
+  for (int st : {136, 144, 152, 176}) {
+    cases.push_back(vt_b64(st, 0, 1));
+    cases.push_back(vt_b64(st, 5, 2));
+  }
+  for (int st : {160, 176}) {
+    cases.push_back(k_rows(st, 0, 1));
+    cases.push_back(k_rows(st, 3, 6));
+  }
   for (int st : {272, 288}) {
     cases.push_back(k_rows(st, 0, 1));
     cases.push_back(k_rows(st, 2, 7));
