@@ -213,10 +213,21 @@ struct OctKernel {
     for (int j = 0; j <= C::NDB; ++j) oacc[j] = Mma<bf16_t>::mac8(av[j], bop, oacc[j]);
   }
 
+  // kept-octet list of one chunk, packed for the passes: lane p of pq / pv
+  // holds list entries 4p..4p+3 (one byte each, score side / value side)
+  struct List {
+    uint32_t pq, pv;
+    int count;
+  };
+
   // Kept octets of chunk c as a lane-indexed list (ascending), then padding
   // after the `count` kept entries: the first kept octet for the score side,
-  // the zero column of V^T for the value side.
-  __device__ __forceinline__ void compute_chunk(int c, int buf, uint32_t mword) {
+  // the zero column of V^T for the value side.  Only the mask word is read,
+  // so a chunk's list is built before the chunk's barrier, while other waves
+  // still compute.
+  __device__ __forceinline__ List make_list(int c, uint32_t mword) const {
+    List li;
+    li.pq = li.pv = 0u;
     const int kbase = c * C::KC;
     uint32_t tb = uniform_u32(mword) >> ((c * C::TPC) & 31);
     if constexpr (C::TPC < 32) tb &= (1u << C::TPC) - 1u;
@@ -224,29 +235,32 @@ struct OctKernel {
     const int nval = left >= C::KC ? C::OPC : (left + 7) >> 3;
     const bool keep = lane < nval && ((tb >> ((lane & (C::OPC - 1)) >> C::LOG2R)) & 1u);
     const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
-    if (bal == 0ull) return;
-    const int count = __builtin_popcountll(bal);
+    li.count = __builtin_popcountll(bal);
+    if (bal == 0ull) return li;
     const int below = (int)prefix_count64(bal);
-    const int tgt = keep ? below : count + (lane - below);
+    const int tgt = keep ? below : li.count + (lane - below);
     const int lst = __builtin_amdgcn_ds_permute(tgt * 4, lane);
     const int first = __builtin_ctzll(bal);
-    const int lq = lane < count ? lst : first;
-    const int lv = lane < count ? lst : C::ZOCT;
-    // Lane p of pq / pv packs list entries 4p..4p+3 (one byte each); a pass
-    // reads its word as a wave-uniform value and every lane extracts the
-    // bytes it needs, which keeps the per-pass list lookups off the LDS.
+    const int lq = lane < li.count ? lst : first;
+    const int lv = lane < li.count ? lst : C::ZOCT;
     const int comb = lq | (lv << 8);
-    uint32_t pq = 0u, pv = 0u;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t x = (uint32_t)__builtin_amdgcn_ds_bpermute(((4 * lane + k) & 63) * 4, comb);
-      pq |= (x & 0xffu) << (8 * k);
-      pv |= ((x >> 8) & 0xffu) << (8 * k);
+      li.pq |= (x & 0xffu) << (8 * k);
+      li.pv |= ((x >> 8) & 0xffu) << (8 * k);
     }
+    return li;
+  }
+
+  // The passes of one chunk: a pass reads its packed word as a wave-uniform
+  // value and every lane extracts the bytes it needs, which keeps the
+  // per-pass list lookups off the LDS.
+  __device__ __forceinline__ void run_list(int buf, const List& li) {
     const uint32_t shq = 8u * (uint32_t)(n >> 3), shv = 8u * (uint32_t)(g >> 1);
-    for (int q0 = 0; q0 < count; q0 += 4) {
-      const uint32_t wq = (uint32_t)__builtin_amdgcn_readlane((int)pq, q0 >> 2);
-      const uint32_t wv = (uint32_t)__builtin_amdgcn_readlane((int)pv, q0 >> 2);
+    for (int q0 = 0; q0 < li.count; q0 += 4) {
+      const uint32_t wq = (uint32_t)__builtin_amdgcn_readlane((int)li.pq, q0 >> 2);
+      const uint32_t wv = (uint32_t)__builtin_amdgcn_readlane((int)li.pv, q0 >> 2);
       const int oq0 = (int)__builtin_amdgcn_ubfe(wq, shq, 8);
       const int oq1 = (int)__builtin_amdgcn_ubfe(wq, shq + 16u, 8);
       const int ovx = (int)__builtin_amdgcn_ubfe(wv, shv, 8);
@@ -290,17 +304,20 @@ struct OctKernel {
       doff[u] = I < C::NI ? dma_offset(I, lane, C::KC) : 0u;
     }
     const int n_chunks = (L + C::KC - 1) / C::KC;
-    uint32_t mcur = issue_chunk(0, 0);
+    const uint32_t m0 = issue_chunk(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
+    List cur = {0u, 0u, 0};
+    if (act) cur = make_list(0, m0);
     __syncthreads();
     for (int c = 0; c < n_chunks; ++c) {
       const int buf = c & 1;
+      const bool more = c + 1 < n_chunks;
       // buffer buf^1 was last read in iteration c-1, which every wave has left
-      const uint32_t mnext = c + 1 < n_chunks ? issue_chunk(c + 1, buf ^ 1) : 0u;
-      if (act) compute_chunk(c, buf, mcur);
+      const uint32_t mnext = more ? issue_chunk(c + 1, buf ^ 1) : 0u;
+      if (act) run_list(buf, cur);
       __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c+1 have landed
+      if (act && more) cur = make_list(c + 1, mnext);
       __syncthreads();                // ... and every other wave's
-      mcur = mnext;
     }
 
     const int r = row0 + n;
