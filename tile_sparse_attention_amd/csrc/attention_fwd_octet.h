@@ -146,18 +146,28 @@ struct OctKernel {
   // position q0+2b+(n>>3)).  The score accumulators leave lane group g with
   // keys 4(g&1)..4(g&1)+3 of octet ovx (position q0+(g>>1)) and of octet ovy
   // (position q0+2+(g>>1)), so its PV operand is two 8-byte V^T reads.
-  __device__ __forceinline__ void pass(int buf, int oq0, int oq1, int ovx, int ovy) {
+  // single: list positions 2 and 3 are padding; the second score block is
+  // then a copy of the first (real kept scores, multiplied by zero V^T
+  // columns), which saves its four MFMAs and K reads.
+  __device__ __forceinline__ void pass(int buf, int oq0, int oq1, int ovx, int ovy, bool single) {
     const float c = p.scale_log2;
     const uint8_t* kb = sm.k[buf] + (n & 7) * C::KRS + 16 * g;
     const uint8_t* ka0 = kb + oq0 * (8 * C::KRS);
     const uint8_t* ka1 = kb + oq1 * (8 * C::KRS);
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    if (single) {
 #pragma unroll
-    for (int sl = 0; sl < C::NSLAB; ++sl) {
-      const u32x4 a0 = *reinterpret_cast<const u32x4*>(ka0 + 64 * sl);
-      const u32x4 a1 = *reinterpret_cast<const u32x4*>(ka1 + 64 * sl);
-      s0 = Mma<bf16_t>::mac8(a0, qf[sl], s0);
-      s1 = Mma<bf16_t>::mac8(a1, qf[sl], s1);
+      for (int sl = 0; sl < C::NSLAB; ++sl)
+        s0 = Mma<bf16_t>::mac8(*reinterpret_cast<const u32x4*>(ka0 + 64 * sl), qf[sl], s0);
+      s1 = s0;
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < C::NSLAB; ++sl) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(ka0 + 64 * sl);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(ka1 + 64 * sl);
+        s0 = Mma<bf16_t>::mac8(a0, qf[sl], s0);
+        s1 = Mma<bf16_t>::mac8(a1, qf[sl], s1);
+      }
     }
     // The first V^T operands (and the ones row, the same bytes for all lanes
     // of a group) are read before the softmax so their latency overlaps it;
@@ -265,7 +275,7 @@ struct OctKernel {
       const int oq1 = (int)__builtin_amdgcn_ubfe(wq, shq + 16u, 8);
       const int ovx = (int)__builtin_amdgcn_ubfe(wv, shv, 8);
       const int ovy = (int)__builtin_amdgcn_ubfe(wv, shv + 16u, 8);
-      pass(buf, oq0, oq1, ovx, ovy);
+      pass(buf, oq0, oq1, ovx, ovy, li.count - q0 <= 2);
     }
   }
 
