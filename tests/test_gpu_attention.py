@@ -31,6 +31,16 @@ def test_bf16_tile_grid_ragged(M, N):
     full_compare(w, _hash_bits(w), f"bf16 d128 {M}x{N} L=1000")
 
 
+@pytest.mark.parametrize("N,L", [(8, 1001), (16, 1003), (32, 997), (64, 1029), (8, 13)])
+def test_bf16_sequence_ends_inside_an_octet(N, L):
+    torch_or_skip()
+    # L is not a multiple of 8: the last kept key tile has keys past L in its
+    # last 8-key run, which must take no part in the softmax (numerator or
+    # denominator).
+    w = small_workload(f"oct_tail_{N}_{L}", L, 128, 16, N, p=0.3, seed=7 * N + L)
+    full_compare(w, _hash_bits(w), f"bf16 d128 16x{N} L={L}")
+
+
 @pytest.mark.parametrize("dtype,d,N", [("f32", 128, 8), ("f32", 64, 1), ("f32", 64, 4),
                                        ("bf16", 64, 8), ("bf16", 64, 1), ("f32", 128, 64)])
 def test_dtype_and_head_dim(dtype, d, N):

@@ -21,23 +21,26 @@
 //     of kept octets with one ballot and one lane permutation (lane i of the
 //     list register holds the i-th kept octet).  A pass takes list entries
 //     4p..4p+3; a list shorter than a multiple of four is padded with the
-//     first kept octet for the score side (a real kept score, so the running
-//     max only sees real kept scores) and with the zero column of V^T for
-//     the value side, whose ones row is zero there as well.
+//     first kept octet (real kept scores, so the running max only sees real
+//     kept scores), whose probabilities the pass sets to zero.
 //   * Scores are formed transposed, S^T = K Q^T (A = K rows from LDS, B = the
 //     Q fragment); a 16-key score block holds two whole octets.  The
 //     accumulators are directly the B operand of O^T += V^T P^T
 //     (probabilities never leave registers); the matching A operand is two
 //     8-byte LDS reads of V^T columns per lane.  Row strides are chosen so
 //     that both reads are free of LDS bank conflicts for any octets.
-//   * The softmax denominator l comes from the same MFMA pipeline: the V^T
-//     workspace carries a ones row (zero past L and in the padding column),
-//     read as a broadcast (one address per lane group).
-//   * Online softmax in base 2, scale*log2(e) folded into one FMA per score;
-//     the reference max is raised (and O, l rescaled) only when some score
-//     exceeds it by more than 2^8, decided by one wave-wide ballot.
+//   * The softmax denominator l comes from the same MFMA pipeline, with a
+//     constant all-ones A operand in registers.
+//   * Online softmax in base 2 with c = |scale| * log2(e) (a negative scale
+//     negates the Q fragment, which is exact).  Every score accumulator
+//     starts from -m/c, m the running reference max, so a probability costs
+//     one multiply and one exp2 and the block maximum is compared with the
+//     rescale threshold as it comes out of the MFMAs.  The reference max is
+//     raised (and O, l rescaled) only when some score exceeds it by more than
+//     2^8, decided by one wave-wide ballot; the first pass sets it to that
+//     pass's maximum.
 //   * Keys past L in the last octet read K row L-1 (the loads clamp the row)
-//     and zero V^T columns, so they add nothing.
+//     and zero V^T columns; their probabilities are set to zero.
 #pragma once
 
 #include "attention_fwd_impl.h"
@@ -61,11 +64,11 @@ struct OctCfg {
   // bytes, which keeps their 8-byte column reads conflict-free.
   static constexpr int KRS = KRB + 32;
   static constexpr int VRB = KC * 2;               // V^T row bytes of one chunk
-  static constexpr int VRS = VRB + 16;             // V^T row stride in LDS (+ zero octet)
-  static constexpr int VROWS = D + 1;              // V^T rows incl. the ones row
-  static constexpr int ZOCT = OPC;                 // octet index of the zero column
+  static constexpr int VRS = VRB + 16;             // V^T row stride in LDS
+  static constexpr int VROWS = D + 1;              // V^T workspace rows (d = 0..D-1, ones row)
+  static constexpr int VROWS_LDS = D;              // V^T rows staged (the ones row is not read)
   static constexpr int NI_K = (KC * KRS + 1023) / 1024;     // 1-KB loads per K chunk
-  static constexpr int NI_V = (VROWS * VRS + 1023) / 1024;  // 1-KB loads per V^T chunk
+  static constexpr int NI_V = (VROWS_LDS * VRS + 1023) / 1024;  // 1-KB loads per V^T chunk
   static constexpr int NI = NI_K + NI_V;
   static constexpr int NI_W = (NI + W - 1) / W;
   static_assert(N >= 8 && N <= 64 && (N & (N - 1)) == 0, "octet kernel: N in {8,16,32,64}");
@@ -91,7 +94,12 @@ struct OctKernel {
   const uint32_t* __restrict__ mrow;
   u32x4 qf[C::NSLAB];
   f32x4 oacc[C::NDB + 1];
-  float m_run;
+  float m_ref;        // reference max of this lane's query (log2 units)
+  f32x4 nm4;          // -m_ref / cs in every element: the initial score accumulator
+  u32x4 ones;         // bf16 ones: the A operand that sums probabilities into l
+  float cs;           // |scale| * log2(e)
+  float thr;          // rescale threshold on unscaled scores: -inf before the first pass,
+                      // then RESCALE_STEP / cs
   uint32_t doff[C::NI_W];  // per-lane load offsets of a full chunk (chunk-invariant)
 
   __device__ __forceinline__ OctKernel(const AttnParams& pp, Smem& s) : p(pp), sm(s) {}
@@ -109,7 +117,7 @@ struct OctKernel {
     }
     const int pos = (I - C::NI_K) * 1024 + 16 * ln;
     const int row = pos / C::VRS, cb = pos - row * C::VRS;
-    return row < C::VROWS && cb < C::VRB ? (uint32_t)(row * p.L_pad * 2 + cb) : OOB;
+    return row < C::VROWS_LDS && cb < C::VRB ? (uint32_t)(row * p.L_pad * 2 + cb) : OOB;
   }
 
   // This wave's share of the loads of chunk c into buffer `buf`, and the
@@ -149,101 +157,130 @@ struct OctKernel {
   // single: list positions 2 and 3 are padding; the second score block is
   // then a copy of the first (real kept scores, multiplied by zero V^T
   // columns), which saves its four MFMAs and K reads.
-  __device__ __forceinline__ void pass(int buf, int oq0, int oq1, int ovx, int ovy, bool single) {
-    const float c = p.scale_log2;
-    const uint8_t* kb = sm.k[buf] + (n & 7) * C::KRS + 16 * g;
-    const uint8_t* ka0 = kb + oq0 * (8 * C::KRS);
-    const uint8_t* ka1 = kb + oq1 * (8 * C::KRS);
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+  // One pass over the four list positions q0..q0+3 (rem = entries left from
+  // q0; positions >= rem are padding).  Score block b (0, 1) holds the octets
+  // at positions q0+2b and q0+2b+1, eight key rows each: lane (g, n) reads
+  // row n&7 of the octet at position q0+2b+(n>>3), at LDS address ka<b>.
+  // The score accumulators leave lane group g with keys 4(g&1)..4(g&1)+3 of
+  // octet ovx (position q0+(g>>1)) and of octet ovy (position q0+2+(g>>1)),
+  // so its PV operand is two 8-byte V^T reads.  When positions 2 and 3 are
+  // padding (rem <= 2) the second score block is a copy of the first, which
+  // saves its four MFMAs and K reads.  lim: keys of the chunk that exist.
+  __device__ __forceinline__ void pass(int buf, uint32_t ka0, uint32_t ka1, int ovx, int ovy, int rem,
+                                       int lim) {
+    const bool single = rem <= 2;
+    // keeps the ones operand in registers instead of rebuilding it per pass
+    asm volatile("" : "+v"(ones));
+    f32x4 s0 = nm4, s1 = nm4;
     // Raised wave priority from the score MFMAs through the softmax: a wave
     // that reaches its score block is preferred over waves in their PV
-    // phase, which spreads the waves of a SIMD over the phases of a pass
-    // (measured 2-3% faster than equal priorities).
+    // phase, which spreads the waves of a SIMD over the phases of a pass.
     __builtin_amdgcn_s_setprio(1);
     if (single) {
 #pragma unroll
       for (int sl = 0; sl < C::NSLAB; ++sl)
-        s0 = Mma<bf16_t>::mac8(*reinterpret_cast<const u32x4*>(ka0 + 64 * sl), qf[sl], s0);
+        s0 = Mma<bf16_t>::mac8(lds_load<u32x4>(ka0 + 64 * sl), qf[sl], s0);
       s1 = s0;
     } else {
 #pragma unroll
       for (int sl = 0; sl < C::NSLAB; ++sl) {
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(ka0 + 64 * sl);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(ka1 + 64 * sl);
+        const u32x4 a0 = lds_load<u32x4>(ka0 + 64 * sl);
+        const u32x4 a1 = lds_load<u32x4>(ka1 + 64 * sl);
         s0 = Mma<bf16_t>::mac8(a0, qf[sl], s0);
         s1 = Mma<bf16_t>::mac8(a1, qf[sl], s1);
       }
     }
-    // The first V^T operands (and the ones row, the same bytes for all lanes
-    // of a group) are read before the softmax so their latency overlaps it;
-    // the rest after, within the register budget.
+    // The first V^T operands are read before the softmax so their latency
+    // overlaps it; the rest after, within the register budget.
     constexpr int EARLY = C::NDB / 2 - 1;
     const int half = 8 * (g & 1);
-    const uint8_t* vx = sm.vt[buf] + n * C::VRS + 16 * ovx + half;
-    const uint8_t* vy = sm.vt[buf] + n * C::VRS + 16 * ovy + half;
-    u32x4 av[C::NDB + 1];
+    const uint32_t vb = lds_addr(sm.vt[buf]) + (uint32_t)(n * C::VRS + half);
+    const uint32_t vx = shl4_add((uint32_t)ovx, vb);
+    const uint32_t vy = shl4_add((uint32_t)ovy, vb);
+    u32x4 av[C::NDB];
     auto vread = [&](int off) {
-      const u32x2 x = *reinterpret_cast<const u32x2*>(vx + off);
-      const u32x2 y = *reinterpret_cast<const u32x2*>(vy + off);
+      const u32x2 x = lds_load<u32x2>(vx + off);
+      const u32x2 y = lds_load<u32x2>(vy + off);
       return u32x4{x[0], x[1], y[0], y[1]};
     };
 #pragma unroll
     for (int j = 0; j < EARLY; ++j) av[j] = vread(16 * j * C::VRS);
-    {
-      const uint8_t* o1 = sm.vt[buf] + D * C::VRS + half;
-      const u32x2 x = *reinterpret_cast<const u32x2*>(o1 + 16 * ovx);
-      const u32x2 y = *reinterpret_cast<const u32x2*>(o1 + 16 * ovy);
-      av[C::NDB] = u32x4{x[0], x[1], y[0], y[1]};
-    }
-    float mr;
-    // (built with NaNs assumed absent, these fold into three-way max/min
+    // (built with NaNs assumed absent, these fold into three-way max
     // instructions without operand quieting)
-    if (c >= 0.f)
-      mr = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                 fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-    else
-      mr = fminf(fminf(fminf(s0[0], s0[1]), fminf(s0[2], s0[3])),
-                 fminf(fminf(s1[0], s1[1]), fminf(s1[2], s1[3])));
-    float mx = c * mr;
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_STEP) != 0ull) {
-      mx = fmaxf(mx, xor_lane16(mx));
-      mx = fmaxf(mx, xor_lane32(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2_fast(m_run - m_new);  // 0 on the first pass
-      m_run = m_new;
+    const float ma = fmaxf(fmaxf(s0[0], s0[1]), s0[2]);
+    const float mb = fmaxf(fmaxf(s0[3], s1[0]), s1[1]);
+    const float mr = fmaxf(fmaxf(ma, mb), fmaxf(s1[2], s1[3]));
+    if (__builtin_amdgcn_ballot_w64(mr > thr) != 0ull) {
+      const float mx = max_across_groups(mr) * cs;
+      const float delta = fmaxf(mx, thr == -INFINITY ? -INFINITY : 0.f);
+      const float alpha = exp2_fast(fminf(-delta, 0.f));
 #pragma unroll
       for (int j = 0; j <= C::NDB; ++j) oacc[j] *= alpha;
+      // (scale 0: every score is 0 and one pass fixes the reference for good)
+      const float ic = cs > 0.f ? 1.f / cs : 0.f;
+      thr = cs > 0.f ? RESCALE_STEP * ic : INFINITY;
+      m_ref += delta;
+      const float nmu = -m_ref * ic;
+      nm4 = f32x4{nmu, nmu, nmu, nmu};
+      const float du = delta * ic;
+      s0 -= du;
+      s1 -= du;
     }
-    const float nm = -m_run;
+    s0 *= cs;
+    s1 *= cs;
+    f32x4 e0, e1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      e0[i] = exp2_fast(s0[i]);
+      e1[i] = exp2_fast(s1[i]);
+    }
+    // keys past the end of the sequence (in the last, partial octet) carry no
+    // probability
+    if (lim & 7) {
+      const int k0 = 8 * ovx + 4 * (g & 1), k1 = 8 * ovy + 4 * (g & 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (k0 + i >= lim) e0[i] = 0.f;
+        if (k1 + i >= lim) e1[i] = 0.f;
+      }
+    }
     bf16x8 pb;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pb[i] = (__bf16)exp2_fast(__builtin_fmaf(s0[i], c, nm));
-      pb[4 + i] = (__bf16)exp2_fast(__builtin_fmaf(s1[i], c, nm));
+      pb[i] = (__bf16)e0[i];
+      pb[4 + i] = (__bf16)e1[i];
     }
-    const u32x4 bop = __builtin_bit_cast(u32x4, pb);
+    u32x4 bop = __builtin_bit_cast(u32x4, pb);
+    // padding list positions (the last pass of a list) carry no probability
+    if (rem < 4) {
+      if ((g >> 1) >= rem) { bop[0] = 0u; bop[1] = 0u; }
+      if (2 + (g >> 1) >= rem) { bop[2] = 0u; bop[3] = 0u; }
+    }
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int j = EARLY; j < C::NDB; ++j) av[j] = vread(16 * j * C::VRS);
 #pragma unroll
-    for (int j = 0; j <= C::NDB; ++j) oacc[j] = Mma<bf16_t>::mac8(av[j], bop, oacc[j]);
+    for (int j = 0; j < C::NDB; ++j) {
+      oacc[j] = Mma<bf16_t>::mac8(av[j], bop, oacc[j]);
+    }
+    oacc[C::NDB] = Mma<bf16_t>::mac8(ones, bop, oacc[C::NDB]);
   }
 
-  // kept-octet list of one chunk, packed for the passes: lane p of pq / pv
-  // holds list entries 4p..4p+3 (one byte each, score side / value side)
+  // kept-octet list of one chunk, packed for the passes: lane p of w holds
+  // list entries 4p..4p+3, one byte each
   struct List {
-    uint32_t pq, pv;
+    uint32_t w;
     int count;
   };
 
-  // Kept octets of chunk c as a lane-indexed list (ascending), then padding
-  // after the `count` kept entries: the first kept octet for the score side,
-  // the zero column of V^T for the value side.  Only the mask word is read,
-  // so a chunk's list is built before the chunk's barrier, while other waves
+  // Kept octets of chunk c as a lane-indexed list (ascending), padded after
+  // the `count` kept entries with the first kept octet (real kept scores,
+  // whose probabilities the pass zeroes).  Only the mask word is read, so a
+  // chunk's list is built before the chunk's barrier, while other waves
   // still compute.
   __device__ __forceinline__ List make_list(int c, uint32_t mword) const {
     List li;
-    li.pq = li.pv = 0u;
+    li.w = 0u;
     const int kbase = c * C::KC;
     uint32_t tb = uniform_u32(mword) >> ((c * C::TPC) & 31);
     if constexpr (C::TPC < 32) tb &= (1u << C::TPC) - 1u;
@@ -258,30 +295,25 @@ struct OctKernel {
     const int lst = __builtin_amdgcn_ds_permute(tgt * 4, lane);
     const int first = __builtin_ctzll(bal);
     const int lq = lane < li.count ? lst : first;
-    const int lv = lane < li.count ? lst : C::ZOCT;
-    const int comb = lq | (lv << 8);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t x = (uint32_t)__builtin_amdgcn_ds_bpermute(((4 * lane + k) & 63) * 4, comb);
-      li.pq |= (x & 0xffu) << (8 * k);
-      li.pv |= ((x >> 8) & 0xffu) << (8 * k);
-    }
+    for (int k = 0; k < 4; ++k)
+      li.w |= (uint32_t)__builtin_amdgcn_ds_bpermute(((4 * lane + k) & 63) * 4, lq) << (8 * k);
     return li;
   }
 
-  // The passes of one chunk: a pass reads its packed word as a wave-uniform
-  // value and every lane extracts the bytes it needs, which keeps the
-  // per-pass list lookups off the LDS.
-  __device__ __forceinline__ void run_list(int buf, const List& li) {
+  // The passes of one chunk (lim: keys of the chunk that exist): a pass
+  // reads its packed word as a wave-uniform value and every lane extracts
+  // the bytes it needs, which keeps the per-pass list lookups off the LDS.
+  __device__ __forceinline__ void run_list(int buf, const List& li, int lim) {
     const uint32_t shq = 8u * (uint32_t)(n >> 3), shv = 8u * (uint32_t)(g >> 1);
+    const uint32_t kb = lds_addr(sm.k[buf]) + (uint32_t)((n & 7) * C::KRS + 16 * g);
     for (int q0 = 0; q0 < li.count; q0 += 4) {
-      const uint32_t wq = (uint32_t)__builtin_amdgcn_readlane((int)li.pq, q0 >> 2);
-      const uint32_t wv = (uint32_t)__builtin_amdgcn_readlane((int)li.pv, q0 >> 2);
-      const int oq0 = (int)__builtin_amdgcn_ubfe(wq, shq, 8);
-      const int oq1 = (int)__builtin_amdgcn_ubfe(wq, shq + 16u, 8);
-      const int ovx = (int)__builtin_amdgcn_ubfe(wv, shv, 8);
-      const int ovy = (int)__builtin_amdgcn_ubfe(wv, shv + 16u, 8);
-      pass(buf, oq0, oq1, ovx, ovy, li.count - q0 <= 2);
+      const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)li.w, q0 >> 2);
+      const uint32_t ka0 = mad_u24(__builtin_amdgcn_ubfe(w, shq, 8), 8u * C::KRS, kb);
+      const uint32_t ka1 = mad_u24(__builtin_amdgcn_ubfe(w, shq + 16u, 8), 8u * C::KRS, kb);
+      const int ovx = (int)__builtin_amdgcn_ubfe(w, shv, 8);
+      const int ovy = (int)__builtin_amdgcn_ubfe(w, shv + 16u, 8);
+      pass(buf, ka0, ka1, ovx, ovy, li.count - q0, lim);
     }
   }
 
@@ -310,9 +342,18 @@ struct OctKernel {
     if (row0 + n >= L)
 #pragma unroll
       for (int s = 0; s < C::NSLAB; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
+    cs = p.scale_log2;
+    if (cs < 0.f) {
+      cs = -cs;
+#pragma unroll
+      for (int s = 0; s < C::NSLAB; ++s) qf[s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    }
 #pragma unroll
     for (int j = 0; j <= C::NDB; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_run = -INFINITY;
+    m_ref = 0.f;
+    nm4 = f32x4{0.f, 0.f, 0.f, 0.f};
+    thr = -INFINITY;
+    ones = u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
 
 #pragma unroll
     for (int u = 0; u < C::NI_W; ++u) {
@@ -322,7 +363,7 @@ struct OctKernel {
     const int n_chunks = (L + C::KC - 1) / C::KC;
     const uint32_t m0 = issue_chunk(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
-    List cur = {0u, 0u, 0};
+    List cur = {0u, 0};
     if (act) cur = make_list(0, m0);
     __syncthreads();
     for (int c = 0; c < n_chunks; ++c) {
@@ -330,7 +371,7 @@ struct OctKernel {
       const bool more = c + 1 < n_chunks;
       // buffer buf^1 was last read in iteration c-1, which every wave has left
       const uint32_t mnext = more ? issue_chunk(c + 1, buf ^ 1) : 0u;
-      if (act) run_list(buf, cur);
+      if (act) run_list(buf, cur, L - c * C::KC < C::KC ? L - c * C::KC : C::KC);
       __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c+1 have landed
       if (act && more) cur = make_list(c + 1, mnext);
       __syncthreads();                // ... and every other wave's
@@ -351,7 +392,7 @@ struct OctKernel {
     }
     if (p.lse != nullptr && g == 0)
       p.lse[(size_t)bh * L + r] =
-          l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+          l_tot > 0.f ? (m_ref + __builtin_log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
   }
 };
 

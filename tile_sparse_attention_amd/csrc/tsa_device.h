@@ -94,6 +94,39 @@ __device__ __forceinline__ int xcd_major_block(int b, int nb) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// LDS byte address of a pointer into a __shared__ array, and a typed LDS
+// load from such an address (integer address arithmetic keeps the per-pass
+// index math to one multiply-add or shift-add per address).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+template <typename T>
+__device__ __forceinline__ T lds_load(uint32_t a) {
+  return *(const __attribute__((address_space(3))) T*)(uintptr_t)a;
+}
+
+// a * b + c (24-bit operands, b wave-uniform) and (a << 4) + c as single
+// instructions; the compiler otherwise splits both into two.
+__device__ __forceinline__ uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ uint32_t shl4_add(uint32_t a, uint32_t c) {
+  uint32_t r;
+  asm("v_lshl_add_u32 %0, %1, 4, %2" : "=v"(r) : "v"(a), "v"(c));
+  return r;
+}
+
+// Maximum over lanes l, l^16, l^32 and l^48 (the four 16-lane rows of the
+// wave), with two lane swaps and no LDS traffic.
+__device__ __forceinline__ float max_across_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // A zero the compiler cannot see through: adding it to an index keeps a
 // loop-invariant computation inside the loop (recomputed, not kept live).
 __device__ __forceinline__ int opaque_zero() {
