@@ -52,6 +52,7 @@ namespace tsa {
 struct AttnParams {
   const void* q;
   const void* k;
+  const void* v;         // V [B*H][L][d] (read as rows by the key-packing kernel)
   const void* vt;        // packed V^T: [B*H][d + 1][L_pad], row d = ones (keys < L)
   const uint32_t* mask;
   void* o;

@@ -2,6 +2,7 @@
 #pragma once
 
 #include "attention_fwd_impl.h"
+#include "attention_fwd_keys.h"
 #include "attention_fwd_octet.h"
 #include "launch.h"
 
@@ -12,6 +13,7 @@ inline AttnParams attn_params(const AttnLaunch& a, int rows_per_block) {
   AttnParams p;
   p.q = a.q;
   p.k = a.k;
+  p.v = a.v;
   p.vt = a.workspace;
   p.mask = a.mask;
   p.o = a.o;
@@ -56,6 +58,17 @@ hipError_t launch_attn_oct(const AttnLaunch& a) {
   return hipGetLastError();
 }
 
+// bf16 with key tiles of N < 8: the key-packing kernel (V read as rows, no
+// V^T workspace).
+template <int D, int N>
+hipError_t launch_attn_key(const AttnLaunch& a) {
+  using C = KeyCfg<D, N>;
+  const AttnParams p = attn_params(a, C::ROWS);
+  const long long blocks = (long long)a.p->B * a.p->H * p.n_qblocks;
+  hipLaunchKernelGGL((attn_key_kernel<D, N>), dim3((unsigned)blocks), dim3(64 * C::W), 0, a.stream, p);
+  return hipGetLastError();
+}
+
 // Chunk size KC, waves per work-group W and 16-row tiles per wave TPW per
 // (element type, head dim, N): the double-buffered K and V^T chunks stay
 // within the 160 KB of LDS, and every variant fits the register file without
@@ -74,6 +87,8 @@ template <typename T, int D, int N>
 hipError_t launch_attn_n(const AttnLaunch& a) {
   if constexpr (sizeof(T) == 2 && N >= 8) {
     return launch_attn_oct<D, N>(a);
+  } else if constexpr (sizeof(T) == 2) {
+    return launch_attn_key<D, N>(a);
   } else {
     using S = AttnShape<T, D, N>;
     return launch_attn_cfg<T, D, N, S::KC, S::W, S::TPW>(a);

@@ -1,0 +1,350 @@
+// Tile-sparse attention forward kernel for bf16 and key tiles of N < 8 keys
+// (gfx950, wave64, 16x16x32 bf16 MFMA).
+//
+// Operation: FG-Attn ("FG-Attn: Leveraging Fine-Grained Sparse Attention in
+// Video Diffusion Models", section Abstract): the query-key dot products of
+// every M x N tile whose keep bit is 0 are skipped and those scores take no
+// part in the softmax; O = softmax(scale * Q K^T over kept tiles) V.  With
+// N = 1 a tile is a single key column of an M-row query tile.
+//
+// Kept keys are packed one by one, 32 per pass, into the contraction of the
+// matrix cores:
+//   * Work-groups, waves, chunk staging and the online softmax are those of
+//     the octet kernel (N >= 8): 16 waves own 16-row query tiles of 256
+//     consecutive rows; keys stream through LDS in double-buffered chunks of
+//     128, K and V both as rows (V is not transposed).
+//   * Per chunk a wave writes the ascending list of its kept keys (one byte
+//     each) into a small LDS area of its own, followed by 32 copies of the
+//     first kept key as padding.  Pass p takes list positions 32p..32p+31.
+//   * Scores S^T = K Q^T: score block b holds positions 16b..16b+15, lane
+//     (g, n) reading 16 bytes of the K row of position 16b+n.
+//   * PV: the A operand (V^T, 16 d values x 32 keys) comes from transposing
+//     LDS reads of V rows: in each 16-lane group g, lane s points at 4 d
+//     values of the key at position 4g+(s>>2), and the read hands lane n the
+//     value at d = n of the group's four keys, which is exactly the key order
+//     of the S^T accumulators (rows 4g..4g+3 of each score block).
+//   * l comes from a register ones operand; probabilities of padding
+//     positions and of keys past L are set to zero.
+// LDS bank conflicts: K and V rows are 288 bytes apart (160 for d = 64), so
+// eight keys read together are conflict-free when their indices differ
+// modulo 8; kept keys are arbitrary, so some reads take two or three rounds.
+#pragma once
+
+#include "attention_fwd_impl.h"
+
+namespace tsa {
+
+template <int D, int N>
+struct KeyCfg {
+  static constexpr int KC = 128;                   // keys per chunk
+  static constexpr int W = 16;                     // waves per work-group
+  static constexpr int ROWS = 16 * W;              // query rows per work-group
+  static constexpr int TPC = KC / N;               // key tiles per chunk (32, 64, 128)
+  static constexpr int MW = TPC / 32;              // mask words per chunk
+  static constexpr int LOG2N = ilog2(N);
+  static constexpr int NSLAB = D / 32;             // 32-wide d slabs of the QK^T contraction
+  static constexpr int NDB = D / 16;               // 16-wide d blocks of O^T
+  static constexpr int RB = D * 2;                 // K / V row bytes in memory
+  static constexpr int RS = RB + 32;               // K / V row stride in LDS
+  static constexpr int NI_T = (KC * RS + 1023) / 1024;  // 1-KB loads per K (or V) tile
+  static constexpr int NI = 2 * NI_T;
+  static constexpr int NI_W = (NI + W - 1) / W;
+  static constexpr int LIST = KC + 32;             // list bytes per wave (entries + padding)
+  static_assert(N == 1 || N == 2 || N == 4, "key kernel: N in {1,2,4}");
+  static_assert(D % 32 == 0 && MW >= 1 && MW <= 4, "shape");
+};
+
+template <int D, int N>
+struct KeyKernel {
+  using C = KeyCfg<D, N>;
+  static constexpr float RESCALE_STEP = 8.f;  // log2 units the max may grow before rescaling
+
+  struct Smem {
+    __attribute__((aligned(16))) uint8_t k[2][C::NI_T * 1024];
+    __attribute__((aligned(16))) uint8_t v[2][C::NI_T * 1024];
+    __attribute__((aligned(16))) uint8_t list[C::W][C::LIST];
+  };
+
+  const AttnParams& p;
+  Smem& sm;
+  int lane, g, n, wave, L;
+  const bf16_t* __restrict__ kg;
+  const bf16_t* __restrict__ vg;
+  const uint32_t* __restrict__ mrow;
+  u32x4 qf[C::NSLAB];
+  f32x4 oacc[C::NDB + 1];
+  float m_ref;        // reference max of this lane's query (log2 units)
+  f32x4 nm4;          // -m_ref / cs in every element: the initial score accumulator
+  u32x4 ones;         // bf16 ones: the A operand that sums probabilities into l
+  float cs;           // |scale| * log2(e)
+  float thr;          // rescale threshold on unscaled scores: -inf before the first pass,
+                      // then RESCALE_STEP / cs
+  uint32_t doff[C::NI_W];  // per-lane load offsets of a full chunk (chunk-invariant)
+
+  __device__ __forceinline__ KeyKernel(const AttnParams& pp, Smem& s) : p(pp), sm(s) {}
+
+  // Byte offset read by lane `ln` for 1-KB load `I` (K tile for I < NI_T,
+  // else V tile) of a chunk with `rows` keys, relative to the tile's
+  // resource base; out of range (reads zero) for the padding bytes of an LDS
+  // row.  Rows past the last key repeat it.
+  __device__ __forceinline__ uint32_t dma_offset(int I, int ln, int rows) const {
+    constexpr uint32_t OOB = 0x80000000u;
+    const int pos = (I < C::NI_T ? I : I - C::NI_T) * 1024 + 16 * ln;
+    const int row = pos / C::RS, cb = pos - row * C::RS;
+    const int r = row < rows ? row : rows - 1;
+    return row < C::KC && cb < C::RB ? (uint32_t)(r * C::RB + cb) : OOB;
+  }
+
+  // This wave's share of the loads of chunk c into buffer `buf`, and the
+  // mask words of chunk c (wave-uniform).  Nothing waits here.
+  __device__ __forceinline__ void issue_chunk(int c, int buf, uint32_t (&mw)[C::MW]) {
+    const int kbase = c * C::KC;
+    const int rows = L - kbase < C::KC ? L - kbase : C::KC;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kg + (size_t)kbase * D), (short)0, rows * C::RB, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vg + (size_t)kbase * D), (short)0, rows * C::RB, kBufferFlags);
+    const bool full = rows == C::KC;
+#pragma unroll
+    for (int u = 0; u < C::NI_W; ++u) {
+      const int I = wave + C::W * u;
+      if (C::NI % C::W == 0 || I < C::NI) {
+        const uint32_t off = full ? doff[u] : dma_offset(I, lane, rows);
+        if (I < C::NI_T)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rk, (__attribute__((address_space(3))) void*)(sm.k[buf] + I * 1024), 16, off, 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rv, (__attribute__((address_space(3))) void*)(sm.v[buf] + (I - C::NI_T) * 1024), 16,
+              off, 0, 0, 0);
+      }
+    }
+    const int w0 = (c * C::TPC) >> 5;
+#pragma unroll
+    for (int i = 0; i < C::MW; ++i) {
+      const int wi = w0 + i;
+      mw[i] = mrow[wi < p.words ? wi : p.words - 1];
+    }
+  }
+
+  // Kept keys of chunk c, ascending, into this wave's list area, then 32
+  // copies of the first kept key; returns the number of kept keys.  Lane l
+  // looks at keys l and l+64 of the chunk.  Only mask words are read, so the
+  // next chunk's list is written before the chunk barrier.
+  __device__ __forceinline__ int make_list(int c, const uint32_t (&mw)[C::MW]) const {
+    const int left = L - c * C::KC;  // keys of this chunk that exist
+    bool keep[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int key = lane + 64 * h;
+      const int t = key >> C::LOG2N;  // tile within the chunk
+      uint32_t w = uniform_u32(mw[0]);
+#pragma unroll
+      for (int i = 1; i < C::MW; ++i)
+        if ((t >> 5) == i) w = uniform_u32(mw[i]);
+      keep[h] = key < left && ((w >> (t & 31)) & 1u);
+    }
+    const uint64_t b0 = __builtin_amdgcn_ballot_w64(keep[0]);
+    const uint64_t b1 = __builtin_amdgcn_ballot_w64(keep[1]);
+    const int c0 = __builtin_popcountll(b0);
+    const int count = c0 + __builtin_popcountll(b1);
+    if (count == 0) return 0;
+    uint8_t* lst = sm.list[wave];
+    if (keep[0]) lst[prefix_count64(b0)] = (uint8_t)lane;
+    if (keep[1]) lst[c0 + prefix_count64(b1)] = (uint8_t)(lane + 64);
+    const int first = b0 != 0ull ? __builtin_ctzll(b0) : 64 + __builtin_ctzll(b1);
+    if (lane < 32) lst[count + lane] = (uint8_t)first;
+    return count;
+  }
+
+  // One pass over list positions q0..q0+31 (rem = entries left from q0;
+  // positions >= rem are padding).  Score block b holds positions
+  // q0+16b..q0+16b+15; the S^T accumulators leave lane group g with the keys
+  // at positions q0+4g..q0+4g+3 (block 0) and q0+16+4g.. (block 1), whose V
+  // values at d = n two transposing reads per d block deliver.  When
+  // positions 16..31 are all padding (rem <= 16) the second score block is a
+  // copy of the first.
+  __device__ __forceinline__ void pass(int buf, int q0, int rem) {
+    const bool single = rem <= 16;
+    // keeps the ones operand in registers instead of rebuilding it per pass
+    asm volatile("" : "+v"(ones));
+    const uint8_t* lst = sm.list[wave];
+    const uint32_t kk0 = lst[q0 + n], kk1 = lst[q0 + 16 + n];
+    const int vp = q0 + 4 * g + (n >> 2);
+    const uint32_t kv0 = lst[vp], kv1 = lst[vp + 16];
+    const uint32_t kb = lds_addr(sm.k[buf]) + (uint32_t)(16 * g);
+    const uint32_t ka0 = mad_u24(kk0, (uint32_t)C::RS, kb);
+    const uint32_t ka1 = mad_u24(kk1, (uint32_t)C::RS, kb);
+    f32x4 s0 = nm4, s1 = nm4;
+    // raised wave priority from the score MFMAs through the softmax (as in
+    // the octet kernel)
+    __builtin_amdgcn_s_setprio(1);
+    if (single) {
+#pragma unroll
+      for (int sl = 0; sl < C::NSLAB; ++sl)
+        s0 = Mma<bf16_t>::mac8(lds_load<u32x4>(ka0 + 64 * sl), qf[sl], s0);
+      s1 = s0;
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < C::NSLAB; ++sl) {
+        const u32x4 a0 = lds_load<u32x4>(ka0 + 64 * sl);
+        const u32x4 a1 = lds_load<u32x4>(ka1 + 64 * sl);
+        s0 = Mma<bf16_t>::mac8(a0, qf[sl], s0);
+        s1 = Mma<bf16_t>::mac8(a1, qf[sl], s1);
+      }
+    }
+    // V operands: lane (g, n) points at d = 4(n&3)..4(n&3)+3 of its V-side
+    // key; the transposing read returns d = n of the group's four keys.
+    constexpr int EARLY = C::NDB / 2 - 1;
+    const uint32_t vb = lds_addr(sm.v[buf]) + (uint32_t)(8 * (n & 3));
+    const uint32_t va0 = mad_u24(kv0, (uint32_t)C::RS, vb);
+    const uint32_t va1 = mad_u24(kv1, (uint32_t)C::RS, vb);
+    u32x4 av[C::NDB];
+    auto vread = [&](int j) {
+      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+      const u32x2 x = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(va0 + 32u * j)));
+      const u32x2 y = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(va1 + 32u * j)));
+      return u32x4{x[0], x[1], y[0], y[1]};
+    };
+#pragma unroll
+    for (int j = 0; j < EARLY; ++j) av[j] = vread(j);
+    const float ma = fmaxf(fmaxf(s0[0], s0[1]), s0[2]);
+    const float mb = fmaxf(fmaxf(s0[3], s1[0]), s1[1]);
+    const float mr = fmaxf(fmaxf(ma, mb), fmaxf(s1[2], s1[3]));
+    if (__builtin_amdgcn_ballot_w64(mr > thr) != 0ull) {
+      const float mx = max_across_groups(mr) * cs;
+      const float delta = fmaxf(mx, thr == -INFINITY ? -INFINITY : 0.f);
+      const float alpha = exp2_fast(fminf(-delta, 0.f));
+#pragma unroll
+      for (int j = 0; j <= C::NDB; ++j) oacc[j] *= alpha;
+      const float ic = cs > 0.f ? 1.f / cs : 0.f;
+      thr = cs > 0.f ? RESCALE_STEP * ic : INFINITY;
+      m_ref += delta;
+      const float nmu = -m_ref * ic;
+      nm4 = f32x4{nmu, nmu, nmu, nmu};
+      const float du = delta * ic;
+      s0 -= du;
+      s1 -= du;
+    }
+    f32x4 e0, e1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      e0[i] = exp2_fast(s0[i] * cs);
+      e1[i] = exp2_fast(s1[i] * cs);
+    }
+    // padding list positions (the last pass of a list) carry no probability
+    if (rem < 32) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (4 * g + i >= rem) e0[i] = 0.f;
+        if (16 + 4 * g + i >= rem) e1[i] = 0.f;
+      }
+    }
+    bf16x8 pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pb[i] = (__bf16)e0[i];
+      pb[4 + i] = (__bf16)e1[i];
+    }
+    const u32x4 bop = __builtin_bit_cast(u32x4, pb);
+    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int j = EARLY; j < C::NDB; ++j) av[j] = vread(j);
+#pragma unroll
+    for (int j = 0; j < C::NDB; ++j) oacc[j] = Mma<bf16_t>::mac8(av[j], bop, oacc[j]);
+    oacc[C::NDB] = Mma<bf16_t>::mac8(ones, bop, oacc[C::NDB]);
+  }
+
+  __device__ __forceinline__ void run() {
+    const int tid = threadIdx.x;
+    lane = tid & 63;
+    g = lane >> 4;
+    n = lane & 15;
+    wave = wave_uniform(tid >> 6);
+    const int lb = xcd_major_block((int)blockIdx.x, (int)gridDim.x);
+    const int bh = lb / p.n_qblocks;
+    const int qb = lb - bh * p.n_qblocks;
+    L = p.L;
+    const size_t head_off = (size_t)bh * (size_t)L * D;
+    const bf16_t* __restrict__ qg = reinterpret_cast<const bf16_t*>(p.q) + head_off;
+    kg = reinterpret_cast<const bf16_t*>(p.k) + head_off;
+    vg = reinterpret_cast<const bf16_t*>(p.v) + head_off;
+
+    const int row0 = qb * C::ROWS + 16 * wave;
+    const bool act = row0 < L;
+    mrow = p.mask + ((size_t)bh * p.T_q + (size_t)(act ? row0 / p.M : 0)) * p.words;
+    const int rq = row0 + n < L ? row0 + n : L - 1;
+#pragma unroll
+    for (int s = 0; s < C::NSLAB; ++s)
+      qf[s] = *reinterpret_cast<const u32x4*>(qg + (size_t)rq * D + 32 * s + 8 * g);
+    if (row0 + n >= L)
+#pragma unroll
+      for (int s = 0; s < C::NSLAB; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
+    cs = p.scale_log2;
+    if (cs < 0.f) {  // c*s = |c| * ((-q) . k), and negating bf16 is exact
+      cs = -cs;
+#pragma unroll
+      for (int s = 0; s < C::NSLAB; ++s) qf[s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    }
+#pragma unroll
+    for (int j = 0; j <= C::NDB; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_ref = 0.f;
+    nm4 = f32x4{0.f, 0.f, 0.f, 0.f};
+    thr = -INFINITY;
+    ones = u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+
+#pragma unroll
+    for (int u = 0; u < C::NI_W; ++u) {
+      const int I = wave + C::W * u;
+      doff[u] = I < C::NI ? dma_offset(I, lane, C::KC) : 0u;
+    }
+    const int n_chunks = (L + C::KC - 1) / C::KC;
+    uint32_t mw[C::MW];
+    issue_chunk(0, 0, mw);
+    __builtin_amdgcn_s_waitcnt(0);
+    int count = act ? make_list(0, mw) : 0;
+    __syncthreads();
+    for (int c = 0; c < n_chunks; ++c) {
+      const int buf = c & 1;
+      const bool more = c + 1 < n_chunks;
+      // buffer buf^1 was last read in iteration c-1, which every wave has left
+      uint32_t mwn[C::MW];
+      if (more) issue_chunk(c + 1, buf ^ 1, mwn);
+      if (act)
+        for (int q0 = 0; q0 < count; q0 += 32) pass(buf, q0, count - q0);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c+1 have landed
+      if (act && more) count = make_list(c + 1, mwn);
+      __syncthreads();                // ... and every other wave's
+    }
+
+    const int r = row0 + n;
+    if (r >= L) return;
+    const float l_tot = oacc[C::NDB][0];
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    bf16_t* og = reinterpret_cast<bf16_t*>(p.o) + head_off + (size_t)r * D;
+#pragma unroll
+    for (int j = 0; j < C::NDB; ++j) {
+      const f32x4 val = oacc[j] * inv;
+      bf16x4 ob;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ob[i] = (__bf16)val[i];
+      *reinterpret_cast<u32x2*>(og + 16 * j + 4 * g) = __builtin_bit_cast(u32x2, ob);
+    }
+    if (p.lse != nullptr && g == 0)
+      p.lse[(size_t)bh * L + r] =
+          l_tot > 0.f ? (m_ref + __builtin_log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+  }
+};
+
+template <int D, int N>
+__global__ __launch_bounds__(1024) void attn_key_kernel(AttnParams p) {
+  static_assert(KeyCfg<D, N>::W == 16, "launch bounds: 16 waves");
+  using K = KeyKernel<D, N>;
+  __shared__ __attribute__((aligned(16))) typename K::Smem sm;
+  K k(p, sm);
+  k.run();
+}
+
+}  // namespace tsa
