@@ -81,8 +81,11 @@ tsa_status_t tsa_workspace_size(tsa_op_t op, const tsa_problem_t* p, size_t* byt
  * multiplied on bf16 matrix cores with the probabilities rounded to bf16.
  * workspace: tsa_workspace_size(TSA_OP_ATTENTION_FWD) bytes, 256-byte aligned;
  * the call packs V transposed into it (B*H*(d+1)*ceil(L/128)*128 elements)
- * before the attention kernel reads it.  Its contents are not needed after
- * the call returns control of the stream. */
+ * and, for bf16 with N >= 8 and L <= 262144, writes after it (at the next
+ * 256-byte boundary) a 64-word bitmap of the 128-key chunks each group of
+ * 256 query rows keeps a tile of, one flag word per group and a count of
+ * flagged groups, before the attention kernels read them.  Its contents are not needed after the call
+ * returns control of the stream. */
 tsa_status_t tsa_attention_fwd(const tsa_problem_t* p,
                                const void* q, const void* k, const void* v,
                                const uint32_t* mask_bits, float scale,

@@ -41,7 +41,10 @@ def test_row_words():
 
 def test_workspace_sizes():
     pr = T.problem(1, 40, 32760, 128, 16, 8)
-    assert T.workspace_size(T.OP_ATTENTION_FWD, pr) == 40 * 129 * 32768 * 2
+    # packed V^T, then (bf16, N >= 8) 64 chunk-bitmap words and a flag per
+    # work-group of 256 query rows, and a count
+    assert T.workspace_size(T.OP_ATTENTION_FWD, pr) == 40 * 129 * 32768 * 2 + (40 * 128 * 65 + 1) * 4
+    assert T.workspace_size(T.OP_ATTENTION_FWD, T.problem(1, 40, 32760, 128, 16, 4)) == 40 * 129 * 32768 * 2
     assert T.workspace_size(T.OP_MASK_COMPACT, pr) >= 40 * 2048 * 4
     pp = T.problem(1, 24, 118800, 128, 16, 16)
     ws = T.workspace_size(T.OP_PREDICT_MASK, pp)

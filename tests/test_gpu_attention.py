@@ -41,6 +41,28 @@ def test_bf16_sequence_ends_inside_an_octet(N, L):
     full_compare(w, _hash_bits(w), f"bf16 d128 16x{N} L={L}")
 
 
+@pytest.mark.parametrize("M,N", [(16, 8), (16, 16), (64, 64), (32, 8)])
+def test_bf16_banded_mask_skips_chunks(M, N):
+    torch_or_skip()
+    # Each query tile keeps key tiles within a band around the diagonal, and
+    # the rows of the second 256-row group keep nothing: most 128-key chunks
+    # are needed by no row of a 256-row group (the chunk-skipping kernel).
+    L = 3000
+    w = small_workload(f"band_{M}x{N}", L, 128, M, N, seed=31 + M + N)
+    rng = np.random.default_rng(M * 100 + N)
+    keep = np.zeros((1, 2, w.T_q, w.T_k), dtype=bool)
+    for h in range(2):
+        for i in range(w.T_q):
+            r0 = i * M
+            if 256 <= r0 < 512:
+                continue
+            lo = max(0, (r0 - 200) // N)
+            hi = min(w.T_k, (r0 + M + 200) // N + 1)
+            keep[0, h, i, lo:hi] = rng.random(hi - lo) < 0.5
+            keep[0, h, i, min(w.T_k - 1, r0 // N)] = True
+    full_compare(w, W.pack_bits(keep), f"bf16 banded {M}x{N} L={L}")
+
+
 @pytest.mark.parametrize("dtype,d,N", [("f32", 128, 8), ("f32", 64, 1), ("f32", 64, 4),
                                        ("bf16", 64, 8), ("bf16", 64, 1), ("f32", 128, 64)])
 def test_dtype_and_head_dim(dtype, d, N):

@@ -90,7 +90,7 @@ tsa_status_t tsa_workspace_size(tsa_op_t op, const tsa_problem_t* p, size_t* byt
   switch (op) {
     case TSA_OP_ATTENTION_FWD:
       if ((s = check_problem(p, true)) != TSA_OK) return s;
-      *bytes = tsa::attention_vt_bytes(p);
+      *bytes = tsa::attention_workspace_bytes(p);
       return TSA_OK;
     case TSA_OP_MASK_COMPACT:
       if ((s = check_problem(p, false)) != TSA_OK) return s;
@@ -116,7 +116,7 @@ tsa_status_t tsa_attention_fwd(const tsa_problem_t* p, const void* q, const void
       !aligned(mask_bits, 4) || (lse && !aligned(lse, 4)))
     return fail(TSA_ERR_INVALID_ARGUMENT, "q/k/v/o need 16-byte, mask/lse 4-byte alignment");
   if (o == q || o == k || o == v) return fail(TSA_ERR_INVALID_ARGUMENT, "o aliases an input");
-  const size_t need = tsa::attention_vt_bytes(p);
+  const size_t need = tsa::attention_workspace_bytes(p);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
     return fail(TSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, 256-byte aligned (got %zu)",
                 need, workspace_bytes);

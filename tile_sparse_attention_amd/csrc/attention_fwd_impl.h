@@ -61,6 +61,12 @@ struct AttnParams {
   int L_pad;             // row length of the packed V^T (multiple of 128)
   int n_qblocks;
   float scale_log2;  // scale * log2(e)
+  // chunk skipping (octet kernel): per work-group, kNeedWords bitmap words
+  // of needed chunks, one flag word per work-group, and the number of
+  // flagged work-groups (null: no skipping)
+  const uint32_t* need;
+  const uint32_t* need_flag;
+  const uint32_t* need_count;
 };
 
 template <typename T> struct ElemTraits;

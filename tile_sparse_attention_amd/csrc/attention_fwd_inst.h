@@ -27,6 +27,9 @@ inline AttnParams attn_params(const AttnLaunch& a, int rows_per_block) {
   p.L_pad = attention_l_pad(pr.L);
   p.n_qblocks = (pr.L + rows_per_block - 1) / rows_per_block;
   p.scale_log2 = a.scale * 1.4426950408889634f;
+  p.need = nullptr;
+  p.need_flag = nullptr;
+  p.need_count = nullptr;
   return p;
 }
 
@@ -48,13 +51,32 @@ hipError_t launch_attn_cfg(const AttnLaunch& a) {
 }
 
 // bf16 with key tiles of N >= 8: the octet-packing kernel.
+// With chunk skipping (at most kMaxChunks chunks), chunk_need_kernel first
+// sorts the work-groups into those that need nearly every chunk (run by the
+// plain kernel) and the rest (run by the skipping kernel).
 template <int D, int N>
 hipError_t launch_attn_oct(const AttnLaunch& a) {
   using C = OctCfg<D, N>;
-  const AttnParams p = attn_params(a, C::ROWS);
+  AttnParams p = attn_params(a, C::ROWS);
   const long long blocks = (long long)a.p->B * a.p->H * p.n_qblocks;
   launch_vt_pack<bf16_t, D>(a, p);
-  hipLaunchKernelGGL((attn_oct_kernel<D, N>), dim3((unsigned)blocks), dim3(64 * C::W), 0, a.stream, p);
+  if (!attention_skips_chunks(a.p)) {
+    hipLaunchKernelGGL((attn_oct_kernel<D, N, false>), dim3((unsigned)blocks), dim3(64 * C::W), 0,
+                       a.stream, p);
+    return hipGetLastError();
+  }
+  uint32_t* need = reinterpret_cast<uint32_t*>(static_cast<char*>(a.workspace) +
+                                               attention_need_offset(a.p));
+  uint32_t* flag = need + attention_groups(a.p) * kNeedWords;
+  uint32_t* count = flag + attention_groups(a.p);
+  p.need = need;
+  p.need_flag = flag;
+  p.need_count = count;
+  hipLaunchKernelGGL(zero_word_kernel<uint32_t>, dim3(1), dim3(64), 0, a.stream, count);
+  hipLaunchKernelGGL((chunk_need_kernel<N>), dim3((unsigned)blocks), dim3(256), 0, a.stream, p, need, flag,
+                     count);
+  hipLaunchKernelGGL((attn_oct_kernel<D, N, false>), dim3((unsigned)blocks), dim3(64 * C::W), 0, a.stream, p);
+  hipLaunchKernelGGL((attn_oct_kernel<D, N, true>), dim3((unsigned)blocks), dim3(64 * C::W), 0, a.stream, p);
   return hipGetLastError();
 }
 

@@ -43,7 +43,10 @@
 //     and zero V^T columns; their probabilities are set to zero.
 #pragma once
 
+#include <type_traits>
+
 #include "attention_fwd_impl.h"
+#include "launch.h"
 
 namespace tsa {
 
@@ -76,15 +79,22 @@ struct OctCfg {
   static_assert(TPC <= 16, "tile bits of a chunk fit one mask word");
 };
 
-template <int D, int N>
+// SKIP: the work-group visits only the chunks its bitmap marks as needed
+// (work-groups flagged by chunk_need_kernel); otherwise every chunk (the
+// work-groups not flagged).
+template <int D, int N, bool SKIP>
 struct OctKernel {
   using C = OctCfg<D, N>;
   static constexpr float RESCALE_STEP = 8.f;  // log2 units the max may grow before rescaling
 
-  struct Smem {
+  struct SmemPlain {
     __attribute__((aligned(16))) uint8_t k[2][C::NI_K * 1024];
     __attribute__((aligned(16))) uint8_t vt[2][C::NI_V * 1024];
   };
+  struct SmemSkip : SmemPlain {
+    uint16_t clist[kMaxChunks];  // needed chunks, ascending
+  };
+  using Smem = typename std::conditional<SKIP, SmemSkip, SmemPlain>::type;
 
   const AttnParams& p;
   Smem& sm;
@@ -324,6 +334,17 @@ struct OctKernel {
     n = lane & 15;
     wave = wave_uniform(tid >> 6);
     const int lb = xcd_major_block((int)blockIdx.x, (int)gridDim.x);
+    // The plain and the skipping kernel each run the work-groups of their
+    // kind.  Skipping is used only when at least a quarter of all
+    // work-groups would gain from it: the skipping kernel runs after the
+    // plain one, so a few flagged work-groups would run alone at the end.
+    if (p.need_flag != nullptr) {
+      const bool many = (long long)wave_uniform((int)*p.need_count) * 4 >= (long long)gridDim.x;
+      const bool mine = many && wave_uniform((int)p.need_flag[lb]) != 0;
+      if (mine != SKIP) return;
+    } else if (SKIP) {
+      return;
+    }
     const int bh = lb / p.n_qblocks;
     const int qb = lb - bh * p.n_qblocks;
     L = p.L;
@@ -348,6 +369,11 @@ struct OctKernel {
 #pragma unroll
       for (int s = 0; s < C::NSLAB; ++s) qf[s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
     }
+    // The fragment is complete here: later code sees registers written by
+    // this statement, not loads in flight, so no load wait lands in the
+    // chunk loop.
+#pragma unroll
+    for (int s = 0; s < C::NSLAB; ++s) asm volatile("" : "+v"(qf[s]));
 #pragma unroll
     for (int j = 0; j <= C::NDB; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_ref = 0.f;
@@ -361,20 +387,72 @@ struct OctKernel {
       doff[u] = I < C::NI ? dma_offset(I, lane, C::KC) : 0u;
     }
     const int n_chunks = (L + C::KC - 1) / C::KC;
-    const uint32_t m0 = issue_chunk(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    List cur = {0u, 0};
-    if (act) cur = make_list(0, m0);
-    __syncthreads();
-    for (int c = 0; c < n_chunks; ++c) {
-      const int buf = c & 1;
-      const bool more = c + 1 < n_chunks;
-      // buffer buf^1 was last read in iteration c-1, which every wave has left
-      const uint32_t mnext = more ? issue_chunk(c + 1, buf ^ 1) : 0u;
-      if (act) run_list(buf, cur, L - c * C::KC < C::KC ? L - c * C::KC : C::KC);
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c+1 have landed
-      if (act && more) cur = make_list(c + 1, mnext);
-      __syncthreads();                // ... and every other wave's
+    if constexpr (SKIP) {
+      // The needed chunks, ascending, into an LDS list: lane i of wave 0
+      // expands bitmap word i at its prefix-sum offset.
+      const int nw = (n_chunks + 31) >> 5;
+      const uint32_t needv = lane < nw ? p.need[(size_t)lb * kNeedWords + lane] : 0u;
+      const int cntw = __builtin_popcount(needv);
+      int incl = cntw;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      const int n_need = wave_uniform(__shfl(incl, 63));
+      if (wave == 0) {
+        int pos = incl - cntw;
+        uint32_t bits = needv;
+        while (bits != 0u) {
+          const int b = __builtin_ctz(bits);
+          bits &= bits - 1u;
+          sm.clist[pos++] = (uint16_t)(32 * lane + b);
+        }
+      }
+      __syncthreads();
+      auto chunk_at = [&](int k) -> int {
+        return k < n_need ? (int)uniform_u32(sm.clist[k]) : n_chunks;
+      };
+      int k = 0;
+      int c = chunk_at(0);
+      List cur = {0u, 0};
+      if (c < n_chunks) {
+        const uint32_t m0 = issue_chunk(c, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+        if (act) cur = make_list(c, m0);
+      }
+      int cn = chunk_at(1);
+      __syncthreads();
+      for (int buf = 0; c < n_chunks; buf ^= 1) {
+        const bool more = cn < n_chunks;
+        // buffer buf^1 was last read in the previous iteration, which every
+        // wave has left
+        const uint32_t mnext = more ? issue_chunk(cn, buf ^ 1) : 0u;
+        const int cnn = chunk_at(k + 2);
+        if (act) run_list(buf, cur, L - c * C::KC < C::KC ? L - c * C::KC : C::KC);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk cn have landed
+        if (act && more) cur = make_list(cn, mnext);
+        __syncthreads();                // ... and every other wave's
+        c = cn;
+        cn = cnn;
+        ++k;
+      }
+    } else {
+      const uint32_t m0 = issue_chunk(0, 0);
+      __builtin_amdgcn_s_waitcnt(0);
+      List cur = {0u, 0};
+      if (act) cur = make_list(0, m0);
+      __syncthreads();
+      for (int c = 0; c < n_chunks; ++c) {
+        const int buf = c & 1;
+        const bool more = c + 1 < n_chunks;
+        // buffer buf^1 was last read in iteration c-1, which every wave has left
+        const uint32_t mnext = more ? issue_chunk(c + 1, buf ^ 1) : 0u;
+        if (act) run_list(buf, cur, L - c * C::KC < C::KC ? L - c * C::KC : C::KC);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c+1 have landed
+        if (act && more) cur = make_list(c + 1, mnext);
+        __syncthreads();                // ... and every other wave's
+      }
     }
 
     const int r = row0 + n;
@@ -396,13 +474,67 @@ struct OctKernel {
   }
 };
 
-template <int D, int N>
+template <int D, int N, bool SKIP>
 __global__ __launch_bounds__(1024) void attn_oct_kernel(AttnParams p) {
   static_assert(OctCfg<D, N>::W == 16, "launch bounds: 16 waves");
-  using K = OctKernel<D, N>;
+  static_assert(OctCfg<D, N>::KC == kChunkKeys && OctCfg<D, N>::ROWS == kRowsPerGroup, "chunk layout");
+  using K = OctKernel<D, N, SKIP>;
   __shared__ __attribute__((aligned(16))) typename K::Smem sm;
   K k(p, sm);
   k.run();
+}
+
+// One work-group per attention work-group (logical numbering): ORs the mask
+// rows of its 256 query rows word by word, marks the 128-key chunks with a
+// kept tile in a bitmap (need, kNeedWords words per work-group) and flags
+// the work-group when fewer than 7/8 of the chunks are needed (counted in
+// `count`, zeroed beforehand).  Mask padding bits past T_k can only mark the
+// last chunk.
+template <typename T>
+__global__ __launch_bounds__(64) void zero_word_kernel(T* w) {
+  if (threadIdx.x == 0) *w = T(0);
+}
+
+template <int N>
+__global__ __launch_bounds__(256) void chunk_need_kernel(AttnParams p, uint32_t* need, uint32_t* flag,
+                                                         uint32_t* count) {
+  constexpr int TPC = kChunkKeys / N;  // key tiles per chunk (<= 16)
+  constexpr int CPW = 32 / TPC;        // chunks per mask word
+  constexpr uint32_t TMASK = (1u << TPC) - 1u;
+  __shared__ uint32_t words[kNeedWords];
+  __shared__ int cnt;
+  const int tid = threadIdx.x;
+  const int g = blockIdx.x;
+  const int bh = g / p.n_qblocks, qb = g - (g / p.n_qblocks) * p.n_qblocks;
+  const int n_chunks = (p.L + kChunkKeys - 1) / kChunkKeys;
+  const int nw = (n_chunks + 31) >> 5;
+  for (int i = tid; i < kNeedWords; i += 256) words[i] = 0u;
+  if (tid == 0) cnt = 0;
+  __syncthreads();
+  const int r0 = qb * kRowsPerGroup;
+  const int r1 = r0 + kRowsPerGroup < p.L ? r0 + kRowsPerGroup : p.L;
+  const int i0 = r0 / p.M, i1 = (r1 - 1) / p.M;
+  const uint32_t* rows = p.mask + ((size_t)bh * p.T_q + i0) * p.words;
+  for (int j = tid; j < p.words; j += 256) {
+    uint32_t w = 0u;
+    for (int i = 0; i <= i1 - i0; ++i) w |= rows[(size_t)i * p.words + j];
+#pragma unroll
+    for (int h = 0; h < CPW; ++h) {
+      const int c = j * CPW + h;
+      if (((w >> (h * TPC)) & TMASK) != 0u && c < n_chunks) atomicOr(&words[c >> 5], 1u << (c & 31));
+    }
+  }
+  __syncthreads();
+  if (tid < kNeedWords) {
+    need[(size_t)g * kNeedWords + tid] = words[tid];
+    if (tid < nw) atomicAdd(&cnt, __builtin_popcount(words[tid]));
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const bool f = cnt * 8 < n_chunks * 7;
+    flag[g] = f ? 1u : 0u;
+    if (f) atomicAdd(count, 1u);
+  }
 }
 
 }  // namespace tsa

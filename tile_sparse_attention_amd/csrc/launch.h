@@ -18,7 +18,7 @@ struct AttnLaunch {
   float scale;
   void* o;
   float* lse;
-  void* workspace;  // packed V^T, attention_vt_bytes() bytes
+  void* workspace;  // packed V^T, then chunk bitmaps: attention_workspace_bytes()
   hipStream_t stream;
 };
 
@@ -27,6 +27,25 @@ inline int attention_l_pad(int L) { return (L + 127) / 128 * 128; }
 inline size_t attention_vt_bytes(const tsa_problem_t* p) {
   const size_t elt = p->dtype == TSA_DTYPE_BF16 ? 2 : 4;
   return (size_t)p->B * p->H * (size_t)(p->d + 1) * (size_t)attention_l_pad(p->L) * elt;
+}
+
+// Chunk skipping (bf16, N >= 8, at most 2048 chunks of 128 keys): per
+// work-group of 256 query rows, a 64-word bitmap of the key chunks any of
+// its rows keeps a tile of and a flag word (1: skipping would pay off for
+// it), then one count of flagged work-groups.
+constexpr int kChunkKeys = 128, kRowsPerGroup = 256, kMaxChunks = 2048, kNeedWords = kMaxChunks / 32;
+inline bool attention_skips_chunks(const tsa_problem_t* p) {
+  return p->dtype == TSA_DTYPE_BF16 && p->N >= 8 && (p->L + kChunkKeys - 1) / kChunkKeys <= kMaxChunks;
+}
+inline size_t attention_groups(const tsa_problem_t* p) {
+  return (size_t)p->B * p->H * (size_t)((p->L + kRowsPerGroup - 1) / kRowsPerGroup);
+}
+inline size_t attention_need_offset(const tsa_problem_t* p) {
+  return (attention_vt_bytes(p) + 255) / 256 * 256;
+}
+inline size_t attention_workspace_bytes(const tsa_problem_t* p) {
+  if (!attention_skips_chunks(p)) return attention_vt_bytes(p);
+  return attention_need_offset(p) + (attention_groups(p) * (kNeedWords + 1) + 1) * sizeof(uint32_t);
 }
 
 hipError_t launch_attention_bf16(const AttnLaunch& a);
