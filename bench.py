@@ -55,6 +55,8 @@ def make_mask(w, q, k):
     kind = w.mask.kind
     if kind == "hash":
         return T.maskgen_hash(w.B, w.H, w.L, w.M, w.N, **W.hash_params(w))
+    if kind == "structured":
+        return T.maskgen_structured(w.B, w.H, w.L, w.M, w.N, **W.structured_params(w))
     if kind == "predicted":
         return T.predict_mask(q, k, w.M, w.N, w.mask.sparsity_percent)
     bits = W.mask_bits(w)

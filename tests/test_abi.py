@@ -124,6 +124,28 @@ def test_maskgen_validation():
                                 None) == T.ERR_INVALID_ARGUMENT
 
 
+def test_structured_maskgen_validation():
+    lib = T.lib()
+    pr = T.problem(1, 2, 512, 64, 16, 16)
+    out = ctypes.c_void_p(0x1000)
+    g = T.StructuredParams(10, 4, 64, 2, 16, 4)
+
+    def call(pats, params=g, prob=pr):
+        arr = (ctypes.c_int32 * len(pats))(*pats)
+        return lib.tsa_maskgen_structured(ctypes.byref(prob), ctypes.byref(params), arr, out, None)
+
+    assert call([0, 5]) == T.ERR_INVALID_ARGUMENT                       # unknown pattern
+    assert call([1, -1]) == T.ERR_INVALID_ARGUMENT
+    assert call([2, 1], T.StructuredParams(10, 4, 0, 2, 16, 4)) == T.ERR_INVALID_ARGUMENT  # frame 0
+    assert call([2, 1], T.StructuredParams(10, 4, 64, 65, 16, 4)) == T.ERR_INVALID_ARGUMENT  # reach
+    assert call([3, 1], T.StructuredParams(10, 4, 64, 2, 16, 17)) == T.ERR_INVALID_ARGUMENT  # stripe
+    assert call([1, 1], T.StructuredParams(-1, 4, 64, 2, 16, 4)) == T.ERR_INVALID_ARGUMENT
+    big = T.problem(1, 129, 512, 64, 16, 16)
+    assert call([1] * 129, prob=big) == T.ERR_UNSUPPORTED
+    assert lib.tsa_maskgen_structured(ctypes.byref(pr), None, (ctypes.c_int32 * 2)(1, 1), out,
+                                      None) == T.ERR_INVALID_ARGUMENT
+
+
 def test_status_strings():
     assert T.status_string(T.OK) == "success"
     assert T.status_string(T.ERR_HIP) == "HIP runtime error"

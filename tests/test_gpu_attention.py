@@ -63,6 +63,20 @@ def test_bf16_banded_mask_skips_chunks(M, N):
     full_compare(w, W.pack_bits(keep), f"bf16 banded {M}x{N} L={L}")
 
 
+@pytest.mark.parametrize("M,N", [(16, 8), (16, 16), (64, 64), (16, 1)])
+def test_bf16_structured_masks_and_skipped_heads(M, N):
+    torch_or_skip()
+    # one head per pattern of the structured generator, two of them empty
+    # (skipped heads: output zero, LSE -inf)
+    pats = (0, 1, 2, 3, 4, 0)
+    L = 2100
+    w = W.Workload(f"struct_{M}x{N}", 1, len(pats), L, 128, M, N, "bf16",
+                   W.MaskRecipe("structured", frame_tokens=330, patterns=pats, diag_width=300,
+                                band_width=20, reach=3, stripe_period=260, stripe_width=40,
+                                force_diag=False), 41 + M + N)
+    full_compare(w, W.mask_bits(w), f"bf16 structured {M}x{N} L={L}")
+
+
 @pytest.mark.parametrize("dtype,d,N", [("f32", 128, 8), ("f32", 64, 1), ("f32", 64, 4),
                                        ("bf16", 64, 8), ("bf16", 64, 1), ("f32", 128, 64)])
 def test_dtype_and_head_dim(dtype, d, N):

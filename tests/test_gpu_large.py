@@ -44,18 +44,23 @@ def _head_bits_from_rows(w, h, tiles):
     return out
 
 
-@pytest.mark.parametrize("name", ["wan480_fine", "wan720_n1"])
+@pytest.mark.parametrize("name", ["wan480_fine", "wan720_n1", "wan480_struct"])
 def test_hash_mask_configs(name):
     torch_or_skip()
     import tile_sparse_attention_amd as T
     w = W.get(name)
     say(f"large {name}: generating inputs")
     q, k, v = W.make_qkv(w)
-    mask = T.maskgen_hash(w.B, w.H, w.L, w.M, w.N, **W.hash_params(w))
+    if w.mask.kind == "structured":
+        mask = T.maskgen_structured(w.B, w.H, w.L, w.M, w.N, **W.structured_params(w))
+    else:
+        mask = T.maskgen_hash(w.B, w.H, w.L, w.M, w.N, **W.hash_params(w))
     say(f"large {name}: attention on GPU")
     o, lse = _attn(w, q.cuda(), k.cuda(), v.cuda(), mask)
     tiles = W.sample_tiles(w)
     heads = _heads(w)
+    if w.mask.kind == "structured":  # one head of every pattern, skipped heads included
+        heads = sorted(set(heads) | {w.mask.patterns.index(t) for t in set(w.mask.patterns)})
     bits_cache = {}
     mnp = mask_to_np(mask)
     for h in heads:

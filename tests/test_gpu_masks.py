@@ -122,3 +122,28 @@ def test_compaction_wan720_n1_sampled_rows():
     assert rp[0] == 0 and np.all(np.diff(rp) >= 0)
     del ci_d
     torch.cuda.empty_cache()
+
+
+def test_structured_maskgen_matches_host():
+    torch_or_skip()
+    import tile_sparse_attention_amd as T
+    for L, M, N in [(1000, 16, 8), (777, 64, 64), (1000, 16, 1), (513, 32, 4)]:
+        pats = (0, 1, 2, 3, 4, 2)
+        w = W.Workload("s", 2, len(pats), L, 64, M, N, "bf16",
+                       W.MaskRecipe("structured", frame_tokens=97, patterns=pats, diag_width=60,
+                                    band_width=7, reach=4, stripe_period=50, stripe_width=9,
+                                    force_diag=False), 1)
+        say(f"structured maskgen L={L} {M}x{N}")
+        m = mask_to_np(T.maskgen_structured(w.B, w.H, w.L, w.M, w.N, **W.structured_params(w)))
+        assert np.array_equal(m, W.mask_bits(w)), (L, M, N)
+
+
+def test_structured_maskgen_full_config_sampled():
+    torch_or_skip()
+    import tile_sparse_attention_amd as T
+    w = W.get("wan480_struct")
+    say("structured maskgen wan480_struct")
+    m = mask_to_np(T.maskgen_structured(w.B, w.H, w.L, w.M, w.N, **W.structured_params(w)))
+    rng = np.random.default_rng(3)
+    rows = [(0, h, i) for h in range(w.H) for i in {0, w.T_q - 1, int(rng.integers(w.T_q))}]
+    assert np.array_equal(_rows_of(m, rows), W.pack_bits(W.mask_rows_bool(w, rows)))

@@ -132,3 +132,57 @@ def test_generation_is_deterministic(name):
     else:
         a, b = W.mask_bits(w), W.mask_bits(w)
     assert np.array_equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# Structured patterns: the tile-level closed forms of the host generator
+# against the token-level rules by brute force (a tile is kept iff its rule
+# holds for some query/key token pair inside it).
+# --------------------------------------------------------------------------
+def _brute_structured(L, M, N, pat, dw, bw, F, reach, P, sw):
+    q = np.arange(L)[:, None]
+    k = np.arange(L)[None, :]
+    if pat == W.gen.PATTERN_EMPTY:
+        tok = np.zeros((L, L), dtype=bool)
+    elif pat == W.gen.PATTERN_DENSE:
+        tok = np.ones((L, L), dtype=bool)
+    elif pat == W.gen.PATTERN_DIAGONAL:
+        tok = np.abs(q - k) <= dw
+    elif pat == W.gen.PATTERN_MULTI_DIAGONAL:
+        tok = np.zeros((L, L), dtype=bool)
+        for t in range(-reach, reach + 1):
+            tok |= np.abs(q - k - t * F) <= bw
+    else:
+        tok = np.broadcast_to((k % P) < sw, (L, L))
+    T_q, T_k = -(-L // M), -(-L // N)
+    out = np.zeros((T_q, T_k), dtype=bool)
+    for i in range(T_q):
+        for j in range(T_k):
+            out[i, j] = tok[i * M:(i + 1) * M, j * N:(j + 1) * N].any()
+    return out
+
+
+@pytest.mark.parametrize("L,M,N", [(97, 16, 1), (200, 16, 8), (257, 32, 4), (300, 64, 64), (130, 16, 16)])
+def test_structured_masks_match_token_rules(L, M, N):
+    dw, bw, F, reach, P, sw = 13, 3, 40, 3, 24, 5
+    pats = (0, 1, 2, 3, 4)
+    w = W.Workload("s", 1, len(pats), L, 64, M, N, "bf16",
+                   W.MaskRecipe("structured", frame_tokens=F, patterns=pats, diag_width=dw,
+                                band_width=bw, reach=reach, stripe_period=P, stripe_width=sw,
+                                force_diag=False), 1)
+    for h, pat in enumerate(pats):
+        rows = np.stack([np.zeros(w.T_q, int), np.full(w.T_q, h), np.arange(w.T_q)], 1)
+        got = W.mask_rows_bool(w, rows)
+        ref = _brute_structured(L, M, N, pat, dw, bw, F, reach, P, sw)
+        assert np.array_equal(got, ref), (L, M, N, pat)
+
+
+def test_struct_workload_densities():
+    w = W.get("wan480_struct")
+    assert w.mask.patterns.count(W.gen.PATTERN_EMPTY) == 2
+    dens = {}
+    for h in (0, 5, 20, 35):
+        rows = np.stack([np.zeros(w.T_q, int), np.full(w.T_q, h), np.arange(w.T_q)], 1)
+        dens[h] = W.mask_rows_bool(w, rows).mean()
+    assert dens[0] == 0.0
+    assert 0.25 < dens[5] < 0.31 and 0.15 < dens[20] < 0.20 and 0.24 < dens[35] < 0.27

@@ -40,6 +40,15 @@ class MaskgenParams(ctypes.Structure):
                 ("frame_radius", ctypes.c_int32), ("force_diag", ctypes.c_int32)]
 
 
+class StructuredParams(ctypes.Structure):
+    _fields_ = [("diag_width", ctypes.c_int32), ("band_width", ctypes.c_int32),
+                ("frame_tokens", ctypes.c_int32),
+                ("reach", ctypes.c_int32), ("stripe_period", ctypes.c_int32),
+                ("stripe_width", ctypes.c_int32)]
+
+
+PATTERN_EMPTY, PATTERN_DIAGONAL, PATTERN_MULTI_DIAGONAL, PATTERN_VERTICAL_STRIPE, PATTERN_DENSE = range(5)
+
 _VP = ctypes.c_void_p
 _PP = ctypes.POINTER(Problem)
 _SIGS = {
@@ -52,6 +61,8 @@ _SIGS = {
     "tsa_predict_mask": (ctypes.c_int, [_PP, _VP, _VP, ctypes.c_int32, _VP, _VP, ctypes.c_size_t,
                                         _VP]),
     "tsa_maskgen_hash": (ctypes.c_int, [_PP, ctypes.POINTER(MaskgenParams), _VP, _VP]),
+    "tsa_maskgen_structured": (ctypes.c_int, [_PP, ctypes.POINTER(StructuredParams),
+                                              ctypes.POINTER(ctypes.c_int32), _VP, _VP]),
     "tsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tsa_last_error": (ctypes.c_char_p, []),
 }
@@ -218,6 +229,22 @@ def maskgen_hash(B, H, L, M, N, *, state0: int, thr_near: int, thr_far: int,
     g = MaskgenParams(state0 & 0xFFFFFFFFFFFFFFFF, thr_near, thr_far, frame_tokens, frame_radius,
                       1 if force_diag else 0)
     _check(lib().tsa_maskgen_hash(ctypes.byref(pr), ctypes.byref(g), _ptr(out), _stream()))
+    return out
+
+
+def maskgen_structured(B, H, L, M, N, head_patterns, *, diag_width: int = 0, band_width: int = 0,
+                       frame_tokens: int = 0, reach: int = 0, stripe_period: int = 0,
+                       stripe_width: int = 0, device="cuda"):
+    """Structured keep-bitmap (tsa_workload.h): one PATTERN_* per head."""
+    torch = _torch()
+    if len(head_patterns) != H:
+        raise TsaError(ERR_INVALID_ARGUMENT, "one pattern per head")
+    pr = Problem(B, H, L, 0, M, N, DTYPE_BF16)
+    out = torch.empty((B, H, -(-L // M), mask_row_words(L, N)), dtype=torch.int32, device=device)
+    g = StructuredParams(diag_width, band_width, frame_tokens, reach, stripe_period, stripe_width)
+    pats = (ctypes.c_int32 * H)(*[int(x) for x in head_patterns])
+    _check(lib().tsa_maskgen_structured(ctypes.byref(pr), ctypes.byref(g), pats, _ptr(out),
+                                        _stream()))
     return out
 
 

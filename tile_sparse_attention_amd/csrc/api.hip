@@ -21,6 +21,8 @@ hipError_t launch_predict_mask(const tsa_problem_t* p, const void* q, const void
                                int sparsity_percent, uint32_t* mask_out, void* workspace,
                                hipStream_t stream);
 size_t predict_workspace(const tsa_problem_t* p);
+hipError_t launch_maskgen_structured(const tsa_problem_t* p, const tsa_structured_params_t* s,
+                                     const int32_t* head_pattern, uint32_t* out, hipStream_t stream);
 hipError_t launch_maskgen_hash(const tsa_problem_t* p, const tsa_maskgen_params_t* g,
                                uint32_t* out, hipStream_t stream);
 }  // namespace tsa
@@ -181,6 +183,34 @@ tsa_status_t tsa_maskgen_hash(const tsa_problem_t* p, const tsa_maskgen_params_t
   const long long words = n_rows(p) * tsa_mask_row_words(p->L, p->N);
   if ((words + 255) / 256 > kMaxGrid) return fail(TSA_ERR_UNSUPPORTED, "bitmap too large");
   const hipError_t e = tsa::launch_maskgen_hash(p, g, mask_out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mask generator launch");
+  return TSA_OK;
+}
+
+tsa_status_t tsa_maskgen_structured(const tsa_problem_t* p, const tsa_structured_params_t* g,
+                                    const int32_t* head_pattern, uint32_t* mask_out, void* stream) {
+  tsa_status_t s = check_problem(p, false);
+  if (s != TSA_OK) return s;
+  if (!g || !head_pattern || !mask_out)
+    return fail(TSA_ERR_INVALID_ARGUMENT, "params, head_pattern and mask_out must be non-NULL");
+  if (p->H > TSA_MAX_PATTERN_HEADS)
+    return fail(TSA_ERR_UNSUPPORTED, "at most %d heads", TSA_MAX_PATTERN_HEADS);
+  bool multi = false, stripe = false;
+  for (int h = 0; h < p->H; ++h) {
+    const int32_t t = head_pattern[h];
+    if (t < TSA_PATTERN_EMPTY || t > TSA_PATTERN_DENSE)
+      return fail(TSA_ERR_INVALID_ARGUMENT, "head %d: unknown pattern %d", h, (int)t);
+    multi = multi || t == TSA_PATTERN_MULTI_DIAGONAL;
+    stripe = stripe || t == TSA_PATTERN_VERTICAL_STRIPE;
+  }
+  if (g->diag_width < 0 || g->band_width < 0 ||
+      (multi && (g->frame_tokens <= 0 || g->reach < 0 || g->reach > 64)) ||
+      (stripe && (g->stripe_period <= 0 || g->stripe_width < 0 || g->stripe_width > g->stripe_period)))
+    return fail(TSA_ERR_INVALID_ARGUMENT, "bad structured-mask parameters");
+  const long long words = n_rows(p) * tsa_mask_row_words(p->L, p->N);
+  if ((words + 255) / 256 > kMaxGrid) return fail(TSA_ERR_UNSUPPORTED, "bitmap too large");
+  const hipError_t e = tsa::launch_maskgen_structured(p, g, head_pattern, mask_out,
+                                                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mask generator launch");
   return TSA_OK;
 }

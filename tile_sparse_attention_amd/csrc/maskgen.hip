@@ -59,4 +59,72 @@ hipError_t launch_maskgen_hash(const tsa_problem_t* p, const tsa_maskgen_params_
   return hipGetLastError();
 }
 
+// Structured patterns (tsa_workload.h): one thread per output word, closed
+// forms per tile.
+struct StructuredArgs {
+  tsa_structured_params_t s;
+  int8_t pattern[TSA_MAX_PATTERN_HEADS];
+};
+
+__device__ __forceinline__ bool ranges_meet(long long a0, long long a1, long long b0, long long b1) {
+  return a0 <= b1 && b0 <= a1;  // inclusive ranges
+}
+
+__global__ __launch_bounds__(256) void maskgen_structured_kernel(uint32_t* __restrict__ out,
+                                                                 long long total_words, int H, int L,
+                                                                 int M, int N, int T_q, int T_k,
+                                                                 int words, StructuredArgs g) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total_words) return;
+  const int w = (int)(idx % words);
+  const long long row = idx / words;  // (b*H + h)*T_q + i
+  const int i = (int)(row % T_q);
+  const int h = (int)((row / T_q) % H);
+  const int pat = g.pattern[h];
+  const long long q0 = (long long)i * M;
+  const long long q1 = (q0 + M < L ? q0 + M : L) - 1;
+  uint32_t bits = 0;
+  for (int t = 0; t < 32; ++t) {
+    const int j = 32 * w + t;
+    if (j >= T_k) break;
+    const long long k0 = (long long)j * N;
+    const long long k1 = (k0 + N < L ? k0 + N : L) - 1;
+    bool keep = false;
+    if (pat == TSA_PATTERN_DENSE) {
+      keep = true;
+    } else if (pat == TSA_PATTERN_DIAGONAL) {
+      // some k in [k0, k1] within width of some q in [q0, q1]
+      keep = ranges_meet(k0, k1, q0 - g.s.diag_width, q1 + g.s.diag_width);
+    } else if (pat == TSA_PATTERN_MULTI_DIAGONAL) {
+      for (int d = -g.s.reach; d <= g.s.reach && !keep; ++d) {
+        const long long sft = (long long)d * g.s.frame_tokens;
+        keep = ranges_meet(k0, k1, q0 + sft - g.s.band_width, q1 + sft + g.s.band_width);
+      }
+    } else if (pat == TSA_PATTERN_VERTICAL_STRIPE) {
+      const long long P = g.s.stripe_period;
+      if (g.s.stripe_width > 0) {
+        const long long r = k0 % P;  // first stripe key at or after k0
+        const long long first = r < g.s.stripe_width ? k0 : k0 + (P - r);
+        keep = first <= k1;
+      }
+    }
+    bits |= (uint32_t)keep << t;
+  }
+  out[idx] = bits;
+}
+
+hipError_t launch_maskgen_structured(const tsa_problem_t* p, const tsa_structured_params_t* s,
+                                     const int32_t* head_pattern, uint32_t* out, hipStream_t stream) {
+  const int T_q = (p->L + p->M - 1) / p->M;
+  const int T_k = (p->L + p->N - 1) / p->N;
+  const int words = (T_k + 31) / 32;
+  const long long total = (long long)p->B * p->H * T_q * words;
+  StructuredArgs g;
+  g.s = *s;
+  for (int h = 0; h < TSA_MAX_PATTERN_HEADS; ++h) g.pattern[h] = h < p->H ? (int8_t)head_pattern[h] : 0;
+  hipLaunchKernelGGL(maskgen_structured_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     stream, out, total, p->H, p->L, p->M, p->N, T_q, T_k, words, g);
+  return hipGetLastError();
+}
+
 }  // namespace tsa

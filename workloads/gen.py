@@ -62,7 +62,7 @@ def prob_threshold(p: float) -> int:
 # --------------------------------------------------------------------------
 @dataclass(frozen=True)
 class MaskRecipe:
-    kind: str                     # "hash" | "exact_drop" | "predicted" | "ones" | "diag_only"
+    kind: str                     # "hash" | "exact_drop" | "predicted" | "ones" | "diag_only" | "structured"
     p_near: float = 0.0           # hash: keep probability near the query frame (or everywhere)
     p_far: float = 0.0            # hash: keep probability outside the frame window
     frame_tokens: int = 0         # hash: tokens per latent frame (0: no frame structure)
@@ -70,6 +70,14 @@ class MaskRecipe:
     drop_fraction: float = 0.0    # exact_drop
     sparsity_percent: int = 0     # predicted
     force_diag: bool = True
+    # structured: one pattern per head (PATTERN_* codes of tsa_workload.h);
+    # frame_tokens is the multi-diagonal spacing
+    patterns: tuple = ()
+    diag_width: int = 0
+    band_width: int = 0
+    reach: int = 0
+    stripe_period: int = 0
+    stripe_width: int = 0
 
 
 @dataclass(frozen=True)
@@ -180,6 +188,20 @@ _add(Workload("hunyuan720", 1, 24, 118800, 128, 16, 16, "bf16",
               description="HunyuanVideo 720p 129f shape (33 x 45x80 tokens), 16x16 tiles, mask "
                           "predicted from pooled Q . pooled K at the per-row 85th percentile"))
 
+# Wan 2.1 480p shape with per-head structured patterns: 2 of 40 heads skipped
+# (the abstract's 3-6% range), the rest diagonal (width 0.15 L), multi-diagonal
+# (width 128 tokens, repeated every 1560-token latent frame over +-20 frames)
+# and vertical stripes (390 of every 1560 keys).
+_STRUCT_PATTERNS = tuple([0, 0] + [1] * 12 + [2] * 13 + [3] * 13)
+_add(Workload("wan480_struct", 1, 40, 32760, 128, 16, 8, "bf16",
+              MaskRecipe("structured", frame_tokens=1560, patterns=_STRUCT_PATTERNS, diag_width=4914,
+                         band_width=128, reach=20, stripe_period=1560, stripe_width=390,
+                         force_diag=False),
+              BASE_SEED + 6,
+              description="Wan 2.1 480p shape, 16x8 tiles, per-head structured masks: 2 heads "
+                          "skipped, 12 diagonal (|q-k| <= 4914), 13 multi-diagonal (|q-k-1560t| <= "
+                          "128, |t| <= 20), 13 vertical-stripe (k mod 1560 < 390)"))
+
 HEADLINE = "wan480_fine"
 
 
@@ -235,6 +257,48 @@ def _hash_rows(w: Workload, rows: np.ndarray) -> np.ndarray:
     return out
 
 
+# Structured patterns (tsa_workload.h), per head: the diagonal, multi-diagonal
+# and vertical-stripe structures and skipped heads that the Sparse-vDiT
+# abstract names.  A tile is kept iff its rule holds for some (query, key)
+# token pair inside it.
+PATTERN_EMPTY, PATTERN_DIAGONAL, PATTERN_MULTI_DIAGONAL, PATTERN_VERTICAL_STRIPE, PATTERN_DENSE = range(5)
+
+
+def _structured_rows(w: Workload, rows: np.ndarray) -> np.ndarray:
+    m = w.mask
+    j = np.arange(w.T_k, dtype=np.int64)
+    k0 = j * w.N
+    k1 = np.minimum(k0 + w.N, w.L) - 1
+    out = np.zeros((len(rows), w.T_k), dtype=bool)
+    for r, (_, h, i) in enumerate(rows):
+        pat = m.patterns[int(h)]
+        q0 = int(i) * w.M
+        q1 = min(q0 + w.M, w.L) - 1
+        if pat == PATTERN_DENSE:
+            out[r] = True
+        elif pat == PATTERN_DIAGONAL:
+            out[r] = (k0 <= q1 + m.diag_width) & (k1 >= q0 - m.diag_width)
+        elif pat == PATTERN_MULTI_DIAGONAL:
+            for t in range(-m.reach, m.reach + 1):
+                sft = t * m.frame_tokens
+                out[r] |= (k0 <= q1 + sft + m.band_width) & (k1 >= q0 + sft - m.band_width)
+        elif pat == PATTERN_VERTICAL_STRIPE and m.stripe_width > 0:
+            rem = k0 % m.stripe_period
+            first = np.where(rem < m.stripe_width, k0, k0 + (m.stripe_period - rem))
+            out[r] = first <= k1
+    return out
+
+
+def structured_params(w: Workload) -> dict:
+    """Arguments of the GPU structured-mask generator for this workload."""
+    m = w.mask
+    if m.kind != "structured":
+        raise ValueError(f"mask recipe {m.kind!r} is not structured")
+    return dict(head_patterns=list(m.patterns), diag_width=m.diag_width, band_width=m.band_width,
+                frame_tokens=m.frame_tokens, reach=m.reach, stripe_period=m.stripe_period,
+                stripe_width=m.stripe_width)
+
+
 def hash_params(w: Workload) -> dict:
     """Parameters of the counter-based mask recipe, as the GPU generator takes them."""
     m = w.mask
@@ -248,11 +312,13 @@ def hash_params(w: Workload) -> dict:
 
 def mask_rows_bool(w: Workload, rows) -> np.ndarray:
     """Keep bits (bool [n, T_k]) of the given (b, h, i) rows, for recipes that
-    can be evaluated row by row (hash, ones, diag_only)."""
+    can be evaluated row by row (hash, structured, ones, diag_only)."""
     rows = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
     k = w.mask.kind
     if k == "hash":
         return _hash_rows(w, rows)
+    if k == "structured":
+        return _structured_rows(w, rows)
     if k == "ones":
         return np.ones((len(rows), w.T_k), dtype=bool)
     if k == "diag_only":
