@@ -77,6 +77,16 @@ def test_bf16_structured_masks_and_skipped_heads(M, N):
     full_compare(w, W.mask_bits(w), f"bf16 structured {M}x{N} L={L}")
 
 
+def test_bf16_one_skipped_head_among_dense_heads():
+    torch_or_skip()
+    # One head with an all-zero mask among heads whose work-groups need every
+    # chunk: only that head's work-groups take the chunk-skipping kernel.
+    w = small_workload("one_empty", 3000, 128, 16, 8, H=8, p=0.5, seed=9)
+    bits = W.mask_bits(w)
+    bits[0, 3] = 0
+    full_compare(w, bits, "bf16 16x8 L=3000, head 3 skipped")
+
+
 @pytest.mark.parametrize("dtype,d,N", [("f32", 128, 8), ("f32", 64, 1), ("f32", 64, 4),
                                        ("bf16", 64, 8), ("bf16", 64, 1), ("f32", 128, 64)])
 def test_dtype_and_head_dim(dtype, d, N):

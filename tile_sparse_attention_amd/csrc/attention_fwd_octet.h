@@ -339,8 +339,11 @@ struct OctKernel {
     // work-groups would gain from it: the skipping kernel runs after the
     // plain one, so a few flagged work-groups would run alone at the end.
     if (p.need_flag != nullptr) {
+      // (flag 2: the work-group needs no chunk at all, e.g. a skipped head;
+      // the skipping kernel writes its zero rows without staging anything)
       const bool many = (long long)wave_uniform((int)*p.need_count) * 4 >= (long long)gridDim.x;
-      const bool mine = many && wave_uniform((int)p.need_flag[lb]) != 0;
+      const int f = wave_uniform((int)p.need_flag[lb]);
+      const bool mine = f == 2 || (many && f == 1);
       if (mine != SKIP) return;
     } else if (SKIP) {
       return;
@@ -487,9 +490,9 @@ __global__ __launch_bounds__(1024) void attn_oct_kernel(AttnParams p) {
 // One work-group per attention work-group (logical numbering): ORs the mask
 // rows of its 256 query rows word by word, marks the 128-key chunks with a
 // kept tile in a bitmap (need, kNeedWords words per work-group) and flags
-// the work-group when fewer than 7/8 of the chunks are needed (counted in
-// `count`, zeroed beforehand).  Mask padding bits past T_k can only mark the
-// last chunk.
+// the work-group when fewer than 7/8 of the chunks are needed (flag 1, or 2
+// when none is; counted in `count`, zeroed beforehand).  Mask padding bits
+// past T_k can only mark the last chunk.
 template <typename T>
 __global__ __launch_bounds__(64) void zero_word_kernel(T* w) {
   if (threadIdx.x == 0) *w = T(0);
@@ -532,7 +535,7 @@ __global__ __launch_bounds__(256) void chunk_need_kernel(AttnParams p, uint32_t*
   __syncthreads();
   if (tid == 0) {
     const bool f = cnt * 8 < n_chunks * 7;
-    flag[g] = f ? 1u : 0u;
+    flag[g] = cnt == 0 ? 2u : f ? 1u : 0u;
     if (f) atomicAdd(count, 1u);
   }
 }
