@@ -23,14 +23,18 @@ METRIC = "kept-tile effective TFLOPS (% bf16 MFMA peak) + ms/call at 70% sparsit
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}     # MI355X dense matrix-core peaks
 KERNEL_SOURCES = ("tile_sparse_attention_amd/csrc/attention_fwd_impl.h",
                   "tile_sparse_attention_amd/csrc/attention_fwd_octet.h",
+                  "tile_sparse_attention_amd/csrc/attention_fwd_keys.h",
                   "tile_sparse_attention_amd/csrc/attention_fwd_inst.h",
+                  "tile_sparse_attention_amd/csrc/launch.h",
                   "tile_sparse_attention_amd/csrc/tsa_device.h",
                   "tile_sparse_attention_amd/build.py")
 
 
 def kernel_name(w) -> str:
     """The attention kernel the library launches for this workload."""
-    return "attn_oct_kernel" if w.dtype == "bf16" and w.N >= 8 else "attn_fwd_kernel"
+    if w.dtype != "bf16":
+        return "attn_fwd_kernel"
+    return "attn_oct_kernel" if w.N >= 8 else "attn_key_kernel"
 
 
 def log(msg):
@@ -164,8 +168,8 @@ def main():
                          "byte counters of a profiler run) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(every (batch, head) is independent; see the sharding note in DESIGN.md)",
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(every (batch, head) is independent, so a caller shards by heads)",
               file=sys.stderr)
         sys.exit(2)
 

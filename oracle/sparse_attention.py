@@ -9,7 +9,7 @@ a tile whose mask bit is 0 has its scores skipped.  Skipped scores take no
 part in the softmax, which is the same as setting them to -inf.  Then
 P = softmax(S) row by row and O = P V.
 
-Readings where the page is silent (each listed in the design doc):
+Readings where the page is silent:
   * bit = 1 keeps a tile; bitmap words are uint32, LSB first, row-major
     [B][H][T_q][words]; padding bits past T_k are ignored.
   * the last query / key tile may be partial; rows and keys past L do not exist.
