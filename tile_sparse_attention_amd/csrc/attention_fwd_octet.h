@@ -18,8 +18,8 @@
 //     global-to-LDS loads issued by all waves; each chunk crosses from L2
 //     once per 256 query rows.
 //   * Per chunk a wave turns the mask bits of its row into the ascending list
-//     of kept octets with one ballot and one lane permutation (lane i of the
-//     list register holds the i-th kept octet).  A pass takes list entries
+//     of kept octets, one nibble per entry in a 64-bit scalar register, with
+//     two lookups in a byte-to-nibble-list table.  A pass takes list entries
 //     4p..4p+3; a list shorter than a multiple of four is padded with the
 //     first kept octet (real kept scores, so the running max only sees real
 //     kept scores), whose probabilities the pass sets to zero.
@@ -78,6 +78,46 @@ struct OctCfg {
   static_assert(D % 32 == 0, "head dim");
   static_assert(TPC <= 16, "tile bits of a chunk fit one mask word");
 };
+
+// Entry b (0..255): the set bits of byte b in ascending order, one nibble
+// each; entry 256 + b: the same list with 8 added to every entry, for the
+// upper byte of a 16-octet mask.
+struct OctetNibbleTable {
+  uint32_t v[512];
+};
+constexpr OctetNibbleTable make_octet_nibbles() {
+  OctetNibbleTable t{};
+  for (int half = 0; half < 2; ++half)
+    for (int b = 0; b < 256; ++b) {
+      uint32_t x = 0u;
+      int j = 0;
+      for (int i = 0; i < 8; ++i)
+        if ((b >> i) & 1) x |= (uint32_t)(i + 8 * half) << (4 * j++);
+      t.v[256 * half + b] = x;
+    }
+  return t;
+}
+static __constant__ OctetNibbleTable kOctetNibbles = make_octet_nibbles();
+
+// Octet mask of a chunk from its tile bits (2^LOG2R octets per tile): bit t
+// of tb becomes bits t*R .. t*R+R-1 (R = 2^LOG2R).
+template <int LOG2R>
+__device__ __forceinline__ uint32_t octet_mask(uint32_t tb) {
+  if constexpr (LOG2R == 0) {
+    return tb;
+  } else if constexpr (LOG2R == 1) {
+    uint32_t x = (tb | (tb << 4)) & 0x0F0Fu;
+    x = (x | (x << 2)) & 0x3333u;
+    x = (x | (x << 1)) & 0x5555u;
+    return x | (x << 1);
+  } else if constexpr (LOG2R == 2) {
+    uint32_t x = (tb | (tb << 6)) & 0x0303u;
+    x = (x | (x << 3)) & 0x1111u;
+    return x * 15u;
+  } else {
+    return ((tb & 1u) | ((tb & 2u) << 7)) * 255u;
+  }
+}
 
 // SKIP: the work-group visits only the chunks its bitmap marks as needed
 // (work-groups flagged by chunk_need_kernel); otherwise every chunk (the
@@ -276,53 +316,48 @@ struct OctKernel {
     oacc[C::NDB] = Mma<bf16_t>::mac8(ones, bop, oacc[C::NDB]);
   }
 
-  // kept-octet list of one chunk, packed for the passes: lane p of w holds
-  // list entries 4p..4p+3, one byte each
+  // kept-octet list of one chunk as a wave-uniform value: entry j (an octet
+  // index of the chunk) in bits 4j..4j+3
   struct List {
-    uint32_t w;
+    uint64_t w;
     int count;
   };
 
-  // Kept octets of chunk c as a lane-indexed list (ascending), padded after
-  // the `count` kept entries with the first kept octet (real kept scores,
-  // whose probabilities the pass zeroes).  Only the mask word is read, so a
-  // chunk's list is built before the chunk's barrier, while other waves
-  // still compute.
+  // Kept octets of chunk c (ascending), padded after the `count` kept
+  // entries with the first kept octet (real kept scores, whose probabilities
+  // the pass zeroes).  A few scalar instructions and two lookups in a small
+  // constant table: no loop, no LDS round trip, and little load on the
+  // scalar unit that all waves of a compute unit share.
   __device__ __forceinline__ List make_list(int c, uint32_t mword) const {
-    List li;
-    li.w = 0u;
-    const int kbase = c * C::KC;
+    List li{0ull, 0};
     uint32_t tb = uniform_u32(mword) >> ((c * C::TPC) & 31);
     if constexpr (C::TPC < 32) tb &= (1u << C::TPC) - 1u;
-    const int left = L - kbase;                       // keys of this chunk that exist
+    const int left = L - c * C::KC;                   // keys of this chunk that exist
     const int nval = left >= C::KC ? C::OPC : (left + 7) >> 3;
-    const bool keep = lane < nval && ((tb >> ((lane & (C::OPC - 1)) >> C::LOG2R)) & 1u);
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
-    li.count = __builtin_popcountll(bal);
-    if (bal == 0ull) return li;
-    const int below = (int)prefix_count64(bal);
-    const int tgt = keep ? below : li.count + (lane - below);
-    const int lst = __builtin_amdgcn_ds_permute(tgt * 4, lane);
-    const int first = __builtin_ctzll(bal);
-    const int lq = lane < li.count ? lst : first;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      li.w |= (uint32_t)__builtin_amdgcn_ds_bpermute(((4 * lane + k) & 63) * 4, lq) << (8 * k);
+    const uint32_t m = octet_mask<C::LOG2R>(tb) & ((1u << nval) - 1u);
+    const uint32_t lo = m & 255u, hi = m >> 8;
+    const int clo = __builtin_popcount(lo);
+    li.count = clo + __builtin_popcount(hi);
+    uint64_t w = (uint64_t)kOctetNibbles.v[lo] | ((uint64_t)kOctetNibbles.v[256 + hi] << (4 * clo));
+    if (li.count != 0 && li.count < 16) w |= (0x1111111111111111ull * (w & 15u)) << (4 * li.count);
+    li.w = w;
     return li;
   }
 
-  // The passes of one chunk (lim: keys of the chunk that exist): a pass
-  // reads its packed word as a wave-uniform value and every lane extracts
-  // the bytes it needs, which keeps the per-pass list lookups off the LDS.
+  // The passes of one chunk (lim: keys of the chunk that exist): each pass
+  // takes the next four list entries as a wave-uniform 16-bit value and every
+  // lane extracts the entries it needs.
   __device__ __forceinline__ void run_list(int buf, const List& li, int lim) {
-    const uint32_t shq = 8u * (uint32_t)(n >> 3), shv = 8u * (uint32_t)(g >> 1);
+    const uint32_t shq = 4u * (uint32_t)(n >> 3), shv = 4u * (uint32_t)(g >> 1);
     const uint32_t kb = lds_addr(sm.k[buf]) + (uint32_t)((n & 7) * C::KRS + 16 * g);
+    uint64_t rest = li.w;
     for (int q0 = 0; q0 < li.count; q0 += 4) {
-      const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)li.w, q0 >> 2);
-      const uint32_t ka0 = mad_u24(__builtin_amdgcn_ubfe(w, shq, 8), 8u * C::KRS, kb);
-      const uint32_t ka1 = mad_u24(__builtin_amdgcn_ubfe(w, shq + 16u, 8), 8u * C::KRS, kb);
-      const int ovx = (int)__builtin_amdgcn_ubfe(w, shv, 8);
-      const int ovy = (int)__builtin_amdgcn_ubfe(w, shv + 16u, 8);
+      const uint32_t w = (uint32_t)rest & 0xffffu;
+      rest >>= 16;
+      const uint32_t ka0 = mad_u24(__builtin_amdgcn_ubfe(w, shq, 4), 8u * C::KRS, kb);
+      const uint32_t ka1 = mad_u24(__builtin_amdgcn_ubfe(w, shq + 8u, 4), 8u * C::KRS, kb);
+      const int ovx = (int)__builtin_amdgcn_ubfe(w, shv, 4);
+      const int ovy = (int)__builtin_amdgcn_ubfe(w, shv + 8u, 4);
       pass(buf, ka0, ka1, ovx, ovy, li.count - q0, lim);
     }
   }
@@ -418,7 +453,7 @@ struct OctKernel {
       };
       int k = 0;
       int c = chunk_at(0);
-      List cur = {0u, 0};
+      List cur = {0ull, 0};
       if (c < n_chunks) {
         const uint32_t m0 = issue_chunk(c, 0);
         __builtin_amdgcn_s_waitcnt(0);
@@ -443,7 +478,7 @@ struct OctKernel {
     } else {
       const uint32_t m0 = issue_chunk(0, 0);
       __builtin_amdgcn_s_waitcnt(0);
-      List cur = {0u, 0};
+      List cur = {0ull, 0};
       if (act) cur = make_list(0, m0);
       __syncthreads();
       for (int c = 0; c < n_chunks; ++c) {
