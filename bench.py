@@ -6,6 +6,9 @@ the Wan 2.1 480p shape with 16x8 tiles at 70% frame-structured sparsity,
 inputs resident in HBM.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+With --backward it times the backward pass (tsa_attention_bwd) of the same
+workload instead and prints that line.
 """
 from __future__ import annotations
 
@@ -155,6 +158,65 @@ def traffic_for(workload: str, sha: str):
     return rec.get("bytes_per_launch")
 
 
+BWD_METRIC = ("backward kept-tile effective TFLOPS (dQ, dK, dV; 5 GEMMs per kept tile = 2.5x the "
+              "forward's kept FLOPs)")
+BWD_SOURCES = ("tile_sparse_attention_amd/csrc/attention_bwd.h", "tile_sparse_attention_amd/csrc/attention_bwd.hip")
+
+
+def bench_backward(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws):
+    """One step = one tsa_attention_bwd call (LSE/D preparation, the dK/dV kernel
+    and the dQ kernel) on the workload, given the forward's O and LSE."""
+    import torch
+
+    import tile_sparse_attention_amd as T
+    import workloads as W
+    if w.dtype != "bf16":
+        raise SystemExit("the backward is bf16 only")
+    do = W.make_do(w).cuda()
+    o, lse = T.attention_fwd(qd, kd, vd, mask, w.M, w.N, w.scale, out=out, return_lse=True, workspace=ws)
+    pr = T.problem(w.B, w.H, w.L, w.d, w.M, w.N, T.DTYPE_BF16)
+    wsb = torch.empty(T.workspace_size(T.OP_ATTENTION_BWD, pr), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        T.attention_bwd(qd, kd, vd, o, do, lse, mask, w.M, w.N, w.scale, workspace=wsb)
+
+    ms_step, ms_kernel, ms_min = time_calls(step, args.steps, args.warmup)
+    fb = 2.5 * flops
+    tflops = fb / (ms_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["bf16"]
+    log(f"backward: {ms_step:.3f} ms/step, call mean {ms_kernel:.3f} ms (min {ms_min:.3f}), "
+        f"{tflops:.1f} TFLOP/s")
+    cfg = {"workload": name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "M": w.M, "N": w.N,
+           "mask": w.description, "kept_fraction": round(flops / dense_flops, 6),
+           "backward_flops": int(fb), "pct_of_peak": round(100 * tflops / peak, 2), "peak_tflops": peak}
+    if not args.no_dense:
+        ones = torch.full_like(mask, -1)
+        o2, l2 = T.attention_fwd(qd, kd, vd, ones, w.M, w.N, w.scale, return_lse=True, workspace=ws)
+
+        def dense_step():
+            T.attention_bwd(qd, kd, vd, o2, do, l2, ones, w.M, w.N, w.scale, workspace=wsb)
+        d_step, _, _ = time_calls(dense_step, max(3, args.steps // 4), 1)
+        cfg["all_ones_ms"] = round(d_step, 4)
+        cfg["all_ones_tflops"] = round(2.5 * dense_flops / (d_step * 1e-3) / 1e12, 2)
+        cfg["speedup_vs_all_ones"] = round(d_step / ms_step, 3)
+        log(f"all-ones backward: {d_step:.3f} ms/step ({cfg['all_ones_tflops']} TFLOP/s), "
+            f"sparse speedup {cfg['speedup_vs_all_ones']}x")
+    h = hashlib.sha256()
+    for p in BWD_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    achieved = fb / (ms_kernel * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None,
+            "kernel": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel", "kernel_sha": h.hexdigest()[:16]}
+    rec = {"metric": BWD_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded normal Q/K/V/dO, generated masks)", "config": cfg, "roofline": roof}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +225,9 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (dQ, dK, dV) of the workload instead and print "
+                         "its own JSON line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run one plain device copy of BYTES bytes (calibrates the HBM "
                          "byte counters of a profiler run) and exit")
@@ -203,6 +268,10 @@ def main():
     flops = kept_flops_device(w, mask)
     dense_flops = 4 * w.B * w.H * w.L * w.L * w.d
     log(f"kept FLOPs {flops:.4e} ({flops / dense_flops:.4f} of dense)")
+
+    if args.backward:
+        bench_backward(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws)
+        return
 
     def step():
         T.attention_fwd(qd, kd, vd, mask, w.M, w.N, w.scale, out=out, workspace=ws)

@@ -1,5 +1,5 @@
 /*
- * tsa.h - fine-grained tile-sparse softmax attention (forward) for AMD MI355X (gfx950).
+ * tsa.h - fine-grained tile-sparse softmax attention (forward and backward) for AMD MI355X (gfx950).
  *
  * The operation is the one described in the abstract of "FG-Attn: Leveraging
  * Fine-Grained Sparse Attention in Video Diffusion Models" (section Abstract):
@@ -53,7 +53,8 @@ typedef enum { TSA_DTYPE_F32 = 0, TSA_DTYPE_BF16 = 1 } tsa_dtype_t;
 typedef enum {
   TSA_OP_ATTENTION_FWD = 0,
   TSA_OP_MASK_COMPACT = 1,
-  TSA_OP_PREDICT_MASK = 2
+  TSA_OP_PREDICT_MASK = 2,
+  TSA_OP_ATTENTION_BWD = 3
 } tsa_op_t;
 
 /* Problem shape: batch B, heads H, sequence length L, head dim d, tile M x N. */
@@ -90,6 +91,30 @@ tsa_status_t tsa_attention_fwd(const tsa_problem_t* p,
                                const void* q, const void* k, const void* v,
                                const uint32_t* mask_bits, float scale,
                                void* o, float* lse,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Gradients of tsa_attention_fwd's output with respect to q, k and v, for an
+ * upstream gradient d_o.  The pages define only the forward (FG-Attn abstract:
+ * skipped M x N tiles excluded from the softmax); this is its derivative by the
+ * chain rule, with P the forward's kept-score softmax and
+ * D[r] = sum_d d_o[r,d] o[r,d]:
+ *   dv = P^T d_o,  dS = P * (d_o v^T - D),  dq = scale dS k,  dk = scale dS^T q.
+ * Skipped tiles get no work; a query row with no kept key contributes nothing.
+ * q, k, v, o, d_o: [B,H,L,d] bf16 (o is the forward's output).  lse: [B,H,L]
+ * fp32, the forward's log-sum-exp (required; -inf marks a row with no kept
+ * key).  mask_bits and scale: as passed to the forward.  dq, dk, dv: [B,H,L,d]
+ * bf16, written in full, none aliasing an input.  Accumulation is fp32; the
+ * probabilities and dS are rounded to bf16 for the matrix cores.
+ * workspace: tsa_workspace_size(TSA_OP_ATTENTION_BWD) bytes, 256-byte aligned
+ * (B*H*ceil(L/128)*256 floats: per 128-row chunk the rows' LSE*log2(e) and D);
+ * not needed after the call.  Supported: bf16 with the forward's d, M and N;
+ * fp32 returns TSA_ERR_UNSUPPORTED. */
+tsa_status_t tsa_attention_bwd(const tsa_problem_t* p,
+                               const void* q, const void* k, const void* v,
+                               const void* o, const void* d_o, const float* lse,
+                               const uint32_t* mask_bits, float scale,
+                               void* dq, void* dk, void* dv,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
 

@@ -91,6 +91,40 @@ def test_attention_rejects_bad_pointers_and_scale():
     assert _attn(pr) == T.ERR_WORKSPACE_TOO_SMALL            # no workspace given
 
 
+def _bwd(pr, ptrs=None, scale=1.0, ws=(None, 0)):
+    # q k v o do lse mask dq dk dv as fake, distinct, aligned addresses
+    p = dict(q=1, k=2, v=3, o=4, do=5, lse=6, m=7, dq=8, dk=9, dv=10)
+    p.update(ptrs or {})
+    a = {n: ctypes.c_void_p(0x10000 * x) if x else ctypes.c_void_p(0) for n, x in p.items()}
+    return T.lib().tsa_attention_bwd(ctypes.byref(pr), a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"],
+                                     a["m"], ctypes.c_float(scale), a["dq"], a["dk"], a["dv"],
+                                     ws[0], ws[1], None)
+
+
+def test_backward_workspace_and_validation():
+    pr = T.problem(1, 40, 32760, 128, 16, 8)
+    # per (b, h) and 128-row chunk: 128 lse2 and 128 D values (fp32)
+    assert T.workspace_size(T.OP_ATTENTION_BWD, pr) == 40 * 256 * 256 * 4
+    with pytest.raises(T.TsaError) as e:
+        T.workspace_size(T.OP_ATTENTION_BWD, T.problem(1, 2, 512, 64, 16, 16, T.DTYPE_F32))
+    assert e.value.status == T.ERR_UNSUPPORTED
+    small = T.problem(1, 2, 512, 64, 16, 16)
+    assert _bwd(T.problem(1, 2, 512, 64, 16, 16, T.DTYPE_F32)) == T.ERR_UNSUPPORTED
+    assert _bwd(T.problem(1, 2, 512, 96, 16, 16)) == T.ERR_UNSUPPORTED
+    assert _bwd(T.problem(1, 2, 512, 64, 16, 3)) == T.ERR_UNSUPPORTED
+    for name in ("q", "o", "do", "lse", "m", "dq", "dv"):
+        assert _bwd(small, {name: 0}) == T.ERR_INVALID_ARGUMENT, name
+    assert _bwd(small, {"dq": 1}) == T.ERR_INVALID_ARGUMENT          # dq aliases q
+    assert _bwd(small, {"dk": 8}) == T.ERR_INVALID_ARGUMENT          # dk aliases dq
+    assert _bwd(small, scale=float("nan")) == T.ERR_INVALID_ARGUMENT
+    # every call above and below fails validation, so nothing is launched
+    assert _bwd(small) == T.ERR_WORKSPACE_TOO_SMALL                 # no workspace given
+    need = T.workspace_size(T.OP_ATTENTION_BWD, small)
+    assert need == 2 * 4 * 256 * 4
+    assert _bwd(small, ws=(ctypes.c_void_p(0x900000), need - 4)) == T.ERR_WORKSPACE_TOO_SMALL
+    assert _bwd(small, ws=(ctypes.c_void_p(0x900010), need)) == T.ERR_WORKSPACE_TOO_SMALL  # misaligned
+
+
 def test_compact_and_predict_validation():
     lib = T.lib()
     pr = T.problem(1, 2, 512, 64, 16, 16)

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libtsa.so")
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
 DTYPE_F32, DTYPE_BF16 = 0, 1
-OP_ATTENTION_FWD, OP_MASK_COMPACT, OP_PREDICT_MASK = 0, 1, 2
+OP_ATTENTION_FWD, OP_MASK_COMPACT, OP_PREDICT_MASK, OP_ATTENTION_BWD = 0, 1, 2, 3
 
 
 class TsaError(RuntimeError):
@@ -56,6 +56,8 @@ _SIGS = {
     "tsa_workspace_size": (ctypes.c_int, [ctypes.c_int, _PP, ctypes.POINTER(ctypes.c_size_t)]),
     "tsa_attention_fwd": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP, _VP,
                                          ctypes.c_size_t, _VP]),
+    "tsa_attention_bwd": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_float,
+                                         _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     "tsa_mask_compact": (ctypes.c_int, [_PP, _VP, _VP, _VP, ctypes.c_int64, _VP, ctypes.c_size_t,
                                         _VP]),
     "tsa_predict_mask": (ctypes.c_int, [_PP, _VP, _VP, ctypes.c_int32, _VP, _VP, ctypes.c_size_t,
@@ -174,6 +176,41 @@ def attention_fwd(q, k, v, mask_bits, M: int, N: int, scale: float | None = None
                                    ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(ws), nws,
                                    _stream()))
     return (out, lse) if return_lse else out
+
+
+def attention_bwd(q, k, v, o, do, lse, mask_bits, M: int, N: int, scale: float | None = None, *,
+                  workspace=None):
+    """(dQ, dK, dV) of tile-sparse attention for the upstream gradient `do`.
+
+    q, k, v, o, do: bf16 [B, H, L, d] (o and lse as the forward returned them
+    with return_lse=True).  `workspace` (uint8 GPU tensor of at least
+    workspace_size(OP_ATTENTION_BWD) bytes) is allocated per call when not given.
+    """
+    torch = _torch()
+    B, H, L, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _need_cuda(q, k, v, o, do, lse, mask_bits)
+    for t in (k, v, o, do):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise TsaError(ERR_INVALID_ARGUMENT, "q, k, v, o, do must have one shape and dtype")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L):
+        raise TsaError(ERR_INVALID_ARGUMENT, "lse must be float32 [B, H, L]")
+    T_q = -(-L // M)
+    if mask_bits.dtype not in (torch.int32, torch.uint32) or \
+            tuple(mask_bits.shape) != (B, H, T_q, mask_row_words(L, N)):
+        raise TsaError(ERR_INVALID_ARGUMENT, "mask_bits must be int32/uint32 [B, H, T_q, words]")
+    pr = Problem(B, H, L, d, M, N, _dtype_code(q))
+    if workspace is None:
+        ws, nws = _workspace(OP_ATTENTION_BWD, pr, q.device)
+    else:
+        _need_cuda(workspace)
+        ws, nws = workspace, workspace.numel() * workspace.element_size()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    _check(lib().tsa_attention_bwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+                                   _ptr(lse), _ptr(mask_bits), ctypes.c_float(scale), _ptr(dq),
+                                   _ptr(dk), _ptr(dv), _ptr(ws), nws, _stream()))
+    return dq, dk, dv
 
 
 def mask_compact(mask_bits, L: int, M: int, N: int, col_capacity: int | None = None):

@@ -102,6 +102,11 @@ tsa_status_t tsa_workspace_size(tsa_op_t op, const tsa_problem_t* p, size_t* byt
       if ((s = check_problem(p, true)) != TSA_OK) return s;
       *bytes = tsa::predict_workspace(p);
       return TSA_OK;
+    case TSA_OP_ATTENTION_BWD:
+      if ((s = check_problem(p, true)) != TSA_OK) return s;
+      if (p->dtype != TSA_DTYPE_BF16) return fail(TSA_ERR_UNSUPPORTED, "backward supports bf16 only");
+      *bytes = tsa::attention_bwd_workspace_bytes(p);
+      return TSA_OK;
   }
   return fail(TSA_ERR_INVALID_ARGUMENT, "unknown op %d", (int)op);
 }
@@ -129,6 +134,37 @@ tsa_status_t tsa_attention_fwd(const tsa_problem_t* p, const void* q, const void
   const hipError_t e = p->dtype == TSA_DTYPE_BF16 ? tsa::launch_attention_bf16(a)
                                                   : tsa::launch_attention_f32(a);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  return TSA_OK;
+}
+
+tsa_status_t tsa_attention_bwd(const tsa_problem_t* p, const void* q, const void* k, const void* v,
+                               const void* o, const void* d_o, const float* lse,
+                               const uint32_t* mask_bits, float scale, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  tsa_status_t s = check_problem(p, true);
+  if (s != TSA_OK) return s;
+  if (p->dtype != TSA_DTYPE_BF16) return fail(TSA_ERR_UNSUPPORTED, "backward supports bf16 only");
+  if (!q || !k || !v || !o || !d_o || !lse || !mask_bits || !dq || !dk || !dv)
+    return fail(TSA_ERR_INVALID_ARGUMENT, "q, k, v, o, d_o, lse, mask_bits, dq, dk and dv must be non-NULL");
+  if (!std::isfinite(scale)) return fail(TSA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(d_o, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(mask_bits, 4) ||
+      !aligned(lse, 4))
+    return fail(TSA_ERR_INVALID_ARGUMENT, "tensors need 16-byte, mask/lse 4-byte alignment");
+  const void* ins[] = {q, k, v, o, d_o, lse};
+  for (const void* x : ins)
+    if (x == dq || x == dk || x == dv) return fail(TSA_ERR_INVALID_ARGUMENT, "a gradient aliases an input");
+  if (dq == dk || dq == dv || dk == dv) return fail(TSA_ERR_INVALID_ARGUMENT, "gradients alias each other");
+  const size_t need = tsa::attention_bwd_workspace_bytes(p);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(TSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, 256-byte aligned (got %zu)",
+                need, workspace_bytes);
+  if ((long long)p->B * p->H * ((p->L + 127) / 128) > kMaxGrid)
+    return fail(TSA_ERR_UNSUPPORTED, "grid too large");
+  tsa::BwdLaunch a{p, q, k, v, o, d_o, lse, mask_bits, scale, dq, dk, dv, workspace,
+                   static_cast<hipStream_t>(stream)};
+  const hipError_t e = tsa::launch_attention_bwd(a);
+  if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
   return TSA_OK;
 }
 

@@ -1,0 +1,664 @@
+// Tile-sparse attention backward kernels (gfx950, wave64, 16x16x32 bf16 MFMA).
+//
+// Operation: the gradient, for an upstream gradient dO of the output, of the
+// FG-Attn forward ("FG-Attn: Leveraging Fine-Grained Sparse Attention in
+// Video Diffusion Models", section Abstract: the scores of every M x N tile
+// whose keep bit is 0 are skipped and take no part in the softmax).  The page
+// defines only the forward; these are its derivatives.  With P the kept-score
+// softmax of the forward, recomputed from the forward's log-sum-exp, and
+// D[r] = sum_d dO[r,d] O[r,d] (= sum_c P[r,c] dP[r,c]):
+//   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),
+//   dQ = scale dS K,   dK = scale dS^T Q.
+// Skipped tiles have P = 0 and cost no matrix-core work.
+//
+// Three kernels, all on the 16x16 MFMA operand layouts of tsa_device.h:
+//   * bwd_prep_kernel: D and lse2 = LSE * log2(e) per row, written per
+//     128-row chunk (128 lse2 values, then 128 D values).  A row past L or
+//     with no kept key gets lse2 = +inf, which makes its probabilities 0.
+//   * bwd_dkdv_kernel: a work-group owns 128 consecutive keys of one (b, h),
+//     eight waves of 16.  Query rows stream through LDS in double-buffered
+//     chunks of 128 rows (Q rows, dO rows and the chunk's lse2 / D).  Per
+//     chunk each wave lists the 16-row query units in which a tile of one of
+//     its keys is kept (M is a multiple of 16, so a unit lies in one mask
+//     row) and processes them two at a time:
+//       S = Q K_w^T, dP = dO V_w^T   (A = Q / dO rows from LDS, B = the
+//                                     wave's K / V fragment in registers),
+//       P = 2^(S c - lse2), dS = P (dP - D)   (c = scale log2(e)),
+//       dV^T += dO^T P, dK^T += Q^T dS   (A = dO^T / Q^T from transposing
+//                                         LDS reads of the same rows).
+//     The accumulator layout of S and dP (lane: four query rows of each
+//     unit, one key) is directly the B operand of the two updates.
+//   * bwd_dq_kernel: a work-group owns 256 query rows (16 waves of 16), as
+//     in the forward; K and V rows stream through LDS in double-buffered
+//     chunks of 128 keys.  Per chunk each wave lists its kept keys (one byte
+//     each, in LDS) and takes them 32 per pass:
+//       S^T = K Q^T, dP^T = V dO^T   (A = K / V rows, B = the wave's Q / dO
+//                                     fragments), P^T, dS^T as above,
+//       dQ^T += K^T dS^T   (A = K^T from transposing reads of the K rows).
+// dK and dV need no atomics (each key belongs to one wave), and dQ is
+// recomputed per query instead of accumulated across key blocks.
+#pragma once
+
+#include "attention_fwd_octet.h"
+
+namespace tsa {
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;      // [B*H][L] natural-log sum-exp from the forward
+  const uint32_t* mask;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* ld;             // [B*H][n_qc][256]: lse2 of a chunk's 128 rows, then D
+  int L, M, T_q, words;
+  int n_qc;              // 128-row chunks per (b, h)
+  int n_kblocks;         // 128-key blocks per (b, h) (dK/dV grid)
+  int n_qblocks;         // 256-row blocks per (b, h) (dQ grid)
+  float scale;           // as passed by the caller
+  float cs;              // |scale| * log2(e)
+};
+
+constexpr int kBwdChunk = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposing LDS read (16-bit elements): within each 16-lane group, lane s
+// points at 4 consecutive elements of row s>>2 of a 4-row block; lane n of
+// the group receives element n of each of the four rows (column n of the
+// 16-column block the four lanes of a row cover).
+__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t a) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a));
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0,
+                                           0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// D = rowsum(dO * O) and lse2 per 128-row chunk: one work-group per chunk
+// (block index = (b*H + h) * n_qc + chunk), two threads per row (half a row
+// each).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+  const int bh = (int)blockIdx.x / p.n_qc, c = (int)blockIdx.x - bh * p.n_qc;
+  const int t = threadIdx.x, row = t >> 1, half = t & 1;
+  const int r = c * kBwdChunk + row;
+  float acc = 0.f;
+  if (r < p.L) {
+    const size_t off = ((size_t)bh * p.L + r) * D + half * (D / 2);
+    const u32x4* og = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(p.o) + off);
+    const u32x4* dg = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(p.dout) + off);
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      const u32x4 a = og[i], b = dg[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc += __uint_as_float(a[e] << 16) * __uint_as_float(b[e] << 16);
+        acc += __uint_as_float(a[e] & 0xffff0000u) * __uint_as_float(b[e] & 0xffff0000u);
+      }
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  if (half == 0) {
+    float* out = p.ld + ((size_t)bh * p.n_qc + c) * 256;
+    float l2 = INFINITY, dd = 0.f;
+    if (r < p.L) {
+      const float ls = p.lse[(size_t)bh * p.L + r];
+      if (ls > -INFINITY && ls < INFINITY) {
+        l2 = ls * kLog2e;
+        dd = acc;
+      }
+    }
+    out[row] = l2;
+    out[kBwdChunk + row] = dd;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: keys owned by waves, query rows streamed.
+template <int D>
+struct DkdvCfg {
+  static constexpr int QC = kBwdChunk;          // query rows per chunk
+  static constexpr int UNITS = QC / 16;         // 16-row query units per chunk
+  static constexpr int W = 8;                   // waves per work-group
+  static constexpr int KEYS = 16 * W;           // keys per work-group
+  static constexpr int NSLAB = D / 32;          // 32-wide d slabs of S and dP
+  static constexpr int NDB = D / 16;            // 16-wide d blocks of dK^T, dV^T
+  static constexpr int RB = 2 * D;              // Q / dO row bytes in memory
+  static constexpr int RS = RB + 32;            // row stride in LDS
+  static constexpr int NI_T = (QC * RS + 1023) / 1024;  // 1-KB loads per Q (or dO) tile
+  static constexpr int NI = 2 * NI_T + 1;       // + one load of the chunk's lse2 and D
+  static constexpr int NI_W = (NI + W - 1) / W;
+  static_assert(UNITS == 8 && D % 32 == 0, "shape");
+};
+
+template <int D, int N>
+struct DkdvKernel {
+  using C = DkdvCfg<D>;
+  static constexpr int LOG2N = ilog2(N);
+  static constexpr int TPW = N >= 16 ? 1 : 16 / N;  // key tiles a wave's 16 keys span
+
+  struct Smem {
+    __attribute__((aligned(16))) uint8_t q[2][C::NI_T * 1024];
+    __attribute__((aligned(16))) uint8_t o[2][C::NI_T * 1024];  // dO rows
+    __attribute__((aligned(16))) float ld[2][256];               // lse2, then D
+  };
+
+  // query units of one chunk with a kept tile for this wave: entry j (a unit
+  // index) in bits 4j..4j+3, padded with the first; keep: per lane, bit u =
+  // the lane's key is kept (and exists) in unit u
+  struct Units {
+    uint64_t w;
+    int count;
+    uint32_t keep;
+  };
+
+  const BwdParams& p;
+  Smem& sm;
+  int lane, g, n, wave, L;
+  int mword, tshift;     // mask word and bit of this wave's first key tile
+  const bf16_t* __restrict__ qg;
+  const bf16_t* __restrict__ og;
+  const float* __restrict__ ldg;
+  const uint32_t* __restrict__ mhead;
+  u32x4 kf[C::NSLAB], vf[C::NSLAB];
+  f32x4 dk[C::NDB], dv[C::NDB];
+  float cs;
+  uint32_t doff[C::NI_W];
+
+  __device__ __forceinline__ DkdvKernel(const BwdParams& pp, Smem& s) : p(pp), sm(s) {}
+
+  // Byte offset read by lane `ln` for 1-KB load I of a chunk with `rows`
+  // query rows (Q tile, dO tile, then the lse2 / D block); out of range
+  // (zero) for row padding; rows past the last repeat it.
+  __device__ __forceinline__ uint32_t dma_offset(int I, int ln, int rows) const {
+    constexpr uint32_t OOB = 0x80000000u;
+    if (I >= 2 * C::NI_T) return 16u * (uint32_t)ln;
+    const int pos = (I < C::NI_T ? I : I - C::NI_T) * 1024 + 16 * ln;
+    const int row = pos / C::RS, cb = pos - row * C::RS;
+    const int r = row < rows ? row : rows - 1;
+    return row < C::QC && cb < C::RB ? (uint32_t)(r * C::RB + cb) : OOB;
+  }
+
+  __device__ __forceinline__ void issue_chunk(int c, int buf, uint32_t (&mw)[C::UNITS]) {
+    const int q0 = c * C::QC;
+    const int rows = L - q0 < C::QC ? L - q0 : C::QC;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(qg + (size_t)q0 * D), (short)0, rows * C::RB, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(og + (size_t)q0 * D), (short)0, rows * C::RB, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(ldg + (size_t)c * 256), (short)0, 1024, kBufferFlags);
+    const bool full = rows == C::QC;
+#pragma unroll
+    for (int u = 0; u < C::NI_W; ++u) {
+      const int I = wave + C::W * u;
+      if (C::NI % C::W == 0 || I < C::NI) {
+        const uint32_t off = full ? doff[u] : dma_offset(I, lane, rows);
+        if (I < C::NI_T)
+          dma16(rq, sm.q[buf] + I * 1024, off);
+        else if (I < 2 * C::NI_T)
+          dma16(ro, sm.o[buf] + (I - C::NI_T) * 1024, off);
+        else
+          dma16(rl, sm.ld[buf], off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < C::UNITS; ++u) {
+      const int r = q0 + 16 * u < L ? q0 + 16 * u : L - 1;
+      mw[u] = mhead[(size_t)(r / p.M) * p.words + mword];
+    }
+  }
+
+  __device__ __forceinline__ Units make_units(int c, const uint32_t (&mw)[C::UNITS], bool kvalid) const {
+    Units un{0ull, 0, 0u};
+    uint32_t umask = 0u;
+    const int q0 = c * C::QC;
+#pragma unroll
+    for (int u = 0; u < C::UNITS; ++u) {
+      const uint32_t f = (uniform_u32(mw[u]) >> tshift) & ((1u << TPW) - 1u);
+      const bool valid = q0 + 16 * u < L;
+      if (valid && f != 0u) umask |= 1u << u;
+      const uint32_t kbit = N >= 16 ? (f & 1u) : ((f >> (n >> LOG2N)) & 1u);
+      un.keep |= (valid ? kbit : 0u) << u;
+    }
+    if (!kvalid) un.keep = 0u;
+    un.count = __builtin_popcount(umask);
+    uint64_t w = (uint64_t)kOctetNibbles.v[umask];
+    if (un.count != 0) w |= (0x1111111111111111ull * (w & 15u)) << (4 * un.count);
+    un.w = w;
+    return un;
+  }
+
+  // Query units u0 and u1 of the chunk in buffer buf (single: u1 is padding).
+  __device__ __forceinline__ void pass(int buf, int u0, int u1, bool single, uint32_t keep) {
+    const uint32_t qa = lds_addr(sm.q[buf]) + (uint32_t)(16 * g);
+    const uint32_t oa = lds_addr(sm.o[buf]) + (uint32_t)(16 * g);
+    const uint32_t r0 = (uint32_t)(16 * u0 + n) * C::RS, r1 = (uint32_t)(16 * u1 + n) * C::RS;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, d0 = s0, d1 = s0;
+    if (single) {
+#pragma unroll
+      for (int sl = 0; sl < C::NSLAB; ++sl) {
+        s0 = Mma<bf16_t>::mac8(lds_load<u32x4>(qa + r0 + 64 * sl), kf[sl], s0);
+        d0 = Mma<bf16_t>::mac8(lds_load<u32x4>(oa + r0 + 64 * sl), vf[sl], d0);
+      }
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < C::NSLAB; ++sl) {
+        const u32x4 a0 = lds_load<u32x4>(qa + r0 + 64 * sl);
+        const u32x4 a1 = lds_load<u32x4>(qa + r1 + 64 * sl);
+        const u32x4 b0 = lds_load<u32x4>(oa + r0 + 64 * sl);
+        const u32x4 b1 = lds_load<u32x4>(oa + r1 + 64 * sl);
+        s0 = Mma<bf16_t>::mac8(a0, kf[sl], s0);
+        s1 = Mma<bf16_t>::mac8(a1, kf[sl], s1);
+        d0 = Mma<bf16_t>::mac8(b0, vf[sl], d0);
+        d1 = Mma<bf16_t>::mac8(b1, vf[sl], d1);
+      }
+    }
+    // lse2 and D of the four query rows each accumulator lane holds
+    const uint32_t lb = lds_addr(sm.ld[buf]);
+    const f32x4 l0 = lds_load<f32x4>(lb + 4u * (uint32_t)(16 * u0 + 4 * g));
+    const f32x4 l1 = lds_load<f32x4>(lb + 4u * (uint32_t)(16 * u1 + 4 * g));
+    const f32x4 e0 = lds_load<f32x4>(lb + 4u * (uint32_t)(C::QC + 16 * u0 + 4 * g));
+    const f32x4 e1 = lds_load<f32x4>(lb + 4u * (uint32_t)(C::QC + 16 * u1 + 4 * g));
+    const bool k0 = (keep >> u0) & 1u;
+    const bool k1 = !single && ((keep >> u1) & 1u);
+    bf16x8 pb, sb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p0 = k0 ? exp2_fast(__builtin_fmaf(s0[i], cs, -l0[i])) : 0.f;
+      const float p1 = k1 ? exp2_fast(__builtin_fmaf(s1[i], cs, -l1[i])) : 0.f;
+      pb[i] = (__bf16)p0;
+      pb[4 + i] = (__bf16)p1;
+      sb[i] = (__bf16)(p0 * (d0[i] - e0[i]));
+      sb[4 + i] = (__bf16)(p1 * (d1[i] - e1[i]));
+    }
+    const u32x4 pbo = __builtin_bit_cast(u32x4, pb), sbo = __builtin_bit_cast(u32x4, sb);
+    // transposing reads: lane (g, n) points at row 4g + n/4 of unit u_b,
+    // d = 16j + 4(n%4) .. +3; it receives d = 16j + n of rows 4g..4g+3
+    const uint32_t tb = (uint32_t)(8 * (n & 3));
+    const uint32_t t0 = (uint32_t)(16 * u0 + 4 * g + (n >> 2)) * C::RS + tb;
+    const uint32_t t1 = (uint32_t)(16 * u1 + 4 * g + (n >> 2)) * C::RS + tb;
+    const uint32_t qt = lds_addr(sm.q[buf]), ot = lds_addr(sm.o[buf]);
+#pragma unroll
+    for (int j = 0; j < C::NDB; ++j) {
+      const u32x2 x = lds_read_tr16(ot + t0 + 32u * j), y = lds_read_tr16(ot + t1 + 32u * j);
+      dv[j] = Mma<bf16_t>::mac8(u32x4{x[0], x[1], y[0], y[1]}, pbo, dv[j]);
+      const u32x2 z = lds_read_tr16(qt + t0 + 32u * j), w = lds_read_tr16(qt + t1 + 32u * j);
+      dk[j] = Mma<bf16_t>::mac8(u32x4{z[0], z[1], w[0], w[1]}, sbo, dk[j]);
+    }
+  }
+
+  __device__ __forceinline__ void run_units(int buf, const Units& un) {
+    uint64_t rest = un.w;
+    for (int q = 0; q < un.count; q += 2) {
+      const int u0 = (int)(rest & 15u), u1 = (int)((rest >> 4) & 15u);
+      rest >>= 8;
+      pass(buf, u0, u1, un.count - q == 1, un.keep);
+    }
+  }
+
+  __device__ __forceinline__ void run() {
+    const int tid = threadIdx.x;
+    lane = tid & 63;
+    g = lane >> 4;
+    n = lane & 15;
+    wave = wave_uniform(tid >> 6);
+    const int lb = xcd_major_block((int)blockIdx.x, (int)gridDim.x);
+    const int bh = lb / p.n_kblocks;
+    const int kb = lb - bh * p.n_kblocks;
+    L = p.L;
+    const size_t head = (size_t)bh * (size_t)L * D;
+    qg = reinterpret_cast<const bf16_t*>(p.q) + head;
+    og = reinterpret_cast<const bf16_t*>(p.dout) + head;
+    ldg = p.ld + (size_t)bh * p.n_qc * 256;
+    mhead = p.mask + (size_t)bh * p.T_q * p.words;
+    const int key0 = kb * C::KEYS + 16 * wave;  // first key of this wave
+    const bool act = key0 < L;
+    const int tile0 = act ? key0 / N : 0;
+    mword = tile0 >> 5;
+    tshift = tile0 & 31;
+    const int key = key0 + n;
+    const bool kvalid = key < L;
+    const int kr = kvalid ? key : L - 1;
+    const bf16_t* kp = reinterpret_cast<const bf16_t*>(p.k) + head + (size_t)kr * D;
+    const bf16_t* vp = reinterpret_cast<const bf16_t*>(p.v) + head + (size_t)kr * D;
+#pragma unroll
+    for (int s = 0; s < C::NSLAB; ++s) {
+      kf[s] = *reinterpret_cast<const u32x4*>(kp + 32 * s + 8 * g);
+      vf[s] = *reinterpret_cast<const u32x4*>(vp + 32 * s + 8 * g);
+    }
+    if (!kvalid)
+#pragma unroll
+      for (int s = 0; s < C::NSLAB; ++s) {
+        kf[s] = u32x4{0u, 0u, 0u, 0u};
+        vf[s] = u32x4{0u, 0u, 0u, 0u};
+      }
+    cs = p.cs;
+    if (p.scale < 0.f)  // c * s = |c| * (q . (-k)), and negating bf16 is exact
+#pragma unroll
+      for (int s = 0; s < C::NSLAB; ++s) kf[s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    // the fragments are complete here: no load wait lands in the chunk loop
+#pragma unroll
+    for (int s = 0; s < C::NSLAB; ++s) {
+      asm volatile("" : "+v"(kf[s]));
+      asm volatile("" : "+v"(vf[s]));
+    }
+#pragma unroll
+    for (int j = 0; j < C::NDB; ++j) {
+      dk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < C::NI_W; ++u) {
+      const int I = wave + C::W * u;
+      doff[u] = I < C::NI ? dma_offset(I, lane, C::QC) : 0u;
+    }
+    const int n_chunks = p.n_qc;
+    uint32_t mw[C::UNITS];
+    issue_chunk(0, 0, mw);
+    __builtin_amdgcn_s_waitcnt(0);
+    Units cur{0ull, 0, 0u};
+    if (act) cur = make_units(0, mw, kvalid);
+    __syncthreads();
+    for (int c = 0; c < n_chunks; ++c) {
+      const int buf = c & 1;
+      const bool more = c + 1 < n_chunks;
+      // buffer buf^1 was last read in iteration c-1, which every wave has left
+      uint32_t mwn[C::UNITS];
+      if (more) issue_chunk(c + 1, buf ^ 1, mwn);
+      if (act) run_units(buf, cur);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c+1 have landed
+      if (act && more) cur = make_units(c + 1, mwn, kvalid);
+      __syncthreads();                // ... and every other wave's
+    }
+
+    if (!kvalid) return;
+    bf16_t* dkg = reinterpret_cast<bf16_t*>(p.dk) + head + (size_t)key * D;
+    bf16_t* dvg = reinterpret_cast<bf16_t*>(p.dv) + head + (size_t)key * D;
+#pragma unroll
+    for (int j = 0; j < C::NDB; ++j) {
+      bf16x4 a, b;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = (__bf16)(dk[j][i] * p.scale);
+        b[i] = (__bf16)dv[j][i];
+      }
+      *reinterpret_cast<u32x2*>(dkg + 16 * j + 4 * g) = __builtin_bit_cast(u32x2, a);
+      *reinterpret_cast<u32x2*>(dvg + 16 * j + 4 * g) = __builtin_bit_cast(u32x2, b);
+    }
+  }
+};
+
+template <int D, int N>
+__global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
+  static_assert(DkdvCfg<D>::W == 8, "launch bounds: 8 waves");
+  using K = DkdvKernel<D, N>;
+  __shared__ __attribute__((aligned(16))) typename K::Smem sm;
+  K k(p, sm);
+  k.run();
+}
+
+// ---------------------------------------------------------------------------
+// dQ: query rows owned by waves, keys streamed (per-key lists, any N).
+template <int D, int N>
+struct DqCfg {
+  static constexpr int KC = kBwdChunk;          // keys per chunk
+  // waves per work-group: 16 (four per SIMD, 128 registers each), but 8 for
+  // N = 1, whose four mask words per chunk do not fit beside the rest
+  static constexpr int W = D == 128 && N == 1 ? 8 : 16;
+  static constexpr int ROWS = 16 * W;           // query rows per work-group
+  static constexpr int NSLAB = D / 32;
+  static constexpr int NDB = D / 16;
+  static constexpr int RB = 2 * D;              // K / V row bytes in memory
+  static constexpr int RS = RB + 32;            // row stride in LDS
+  static constexpr int NI_T = (KC * RS + 1023) / 1024;
+  static constexpr int NI = 2 * NI_T;
+  static constexpr int NI_W = (NI + W - 1) / W;
+  static constexpr int LIST = KC + 32;          // list bytes per wave (entries + padding)
+};
+
+template <int D, int N>
+struct DqKernel {
+  using C = DqCfg<D, N>;
+  static constexpr int LOG2N = ilog2(N);
+  static constexpr int TPC = C::KC / N;                 // key tiles per chunk
+  static constexpr int MW = TPC >= 32 ? TPC / 32 : 1;   // mask words per chunk
+
+  struct Smem {
+    __attribute__((aligned(16))) uint8_t k[2][C::NI_T * 1024];
+    __attribute__((aligned(16))) uint8_t v[2][C::NI_T * 1024];
+    __attribute__((aligned(16))) uint8_t list[C::W][C::LIST];
+  };
+
+  const BwdParams& p;
+  Smem& sm;
+  int lane, g, n, wave, L;
+  const bf16_t* __restrict__ kg;
+  const bf16_t* __restrict__ vg;
+  const uint32_t* __restrict__ mrow;
+  u32x4 qf[C::NSLAB], df[C::NSLAB];
+  f32x4 dq[C::NDB];
+  float l2, dd, cs;  // lse2 and D of this lane's query row
+  uint32_t doff[C::NI_W];
+
+  __device__ __forceinline__ DqKernel(const BwdParams& pp, Smem& s) : p(pp), sm(s) {}
+
+  __device__ __forceinline__ uint32_t dma_offset(int I, int ln, int rows) const {
+    constexpr uint32_t OOB = 0x80000000u;
+    const int pos = (I < C::NI_T ? I : I - C::NI_T) * 1024 + 16 * ln;
+    const int row = pos / C::RS, cb = pos - row * C::RS;
+    const int r = row < rows ? row : rows - 1;
+    return row < C::KC && cb < C::RB ? (uint32_t)(r * C::RB + cb) : OOB;
+  }
+
+  __device__ __forceinline__ void issue_chunk(int c, int buf, uint32_t (&mw)[MW]) {
+    const int kbase = c * C::KC;
+    const int rows = L - kbase < C::KC ? L - kbase : C::KC;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kg + (size_t)kbase * D), (short)0, rows * C::RB, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vg + (size_t)kbase * D), (short)0, rows * C::RB, kBufferFlags);
+    const bool full = rows == C::KC;
+#pragma unroll
+    for (int u = 0; u < C::NI_W; ++u) {
+      const int I = wave + C::W * u;
+      if (C::NI % C::W == 0 || I < C::NI) {
+        const uint32_t off = full ? doff[u] : dma_offset(I, lane, rows);
+        if (I < C::NI_T)
+          dma16(rk, sm.k[buf] + I * 1024, off);
+        else
+          dma16(rv, sm.v[buf] + (I - C::NI_T) * 1024, off);
+      }
+    }
+    const int w0 = (c * TPC) >> 5;
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      const int wi = w0 + i;
+      mw[i] = mrow[wi < p.words ? wi : p.words - 1];
+    }
+  }
+
+  // Kept keys of chunk c, ascending, into this wave's list area, then 32
+  // copies of the first kept key; returns the number of kept keys.  Lane l
+  // looks at keys l and l + 64 of the chunk.
+  __device__ __forceinline__ int make_list(int c, const uint32_t (&mw)[MW]) const {
+    const int left = L - c * C::KC;
+    const int bit0 = TPC < 32 ? (c * TPC) & 31 : 0;  // bit of the chunk's first tile
+    bool keep[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int key = lane + 64 * h;
+      const int b = bit0 + (key >> LOG2N);
+      uint32_t w = uniform_u32(mw[0]);
+#pragma unroll
+      for (int i = 1; i < MW; ++i)
+        if ((b >> 5) == i) w = uniform_u32(mw[i]);
+      keep[h] = key < left && ((w >> (b & 31)) & 1u);
+    }
+    const uint64_t b0 = __builtin_amdgcn_ballot_w64(keep[0]);
+    const uint64_t b1 = __builtin_amdgcn_ballot_w64(keep[1]);
+    const int c0 = __builtin_popcountll(b0);
+    const int count = c0 + __builtin_popcountll(b1);
+    if (count == 0) return 0;
+    uint8_t* lst = sm.list[wave];
+    if (keep[0]) lst[prefix_count64(b0)] = (uint8_t)lane;
+    if (keep[1]) lst[c0 + prefix_count64(b1)] = (uint8_t)(lane + 64);
+    const int first = b0 != 0ull ? __builtin_ctzll(b0) : 64 + __builtin_ctzll(b1);
+    if (lane < 32) lst[count + lane] = (uint8_t)first;
+    return count;
+  }
+
+  // List positions q0..q0+31 (rem = entries left from q0; positions >= rem
+  // are padding).  Score block b holds positions q0+16b..q0+16b+15; the
+  // accumulators leave lane group g with positions 4g..4g+3 of each block.
+  __device__ __forceinline__ void pass(int buf, int q0, int rem) {
+    const bool single = rem <= 16;
+    const uint8_t* lst = sm.list[wave];
+    const uint32_t kk0 = lst[q0 + n], kk1 = lst[q0 + 16 + n];
+    const int tp = q0 + 4 * g + (n >> 2);
+    const uint32_t kt0 = lst[tp], kt1 = lst[tp + 16];
+    const uint32_t kb = lds_addr(sm.k[buf]) + (uint32_t)(16 * g);
+    const uint32_t vb = lds_addr(sm.v[buf]) + (uint32_t)(16 * g);
+    const uint32_t ka0 = mad_u24(kk0, (uint32_t)C::RS, kb), ka1 = mad_u24(kk1, (uint32_t)C::RS, kb);
+    const uint32_t va0 = mad_u24(kk0, (uint32_t)C::RS, vb), va1 = mad_u24(kk1, (uint32_t)C::RS, vb);
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, d0 = s0, d1 = s0;
+    if (single) {
+#pragma unroll
+      for (int sl = 0; sl < C::NSLAB; ++sl) {
+        s0 = Mma<bf16_t>::mac8(lds_load<u32x4>(ka0 + 64 * sl), qf[sl], s0);
+        d0 = Mma<bf16_t>::mac8(lds_load<u32x4>(va0 + 64 * sl), df[sl], d0);
+      }
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < C::NSLAB; ++sl) {
+        const u32x4 a0 = lds_load<u32x4>(ka0 + 64 * sl);
+        const u32x4 a1 = lds_load<u32x4>(ka1 + 64 * sl);
+        const u32x4 b0 = lds_load<u32x4>(va0 + 64 * sl);
+        const u32x4 b1 = lds_load<u32x4>(va1 + 64 * sl);
+        s0 = Mma<bf16_t>::mac8(a0, qf[sl], s0);
+        s1 = Mma<bf16_t>::mac8(a1, qf[sl], s1);
+        d0 = Mma<bf16_t>::mac8(b0, df[sl], d0);
+        d1 = Mma<bf16_t>::mac8(b1, df[sl], d1);
+      }
+    }
+    bf16x8 sb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float p0 = exp2_fast(__builtin_fmaf(s0[i], cs, -l2));
+      float p1 = exp2_fast(__builtin_fmaf(s1[i], cs, -l2));
+      if (4 * g + i >= rem) p0 = 0.f;           // padding positions
+      if (single || 16 + 4 * g + i >= rem) p1 = 0.f;
+      sb[i] = (__bf16)(p0 * (d0[i] - dd));
+      sb[4 + i] = (__bf16)(p1 * (d1[i] - dd));
+    }
+    const u32x4 sbo = __builtin_bit_cast(u32x4, sb);
+    // K^T operand: lane (g, n) points at d = 16j + 4(n%4) of the key at
+    // position 4g + n/4 of each block and receives d = 16j + n of the four keys
+    const uint32_t tb = lds_addr(sm.k[buf]) + (uint32_t)(8 * (n & 3));
+    const uint32_t ta0 = mad_u24(kt0, (uint32_t)C::RS, tb), ta1 = mad_u24(kt1, (uint32_t)C::RS, tb);
+#pragma unroll
+    for (int j = 0; j < C::NDB; ++j) {
+      const u32x2 x = lds_read_tr16(ta0 + 32u * j), y = lds_read_tr16(ta1 + 32u * j);
+      dq[j] = Mma<bf16_t>::mac8(u32x4{x[0], x[1], y[0], y[1]}, sbo, dq[j]);
+    }
+  }
+
+  __device__ __forceinline__ void run() {
+    const int tid = threadIdx.x;
+    lane = tid & 63;
+    g = lane >> 4;
+    n = lane & 15;
+    wave = wave_uniform(tid >> 6);
+    const int lb = xcd_major_block((int)blockIdx.x, (int)gridDim.x);
+    const int bh = lb / p.n_qblocks;
+    const int qb = lb - bh * p.n_qblocks;
+    L = p.L;
+    const size_t head = (size_t)bh * (size_t)L * D;
+    kg = reinterpret_cast<const bf16_t*>(p.k) + head;
+    vg = reinterpret_cast<const bf16_t*>(p.v) + head;
+    const int row0 = qb * C::ROWS + 16 * wave;
+    const bool act = row0 < L;
+    mrow = p.mask + ((size_t)bh * p.T_q + (size_t)(act ? row0 / p.M : 0)) * p.words;
+    const int r = row0 + n;
+    const bool rvalid = r < L;
+    const int rq = rvalid ? r : L - 1;
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(p.q) + head + (size_t)rq * D;
+    const bf16_t* dp = reinterpret_cast<const bf16_t*>(p.dout) + head + (size_t)rq * D;
+#pragma unroll
+    for (int s = 0; s < C::NSLAB; ++s) {
+      qf[s] = *reinterpret_cast<const u32x4*>(qp + 32 * s + 8 * g);
+      df[s] = *reinterpret_cast<const u32x4*>(dp + 32 * s + 8 * g);
+    }
+    if (!rvalid)
+#pragma unroll
+      for (int s = 0; s < C::NSLAB; ++s) {
+        qf[s] = u32x4{0u, 0u, 0u, 0u};
+        df[s] = u32x4{0u, 0u, 0u, 0u};
+      }
+    cs = p.cs;
+    if (p.scale < 0.f)
+#pragma unroll
+      for (int s = 0; s < C::NSLAB; ++s) qf[s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    const float* ldr = p.ld + ((size_t)bh * p.n_qc + (size_t)(rq / kBwdChunk)) * 256 + (rq % kBwdChunk);
+    l2 = rvalid ? ldr[0] : INFINITY;
+    dd = rvalid ? ldr[kBwdChunk] : 0.f;
+#pragma unroll
+    for (int s = 0; s < C::NSLAB; ++s) {
+      asm volatile("" : "+v"(qf[s]));
+      asm volatile("" : "+v"(df[s]));
+    }
+    asm volatile("" : "+v"(l2), "+v"(dd));
+#pragma unroll
+    for (int j = 0; j < C::NDB; ++j) dq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < C::NI_W; ++u) {
+      const int I = wave + C::W * u;
+      doff[u] = I < C::NI ? dma_offset(I, lane, C::KC) : 0u;
+    }
+    const int n_chunks = (L + C::KC - 1) / C::KC;
+    uint32_t mw[MW];
+    issue_chunk(0, 0, mw);
+    __builtin_amdgcn_s_waitcnt(0);
+    int count = act ? make_list(0, mw) : 0;
+    __syncthreads();
+    for (int c = 0; c < n_chunks; ++c) {
+      const int buf = c & 1;
+      const bool more = c + 1 < n_chunks;
+      uint32_t mwn[MW];
+      if (more) issue_chunk(c + 1, buf ^ 1, mwn);
+      if (act)
+        for (int q0 = 0; q0 < count; q0 += 32) pass(buf, q0, count - q0);
+      __builtin_amdgcn_s_waitcnt(0);
+      if (act && more) count = make_list(c + 1, mwn);
+      __syncthreads();
+    }
+
+    if (!rvalid) return;
+    bf16_t* dqg = reinterpret_cast<bf16_t*>(p.dq) + head + (size_t)r * D;
+#pragma unroll
+    for (int j = 0; j < C::NDB; ++j) {
+      bf16x4 a;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = (__bf16)(dq[j][i] * p.scale);
+      *reinterpret_cast<u32x2*>(dqg + 16 * j + 4 * g) = __builtin_bit_cast(u32x2, a);
+    }
+  }
+};
+
+template <int D, int N>
+__global__ __launch_bounds__((64 * DqCfg<D, N>::W)) void bwd_dq_kernel(BwdParams p) {
+  using K = DqKernel<D, N>;
+  __shared__ __attribute__((aligned(16))) typename K::Smem sm;
+  K k(p, sm);
+  k.run();
+}
+
+}  // namespace tsa

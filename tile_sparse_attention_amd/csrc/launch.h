@@ -48,6 +48,29 @@ inline size_t attention_workspace_bytes(const tsa_problem_t* p) {
   return attention_need_offset(p) + (attention_groups(p) * (kNeedWords + 1) + 1) * sizeof(uint32_t);
 }
 
+// Backward (bf16): the workspace holds, per (b, h) and 128-row chunk, the
+// chunk's 128 lse2 values and 128 D values (fp32).
+struct BwdLaunch {
+  const tsa_problem_t* p;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  const uint32_t* mask;
+  float scale;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* workspace;
+  hipStream_t stream;
+};
+inline size_t attention_bwd_workspace_bytes(const tsa_problem_t* p) {
+  return (size_t)p->B * p->H * (size_t)((p->L + 127) / 128) * 256 * sizeof(float);
+}
+hipError_t launch_attention_bwd(const BwdLaunch& a);
+
 hipError_t launch_attention_bf16(const AttnLaunch& a);
 hipError_t launch_attention_f32(const AttnLaunch& a);
 

@@ -7,6 +7,6 @@ without sharing any of the method's code.
 """
 from .gen import (  # noqa: F401
     Workload, MaskRecipe, CONFIGS, HEADLINE, get, splitmix64, pack_bits,
-    mask_bits, mask_rows_bool, make_qkv, sample_tiles, row_words, diag_tiles,
+    mask_bits, mask_rows_bool, make_qkv, make_do, sample_tiles, row_words, diag_tiles,
     frame_thresholds, hash_params, prob_threshold, structured_params,
 )

@@ -391,6 +391,17 @@ def make_qkv(w: Workload, heads=None):
     return tuple(out)
 
 
+def make_do(w: Workload, heads=None):
+    """Seeded upstream gradient dO for the backward: torch CPU [B, H, L, d] in the
+    workload dtype, standard normal from its own stream (seed * 8 + 5)."""
+    import torch
+
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    g = torch.Generator().manual_seed(w.seed * 8 + 5)
+    x = torch.randn(w.B, w.H, w.L, w.d, generator=g, dtype=torch.float32).to(tdt)
+    return x[:, :heads].contiguous() if heads is not None else x
+
+
 # --------------------------------------------------------------------------
 # Parity sampling
 # --------------------------------------------------------------------------
