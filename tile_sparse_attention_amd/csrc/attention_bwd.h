@@ -66,16 +66,6 @@ struct BwdParams {
 constexpr int kBwdChunk = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// Transposing LDS read (16-bit elements): within each 16-lane group, lane s
-// points at 4 consecutive elements of row s>>2 of a 4-row block; lane n of
-// the group receives element n of each of the four rows (column n of the
-// 16-column block the four lanes of a row cover).
-__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t a) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a));
-}
-
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0,
                                            0, 0);
@@ -145,23 +135,24 @@ struct DkdvKernel {
   static constexpr int LOG2N = ilog2(N);
   static constexpr int TPW = N >= 16 ? 1 : 16 / N;  // key tiles a wave's 16 keys span
 
-  struct Smem {
-    __attribute__((aligned(16))) uint8_t q[2][C::NI_T * 1024];
-    __attribute__((aligned(16))) uint8_t o[2][C::NI_T * 1024];  // dO rows
-    __attribute__((aligned(16))) float ld[2][256];               // lse2, then D
+  // one staging buffer; the two buffers are separate __shared__ objects
+  struct Buf {
+    __attribute__((aligned(16))) uint8_t q[C::NI_T * 1024];
+    __attribute__((aligned(16))) uint8_t o[C::NI_T * 1024];  // dO rows
+    __attribute__((aligned(16))) float ld[256];               // lse2, then D
   };
 
-  // query units of one chunk with a kept tile for this wave: entry j (a unit
-  // index) in bits 4j..4j+3, padded with the first; keep: per lane, bit u =
-  // the lane's key is kept (and exists) in unit u
+  // query units of one chunk with a kept tile for this wave (bit u of
+  // `units`, wave-uniform); keep: per lane, bit u = the lane's key is kept
+  // (and exists) in unit u
   struct Units {
-    uint64_t w;
-    int count;
+    uint32_t units;
     uint32_t keep;
   };
 
   const BwdParams& p;
-  Smem& sm;
+  Buf& bf0;
+  Buf& bf1;
   int lane, g, n, wave, L;
   int mword, tshift;     // mask word and bit of this wave's first key tile
   const bf16_t* __restrict__ qg;
@@ -173,7 +164,12 @@ struct DkdvKernel {
   float cs;
   uint32_t doff[C::NI_W];
 
-  __device__ __forceinline__ DkdvKernel(const BwdParams& pp, Smem& s) : p(pp), sm(s) {}
+  __device__ __forceinline__ DkdvKernel(const BwdParams& pp, Buf& b0, Buf& b1) : p(pp), bf0(b0), bf1(b1) {}
+
+  template <int B>
+  __device__ __forceinline__ Buf& bufr() const {
+    return B ? bf1 : bf0;
+  }
 
   // Byte offset read by lane `ln` for 1-KB load I of a chunk with `rows`
   // query rows (Q tile, dO tile, then the lse2 / D block); out of range
@@ -187,7 +183,10 @@ struct DkdvKernel {
     return row < C::QC && cb < C::RB ? (uint32_t)(r * C::RB + cb) : OOB;
   }
 
-  __device__ __forceinline__ void issue_chunk(int c, int buf, uint32_t (&mw)[C::UNITS]) {
+  // This wave's share of the loads of chunk c into buffer buf, and (lane
+  // u < UNITS) the mask word of query unit u; nothing waits here.
+  template <int B>
+  __device__ __forceinline__ uint32_t issue_chunk(int c) {
     const int q0 = c * C::QC;
     const int rows = L - q0 < C::QC ? L - q0 : C::QC;
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
@@ -203,71 +202,83 @@ struct DkdvKernel {
       if (C::NI % C::W == 0 || I < C::NI) {
         const uint32_t off = full ? doff[u] : dma_offset(I, lane, rows);
         if (I < C::NI_T)
-          dma16(rq, sm.q[buf] + I * 1024, off);
+          dma16(rq, bufr<B>().q + I * 1024, off);
         else if (I < 2 * C::NI_T)
-          dma16(ro, sm.o[buf] + (I - C::NI_T) * 1024, off);
+          dma16(ro, bufr<B>().o + (I - C::NI_T) * 1024, off);
         else
-          dma16(rl, sm.ld[buf], off);
+          dma16(rl, bufr<B>().ld, off);
       }
     }
-#pragma unroll
-    for (int u = 0; u < C::UNITS; ++u) {
-      const int r = q0 + 16 * u < L ? q0 + 16 * u : L - 1;
-      mw[u] = mhead[(size_t)(r / p.M) * p.words + mword];
-    }
+    const int r = q0 + 16 * (lane & (C::UNITS - 1)) < L ? q0 + 16 * (lane & (C::UNITS - 1)) : L - 1;
+    return mhead[(size_t)(r / p.M) * p.words + mword];
   }
 
-  __device__ __forceinline__ Units make_units(int c, const uint32_t (&mw)[C::UNITS], bool kvalid) const {
-    Units un{0ull, 0, 0u};
-    uint32_t umask = 0u;
+  // Units of chunk c from the mask words issue_chunk returned (lane u holds
+  // unit u's word): one ballot for the unit set, and per lane the keep bits
+  // of its key.
+  __device__ __forceinline__ Units make_units(int c, uint32_t mwv, bool kvalid) const {
     const int q0 = c * C::QC;
+    const uint32_t f = (mwv >> tshift) & ((1u << TPW) - 1u);
+    const bool kept = lane < C::UNITS && q0 + 16 * lane < L && f != 0u;
+    Units un{(uint32_t)__builtin_amdgcn_ballot_w64(kept), 0u};
 #pragma unroll
     for (int u = 0; u < C::UNITS; ++u) {
-      const uint32_t f = (uniform_u32(mw[u]) >> tshift) & ((1u << TPW) - 1u);
-      const bool valid = q0 + 16 * u < L;
-      if (valid && f != 0u) umask |= 1u << u;
-      const uint32_t kbit = N >= 16 ? (f & 1u) : ((f >> (n >> LOG2N)) & 1u);
-      un.keep |= (valid ? kbit : 0u) << u;
+      const uint32_t fu = (uint32_t)__builtin_amdgcn_readlane((int)f, u);
+      const uint32_t kbit = N >= 16 ? (fu & 1u) : ((fu >> (n >> LOG2N)) & 1u);
+      un.keep |= ((un.units >> u) & kbit) << u;
     }
     if (!kvalid) un.keep = 0u;
-    un.count = __builtin_popcount(umask);
-    uint64_t w = (uint64_t)kOctetNibbles.v[umask];
-    if (un.count != 0) w |= (0x1111111111111111ull * (w & 15u)) << (4 * un.count);
-    un.w = w;
     return un;
   }
 
-  // Query units u0 and u1 of the chunk in buffer buf (single: u1 is padding).
-  __device__ __forceinline__ void pass(int buf, int u0, int u1, bool single, uint32_t keep) {
-    const uint32_t qa = lds_addr(sm.q[buf]) + (uint32_t)(16 * g);
-    const uint32_t oa = lds_addr(sm.o[buf]) + (uint32_t)(16 * g);
+  // A operands of S and dP for query units u0 and u1: 16-byte reads of the
+  // Q and dO rows (block 1 skipped when u1 is padding)
+  struct Ops {
+    u32x4 q0[C::NSLAB], q1[C::NSLAB], o0[C::NSLAB], o1[C::NSLAB];
+  };
+
+  template <int B>
+  __device__ __forceinline__ void load_ops(Ops& op, int u0, int u1, bool single) const {
+    const lds_cptr qa = to_lds(bufr<B>().q) + 16 * g;
+    const lds_cptr oa = to_lds(bufr<B>().o) + 16 * g;
     const uint32_t r0 = (uint32_t)(16 * u0 + n) * C::RS, r1 = (uint32_t)(16 * u1 + n) * C::RS;
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, d0 = s0, d1 = s0;
-    if (single) {
 #pragma unroll
-      for (int sl = 0; sl < C::NSLAB; ++sl) {
-        s0 = Mma<bf16_t>::mac8(lds_load<u32x4>(qa + r0 + 64 * sl), kf[sl], s0);
-        d0 = Mma<bf16_t>::mac8(lds_load<u32x4>(oa + r0 + 64 * sl), vf[sl], d0);
-      }
-    } else {
-#pragma unroll
-      for (int sl = 0; sl < C::NSLAB; ++sl) {
-        const u32x4 a0 = lds_load<u32x4>(qa + r0 + 64 * sl);
-        const u32x4 a1 = lds_load<u32x4>(qa + r1 + 64 * sl);
-        const u32x4 b0 = lds_load<u32x4>(oa + r0 + 64 * sl);
-        const u32x4 b1 = lds_load<u32x4>(oa + r1 + 64 * sl);
-        s0 = Mma<bf16_t>::mac8(a0, kf[sl], s0);
-        s1 = Mma<bf16_t>::mac8(a1, kf[sl], s1);
-        d0 = Mma<bf16_t>::mac8(b0, vf[sl], d0);
-        d1 = Mma<bf16_t>::mac8(b1, vf[sl], d1);
-      }
+    for (int sl = 0; sl < C::NSLAB; ++sl) {
+      op.q0[sl] = lds_read16(qa + r0 + 64 * sl);
+      op.o0[sl] = lds_read16(oa + r0 + 64 * sl);
     }
+    if (!single)
+#pragma unroll
+      for (int sl = 0; sl < C::NSLAB; ++sl) {
+        op.q1[sl] = lds_read16(qa + r1 + 64 * sl);
+        op.o1[sl] = lds_read16(oa + r1 + 64 * sl);
+      }
+  }
+
+  // Query units u0 and u1 of the chunk in buffer buf (single: u1 is padding),
+  // with their S / dP operands already in `op`; `next` issues the next
+  // pass's operand reads once the score MFMAs have taken these.
+  template <int B, typename F>
+  __device__ __forceinline__ void pass(int u0, int u1, bool single, uint32_t keep, const Ops& op, F&& next) {
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, d0 = s0, d1 = s0;
+#pragma unroll
+    for (int sl = 0; sl < C::NSLAB; ++sl) {
+      s0 = Mma<bf16_t>::mac8(op.q0[sl], kf[sl], s0);
+      d0 = Mma<bf16_t>::mac8(op.o0[sl], vf[sl], d0);
+    }
+    if (!single)
+#pragma unroll
+      for (int sl = 0; sl < C::NSLAB; ++sl) {
+        s1 = Mma<bf16_t>::mac8(op.q1[sl], kf[sl], s1);
+        d1 = Mma<bf16_t>::mac8(op.o1[sl], vf[sl], d1);
+      }
+    next();
     // lse2 and D of the four query rows each accumulator lane holds
-    const uint32_t lb = lds_addr(sm.ld[buf]);
-    const f32x4 l0 = lds_load<f32x4>(lb + 4u * (uint32_t)(16 * u0 + 4 * g));
-    const f32x4 l1 = lds_load<f32x4>(lb + 4u * (uint32_t)(16 * u1 + 4 * g));
-    const f32x4 e0 = lds_load<f32x4>(lb + 4u * (uint32_t)(C::QC + 16 * u0 + 4 * g));
-    const f32x4 e1 = lds_load<f32x4>(lb + 4u * (uint32_t)(C::QC + 16 * u1 + 4 * g));
+    const float* lb = bufr<B>().ld;
+    const f32x4 l0 = *reinterpret_cast<const f32x4*>(lb + 16 * u0 + 4 * g);
+    const f32x4 l1 = *reinterpret_cast<const f32x4*>(lb + 16 * u1 + 4 * g);
+    const f32x4 e0 = *reinterpret_cast<const f32x4*>(lb + C::QC + 16 * u0 + 4 * g);
+    const f32x4 e1 = *reinterpret_cast<const f32x4*>(lb + C::QC + 16 * u1 + 4 * g);
     const bool k0 = (keep >> u0) & 1u;
     const bool k1 = !single && ((keep >> u1) & 1u);
     bf16x8 pb, sb;
@@ -286,23 +297,73 @@ struct DkdvKernel {
     const uint32_t tb = (uint32_t)(8 * (n & 3));
     const uint32_t t0 = (uint32_t)(16 * u0 + 4 * g + (n >> 2)) * C::RS + tb;
     const uint32_t t1 = (uint32_t)(16 * u1 + 4 * g + (n >> 2)) * C::RS + tb;
-    const uint32_t qt = lds_addr(sm.q[buf]), ot = lds_addr(sm.o[buf]);
+    const lds_cptr qt = to_lds(bufr<B>().q);
+    const lds_cptr ot = to_lds(bufr<B>().o);
+    // d block j + 1's operands are read while block j multiplies
+    auto tr = [&](lds_cptr base, int j) {
+      const u32x2 x = lds_read_tr16(base + t0 + 32u * j), y = lds_read_tr16(base + t1 + 32u * j);
+      return u32x4{x[0], x[1], y[0], y[1]};
+    };
+    u32x4 av = tr(ot, 0), ak = tr(qt, 0);
 #pragma unroll
     for (int j = 0; j < C::NDB; ++j) {
-      const u32x2 x = lds_read_tr16(ot + t0 + 32u * j), y = lds_read_tr16(ot + t1 + 32u * j);
-      dv[j] = Mma<bf16_t>::mac8(u32x4{x[0], x[1], y[0], y[1]}, pbo, dv[j]);
-      const u32x2 z = lds_read_tr16(qt + t0 + 32u * j), w = lds_read_tr16(qt + t1 + 32u * j);
-      dk[j] = Mma<bf16_t>::mac8(u32x4{z[0], z[1], w[0], w[1]}, sbo, dk[j]);
+      u32x4 nav = av, nak = ak;
+      if (j + 1 < C::NDB) {
+        nav = tr(ot, j + 1);
+        nak = tr(qt, j + 1);
+      }
+      dv[j] = Mma<bf16_t>::mac8(av, pbo, dv[j]);
+      dk[j] = Mma<bf16_t>::mac8(ak, sbo, dk[j]);
+      av = nav;
+      ak = nak;
     }
   }
 
-  __device__ __forceinline__ void run_units(int buf, const Units& un) {
-    uint64_t rest = un.w;
-    for (int q = 0; q < un.count; q += 2) {
-      const int u0 = (int)(rest & 15u), u1 = (int)((rest >> 4) & 15u);
-      rest >>= 8;
-      pass(buf, u0, u1, un.count - q == 1, un.keep);
+  // The chunk's units two at a time (ascending; an odd last one alone), each
+  // pass's S / dP operands read during the previous pass.
+  template <int B>
+  __device__ __forceinline__ void run_units(const Units& un) {
+    uint32_t m = un.units;
+    if (m == 0u) return;
+    auto take = [&](int& a, int& b, bool& single) {
+      a = __builtin_ctz(m);
+      m &= m - 1u;
+      single = m == 0u;
+      b = single ? a : __builtin_ctz(m);
+      if (!single) m &= m - 1u;
+    };
+    int u0, u1;
+    bool single;
+    take(u0, u1, single);
+    Ops op;
+    load_ops<B>(op, u0, u1, single);
+    for (;;) {
+      const bool more = m != 0u;
+      int nu0 = 0, nu1 = 0;
+      bool nsingle = true;
+      if (more) take(nu0, nu1, nsingle);
+      Ops nop;
+      pass<B>(u0, u1, single, un.keep, op, [&] {
+        if (more) load_ops<B>(nop, nu0, nu1, nsingle);
+      });
+      if (!more) break;
+      u0 = nu0;
+      u1 = nu1;
+      single = nsingle;
+      op = nop;
     }
+  }
+
+  // Chunk c from buffer B while chunk c+1 loads into the other buffer.
+  template <int B>
+  __device__ __forceinline__ void chunk_step(int c, int n_chunks, bool act, bool kvalid, Units& cur) {
+    const bool more = c + 1 < n_chunks;
+    // buffer B^1 was last read in the previous step, which every wave has left
+    const uint32_t mwn = more ? issue_chunk<B ^ 1>(c + 1) : 0u;
+    if (act) run_units<B>(cur);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c+1 have landed
+    if (act && more) cur = make_units(c + 1, mwn, kvalid);
+    __syncthreads();                // ... and every other wave's
   }
 
   __device__ __forceinline__ void run() {
@@ -362,22 +423,15 @@ struct DkdvKernel {
       doff[u] = I < C::NI ? dma_offset(I, lane, C::QC) : 0u;
     }
     const int n_chunks = p.n_qc;
-    uint32_t mw[C::UNITS];
-    issue_chunk(0, 0, mw);
+    const uint32_t mw0 = issue_chunk<0>(0);
     __builtin_amdgcn_s_waitcnt(0);
-    Units cur{0ull, 0, 0u};
-    if (act) cur = make_units(0, mw, kvalid);
+    Units cur{0u, 0u};
+    if (act) cur = make_units(0, mw0, kvalid);
     __syncthreads();
-    for (int c = 0; c < n_chunks; ++c) {
-      const int buf = c & 1;
-      const bool more = c + 1 < n_chunks;
-      // buffer buf^1 was last read in iteration c-1, which every wave has left
-      uint32_t mwn[C::UNITS];
-      if (more) issue_chunk(c + 1, buf ^ 1, mwn);
-      if (act) run_units(buf, cur);
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c+1 have landed
-      if (act && more) cur = make_units(c + 1, mwn, kvalid);
-      __syncthreads();                // ... and every other wave's
+    // two chunks per iteration, so that each step names its buffer statically
+    for (int c = 0; c < n_chunks; c += 2) {
+      chunk_step<0>(c, n_chunks, act, kvalid, cur);
+      if (c + 1 < n_chunks) chunk_step<1>(c + 1, n_chunks, act, kvalid, cur);
     }
 
     if (!kvalid) return;
@@ -401,8 +455,9 @@ template <int D, int N>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   static_assert(DkdvCfg<D>::W == 8, "launch bounds: 8 waves");
   using K = DkdvKernel<D, N>;
-  __shared__ __attribute__((aligned(16))) typename K::Smem sm;
-  K k(p, sm);
+  __shared__ __attribute__((aligned(16))) typename K::Buf b0;
+  __shared__ __attribute__((aligned(16))) typename K::Buf b1;
+  K k(p, b0, b1);
   k.run();
 }
 
@@ -432,14 +487,20 @@ struct DqKernel {
   static constexpr int TPC = C::KC / N;                 // key tiles per chunk
   static constexpr int MW = TPC >= 32 ? TPC / 32 : 1;   // mask words per chunk
 
-  struct Smem {
-    __attribute__((aligned(16))) uint8_t k[2][C::NI_T * 1024];
-    __attribute__((aligned(16))) uint8_t v[2][C::NI_T * 1024];
+  // one staging buffer (the two are separate __shared__ objects) and the
+  // per-wave key lists
+  struct Buf {
+    __attribute__((aligned(16))) uint8_t k[C::NI_T * 1024];
+    __attribute__((aligned(16))) uint8_t v[C::NI_T * 1024];
+  };
+  struct Lists {
     __attribute__((aligned(16))) uint8_t list[C::W][C::LIST];
   };
 
   const BwdParams& p;
-  Smem& sm;
+  Buf& bf0;
+  Buf& bf1;
+  Lists& ls;
   int lane, g, n, wave, L;
   const bf16_t* __restrict__ kg;
   const bf16_t* __restrict__ vg;
@@ -447,9 +508,14 @@ struct DqKernel {
   u32x4 qf[C::NSLAB], df[C::NSLAB];
   f32x4 dq[C::NDB];
   float l2, dd, cs;  // lse2 and D of this lane's query row
-  uint32_t doff[C::NI_W];
 
-  __device__ __forceinline__ DqKernel(const BwdParams& pp, Smem& s) : p(pp), sm(s) {}
+  __device__ __forceinline__ DqKernel(const BwdParams& pp, Buf& b0, Buf& b1, Lists& l)
+      : p(pp), bf0(b0), bf1(b1), ls(l) {}
+
+  template <int B>
+  __device__ __forceinline__ Buf& bufr() const {
+    return B ? bf1 : bf0;
+  }
 
   __device__ __forceinline__ uint32_t dma_offset(int I, int ln, int rows) const {
     constexpr uint32_t OOB = 0x80000000u;
@@ -459,7 +525,8 @@ struct DqKernel {
     return row < C::KC && cb < C::RB ? (uint32_t)(r * C::RB + cb) : OOB;
   }
 
-  __device__ __forceinline__ void issue_chunk(int c, int buf, uint32_t (&mw)[MW]) {
+  template <int B>
+  __device__ __forceinline__ void issue_chunk(int c, uint32_t (&mw)[MW]) {
     const int kbase = c * C::KC;
     const int rows = L - kbase < C::KC ? L - kbase : C::KC;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -471,11 +538,12 @@ struct DqKernel {
     for (int u = 0; u < C::NI_W; ++u) {
       const int I = wave + C::W * u;
       if (C::NI % C::W == 0 || I < C::NI) {
-        const uint32_t off = full ? doff[u] : dma_offset(I, lane, rows);
+        // (offsets recomputed per chunk: registers are tight at 16 waves)
+        const uint32_t off = dma_offset(I, lane, full ? C::KC : rows);
         if (I < C::NI_T)
-          dma16(rk, sm.k[buf] + I * 1024, off);
+          dma16(rk, bufr<B>().k + I * 1024, off);
         else
-          dma16(rv, sm.v[buf] + (I - C::NI_T) * 1024, off);
+          dma16(rv, bufr<B>().v + (I - C::NI_T) * 1024, off);
       }
     }
     const int w0 = (c * TPC) >> 5;
@@ -508,7 +576,7 @@ struct DqKernel {
     const int c0 = __builtin_popcountll(b0);
     const int count = c0 + __builtin_popcountll(b1);
     if (count == 0) return 0;
-    uint8_t* lst = sm.list[wave];
+    uint8_t* lst = ls.list[wave];
     if (keep[0]) lst[prefix_count64(b0)] = (uint8_t)lane;
     if (keep[1]) lst[c0 + prefix_count64(b1)] = (uint8_t)(lane + 64);
     const int first = b0 != 0ull ? __builtin_ctzll(b0) : 64 + __builtin_ctzll(b1);
@@ -519,30 +587,31 @@ struct DqKernel {
   // List positions q0..q0+31 (rem = entries left from q0; positions >= rem
   // are padding).  Score block b holds positions q0+16b..q0+16b+15; the
   // accumulators leave lane group g with positions 4g..4g+3 of each block.
-  __device__ __forceinline__ void pass(int buf, int q0, int rem) {
+  template <int B>
+  __device__ __forceinline__ void pass(int q0, int rem) {
     const bool single = rem <= 16;
-    const uint8_t* lst = sm.list[wave];
+    const uint8_t* lst = ls.list[wave];
     const uint32_t kk0 = lst[q0 + n], kk1 = lst[q0 + 16 + n];
     const int tp = q0 + 4 * g + (n >> 2);
     const uint32_t kt0 = lst[tp], kt1 = lst[tp + 16];
-    const uint32_t kb = lds_addr(sm.k[buf]) + (uint32_t)(16 * g);
-    const uint32_t vb = lds_addr(sm.v[buf]) + (uint32_t)(16 * g);
-    const uint32_t ka0 = mad_u24(kk0, (uint32_t)C::RS, kb), ka1 = mad_u24(kk1, (uint32_t)C::RS, kb);
-    const uint32_t va0 = mad_u24(kk0, (uint32_t)C::RS, vb), va1 = mad_u24(kk1, (uint32_t)C::RS, vb);
+    const lds_cptr kbase = to_lds(bufr<B>().k), vbase = to_lds(bufr<B>().v);
+    const lds_cptr ka0 = kbase + (16 * g + kk0 * C::RS), ka1 = kbase + (16 * g + kk1 * C::RS);
+    const lds_cptr va0 = vbase + (16 * g + kk0 * C::RS), va1 = vbase + (16 * g + kk1 * C::RS);
+    auto ld16 = [](lds_cptr a) { return lds_read16(a); };
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, d0 = s0, d1 = s0;
     if (single) {
 #pragma unroll
       for (int sl = 0; sl < C::NSLAB; ++sl) {
-        s0 = Mma<bf16_t>::mac8(lds_load<u32x4>(ka0 + 64 * sl), qf[sl], s0);
-        d0 = Mma<bf16_t>::mac8(lds_load<u32x4>(va0 + 64 * sl), df[sl], d0);
+        s0 = Mma<bf16_t>::mac8(ld16(ka0 + 64 * sl), qf[sl], s0);
+        d0 = Mma<bf16_t>::mac8(ld16(va0 + 64 * sl), df[sl], d0);
       }
     } else {
 #pragma unroll
       for (int sl = 0; sl < C::NSLAB; ++sl) {
-        const u32x4 a0 = lds_load<u32x4>(ka0 + 64 * sl);
-        const u32x4 a1 = lds_load<u32x4>(ka1 + 64 * sl);
-        const u32x4 b0 = lds_load<u32x4>(va0 + 64 * sl);
-        const u32x4 b1 = lds_load<u32x4>(va1 + 64 * sl);
+        const u32x4 a0 = ld16(ka0 + 64 * sl);
+        const u32x4 a1 = ld16(ka1 + 64 * sl);
+        const u32x4 b0 = ld16(va0 + 64 * sl);
+        const u32x4 b1 = ld16(va1 + 64 * sl);
         s0 = Mma<bf16_t>::mac8(a0, qf[sl], s0);
         s1 = Mma<bf16_t>::mac8(a1, qf[sl], s1);
         d0 = Mma<bf16_t>::mac8(b0, df[sl], d0);
@@ -562,13 +631,28 @@ struct DqKernel {
     const u32x4 sbo = __builtin_bit_cast(u32x4, sb);
     // K^T operand: lane (g, n) points at d = 16j + 4(n%4) of the key at
     // position 4g + n/4 of each block and receives d = 16j + n of the four keys
-    const uint32_t tb = lds_addr(sm.k[buf]) + (uint32_t)(8 * (n & 3));
-    const uint32_t ta0 = mad_u24(kt0, (uint32_t)C::RS, tb), ta1 = mad_u24(kt1, (uint32_t)C::RS, tb);
+    const lds_cptr ta0 = kbase + (8 * (n & 3) + kt0 * C::RS);
+    const lds_cptr ta1 = kbase + (8 * (n & 3) + kt1 * C::RS);
+    auto tr = [&](int j) {
+      const u32x2 x = lds_read_tr16(ta0 + 32 * j), y = lds_read_tr16(ta1 + 32 * j);
+      return u32x4{x[0], x[1], y[0], y[1]};
+    };
 #pragma unroll
-    for (int j = 0; j < C::NDB; ++j) {
-      const u32x2 x = lds_read_tr16(ta0 + 32u * j), y = lds_read_tr16(ta1 + 32u * j);
-      dq[j] = Mma<bf16_t>::mac8(u32x4{x[0], x[1], y[0], y[1]}, sbo, dq[j]);
-    }
+    for (int j = 0; j < C::NDB; ++j) dq[j] = Mma<bf16_t>::mac8(tr(j), sbo, dq[j]);
+  }
+
+  // Chunk c from buffer B while chunk c+1 loads into the other buffer.
+  template <int B>
+  __device__ __forceinline__ void chunk_step(int c, int n_chunks, bool act, int& count) {
+    const bool more = c + 1 < n_chunks;
+    uint32_t mwn[MW];
+    // buffer B^1 was last read in the previous step, which every wave has left
+    if (more) issue_chunk<B ^ 1>(c + 1, mwn);
+    if (act)
+      for (int q0 = 0; q0 < count; q0 += 32) pass<B>(q0, count - q0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c+1 have landed
+    if (act && more) count = make_list(c + 1, mwn);
+    __syncthreads();                // ... and every other wave's
   }
 
   __device__ __forceinline__ void run() {
@@ -618,27 +702,16 @@ struct DqKernel {
     asm volatile("" : "+v"(l2), "+v"(dd));
 #pragma unroll
     for (int j = 0; j < C::NDB; ++j) dq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < C::NI_W; ++u) {
-      const int I = wave + C::W * u;
-      doff[u] = I < C::NI ? dma_offset(I, lane, C::KC) : 0u;
-    }
     const int n_chunks = (L + C::KC - 1) / C::KC;
     uint32_t mw[MW];
-    issue_chunk(0, 0, mw);
+    issue_chunk<0>(0, mw);
     __builtin_amdgcn_s_waitcnt(0);
     int count = act ? make_list(0, mw) : 0;
     __syncthreads();
-    for (int c = 0; c < n_chunks; ++c) {
-      const int buf = c & 1;
-      const bool more = c + 1 < n_chunks;
-      uint32_t mwn[MW];
-      if (more) issue_chunk(c + 1, buf ^ 1, mwn);
-      if (act)
-        for (int q0 = 0; q0 < count; q0 += 32) pass(buf, q0, count - q0);
-      __builtin_amdgcn_s_waitcnt(0);
-      if (act && more) count = make_list(c + 1, mwn);
-      __syncthreads();
+    // two chunks per iteration, so that each step names its buffer statically
+    for (int c = 0; c < n_chunks; c += 2) {
+      chunk_step<0>(c, n_chunks, act, count);
+      if (c + 1 < n_chunks) chunk_step<1>(c + 1, n_chunks, act, count);
     }
 
     if (!rvalid) return;
@@ -656,8 +729,10 @@ struct DqKernel {
 template <int D, int N>
 __global__ __launch_bounds__((64 * DqCfg<D, N>::W)) void bwd_dq_kernel(BwdParams p) {
   using K = DqKernel<D, N>;
-  __shared__ __attribute__((aligned(16))) typename K::Smem sm;
-  K k(p, sm);
+  __shared__ __attribute__((aligned(16))) typename K::Buf b0;
+  __shared__ __attribute__((aligned(16))) typename K::Buf b1;
+  __shared__ __attribute__((aligned(16))) typename K::Lists lists;
+  K k(p, b0, b1, lists);
   k.run();
 }
 

@@ -59,14 +59,20 @@ struct KeyKernel {
   using C = KeyCfg<D, N>;
   static constexpr float RESCALE_STEP = 8.f;  // log2 units the max may grow before rescaling
 
-  struct Smem {
-    __attribute__((aligned(16))) uint8_t k[2][C::NI_T * 1024];
-    __attribute__((aligned(16))) uint8_t v[2][C::NI_T * 1024];
+  // one staging buffer (K and V rows of a chunk; the two buffers are separate
+  // __shared__ objects, see lds_cptr) and the per-wave key lists
+  struct Buf {
+    __attribute__((aligned(16))) uint8_t k[C::NI_T * 1024];
+    __attribute__((aligned(16))) uint8_t v[C::NI_T * 1024];
+  };
+  struct Lists {
     __attribute__((aligned(16))) uint8_t list[C::W][C::LIST];
   };
 
   const AttnParams& p;
-  Smem& sm;
+  Buf& bf0;
+  Buf& bf1;
+  Lists& ls;
   int lane, g, n, wave, L;
   const bf16_t* __restrict__ kg;
   const bf16_t* __restrict__ vg;
@@ -79,9 +85,14 @@ struct KeyKernel {
   float cs;           // |scale| * log2(e)
   float thr;          // rescale threshold on unscaled scores: -inf before the first pass,
                       // then RESCALE_STEP / cs
-  uint32_t doff[C::NI_W];  // per-lane load offsets of a full chunk (chunk-invariant)
 
-  __device__ __forceinline__ KeyKernel(const AttnParams& pp, Smem& s) : p(pp), sm(s) {}
+  __device__ __forceinline__ KeyKernel(const AttnParams& pp, Buf& b0, Buf& b1, Lists& l)
+      : p(pp), bf0(b0), bf1(b1), ls(l) {}
+
+  template <int B>
+  __device__ __forceinline__ Buf& bufr() const {
+    return B ? bf1 : bf0;
+  }
 
   // Byte offset read by lane `ln` for 1-KB load `I` (K tile for I < NI_T,
   // else V tile) of a chunk with `rows` keys, relative to the tile's
@@ -97,7 +108,8 @@ struct KeyKernel {
 
   // This wave's share of the loads of chunk c into buffer `buf`, and the
   // mask words of chunk c (wave-uniform).  Nothing waits here.
-  __device__ __forceinline__ void issue_chunk(int c, int buf, uint32_t (&mw)[C::MW]) {
+  template <int B>
+  __device__ __forceinline__ void issue_chunk(int c, uint32_t (&mw)[C::MW]) {
     const int kbase = c * C::KC;
     const int rows = L - kbase < C::KC ? L - kbase : C::KC;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -109,13 +121,14 @@ struct KeyKernel {
     for (int u = 0; u < C::NI_W; ++u) {
       const int I = wave + C::W * u;
       if (C::NI % C::W == 0 || I < C::NI) {
-        const uint32_t off = full ? doff[u] : dma_offset(I, lane, rows);
+        // (offsets recomputed per chunk: registers are tight at 16 waves)
+        const uint32_t off = dma_offset(I, lane, full ? C::KC : rows);
         if (I < C::NI_T)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rk, (__attribute__((address_space(3))) void*)(sm.k[buf] + I * 1024), 16, off, 0, 0, 0);
+              rk, (__attribute__((address_space(3))) void*)(bufr<B>().k + I * 1024), 16, off, 0, 0, 0);
         else
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rv, (__attribute__((address_space(3))) void*)(sm.v[buf] + (I - C::NI_T) * 1024), 16,
+              rv, (__attribute__((address_space(3))) void*)(bufr<B>().v + (I - C::NI_T) * 1024), 16,
               off, 0, 0, 0);
       }
     }
@@ -149,7 +162,7 @@ struct KeyKernel {
     const int c0 = __builtin_popcountll(b0);
     const int count = c0 + __builtin_popcountll(b1);
     if (count == 0) return 0;
-    uint8_t* lst = sm.list[wave];
+    uint8_t* lst = ls.list[wave];
     if (keep[0]) lst[prefix_count64(b0)] = (uint8_t)lane;
     if (keep[1]) lst[c0 + prefix_count64(b1)] = (uint8_t)(lane + 64);
     const int first = b0 != 0ull ? __builtin_ctzll(b0) : 64 + __builtin_ctzll(b1);
@@ -164,17 +177,18 @@ struct KeyKernel {
   // values at d = n two transposing reads per d block deliver.  When
   // positions 16..31 are all padding (rem <= 16) the second score block is a
   // copy of the first.
-  __device__ __forceinline__ void pass(int buf, int q0, int rem) {
+  template <int B>
+  __device__ __forceinline__ void pass(int q0, int rem) {
     const bool single = rem <= 16;
     // keeps the ones operand in registers instead of rebuilding it per pass
     asm volatile("" : "+v"(ones));
-    const uint8_t* lst = sm.list[wave];
+    const uint8_t* lst = ls.list[wave];
     const uint32_t kk0 = lst[q0 + n], kk1 = lst[q0 + 16 + n];
     const int vp = q0 + 4 * g + (n >> 2);
     const uint32_t kv0 = lst[vp], kv1 = lst[vp + 16];
-    const uint32_t kb = lds_addr(sm.k[buf]) + (uint32_t)(16 * g);
-    const uint32_t ka0 = mad_u24(kk0, (uint32_t)C::RS, kb);
-    const uint32_t ka1 = mad_u24(kk1, (uint32_t)C::RS, kb);
+    const lds_cptr kb = to_lds(bufr<B>().k) + 16 * g;
+    const lds_cptr ka0 = kb + kk0 * C::RS;
+    const lds_cptr ka1 = kb + kk1 * C::RS;
     f32x4 s0 = nm4, s1 = nm4;
     // raised wave priority from the score MFMAs through the softmax (as in
     // the octet kernel)
@@ -182,13 +196,13 @@ struct KeyKernel {
     if (single) {
 #pragma unroll
       for (int sl = 0; sl < C::NSLAB; ++sl)
-        s0 = Mma<bf16_t>::mac8(lds_load<u32x4>(ka0 + 64 * sl), qf[sl], s0);
+        s0 = Mma<bf16_t>::mac8(lds_read16(ka0 + 64 * sl), qf[sl], s0);
       s1 = s0;
     } else {
 #pragma unroll
       for (int sl = 0; sl < C::NSLAB; ++sl) {
-        const u32x4 a0 = lds_load<u32x4>(ka0 + 64 * sl);
-        const u32x4 a1 = lds_load<u32x4>(ka1 + 64 * sl);
+        const u32x4 a0 = lds_read16(ka0 + 64 * sl);
+        const u32x4 a1 = lds_read16(ka1 + 64 * sl);
         s0 = Mma<bf16_t>::mac8(a0, qf[sl], s0);
         s1 = Mma<bf16_t>::mac8(a1, qf[sl], s1);
       }
@@ -196,16 +210,12 @@ struct KeyKernel {
     // V operands: lane (g, n) points at d = 4(n&3)..4(n&3)+3 of its V-side
     // key; the transposing read returns d = n of the group's four keys.
     constexpr int EARLY = C::NDB / 2 - 1;
-    const uint32_t vb = lds_addr(sm.v[buf]) + (uint32_t)(8 * (n & 3));
-    const uint32_t va0 = mad_u24(kv0, (uint32_t)C::RS, vb);
-    const uint32_t va1 = mad_u24(kv1, (uint32_t)C::RS, vb);
+    const lds_cptr vb = to_lds(bufr<B>().v) + 8 * (n & 3);
+    const lds_cptr va0 = vb + kv0 * C::RS;
+    const lds_cptr va1 = vb + kv1 * C::RS;
     u32x4 av[C::NDB];
     auto vread = [&](int j) {
-      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-      const u32x2 x = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(va0 + 32u * j)));
-      const u32x2 y = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(va1 + 32u * j)));
+      const u32x2 x = lds_read_tr16(va0 + 32 * j), y = lds_read_tr16(va1 + 32 * j);
       return u32x4{x[0], x[1], y[0], y[1]};
     };
 #pragma unroll
@@ -257,6 +267,20 @@ struct KeyKernel {
     oacc[C::NDB] = Mma<bf16_t>::mac8(ones, bop, oacc[C::NDB]);
   }
 
+  // Chunk c from buffer B while chunk c+1 loads into the other buffer.
+  template <int B>
+  __device__ __forceinline__ void chunk_step(int c, int n_chunks, bool act, int& count) {
+    const bool more = c + 1 < n_chunks;
+    uint32_t mwn[C::MW];
+    // buffer B^1 was last read in the previous step, which every wave has left
+    if (more) issue_chunk<B ^ 1>(c + 1, mwn);
+    if (act)
+      for (int q0 = 0; q0 < count; q0 += 32) pass<B>(q0, count - q0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c+1 have landed
+    if (act && more) count = make_list(c + 1, mwn);
+    __syncthreads();                // ... and every other wave's
+  }
+
   __device__ __forceinline__ void run() {
     const int tid = threadIdx.x;
     lane = tid & 63;
@@ -295,28 +319,16 @@ struct KeyKernel {
     thr = -INFINITY;
     ones = u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
 
-#pragma unroll
-    for (int u = 0; u < C::NI_W; ++u) {
-      const int I = wave + C::W * u;
-      doff[u] = I < C::NI ? dma_offset(I, lane, C::KC) : 0u;
-    }
     const int n_chunks = (L + C::KC - 1) / C::KC;
     uint32_t mw[C::MW];
-    issue_chunk(0, 0, mw);
+    issue_chunk<0>(0, mw);
     __builtin_amdgcn_s_waitcnt(0);
     int count = act ? make_list(0, mw) : 0;
     __syncthreads();
-    for (int c = 0; c < n_chunks; ++c) {
-      const int buf = c & 1;
-      const bool more = c + 1 < n_chunks;
-      // buffer buf^1 was last read in iteration c-1, which every wave has left
-      uint32_t mwn[C::MW];
-      if (more) issue_chunk(c + 1, buf ^ 1, mwn);
-      if (act)
-        for (int q0 = 0; q0 < count; q0 += 32) pass(buf, q0, count - q0);
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c+1 have landed
-      if (act && more) count = make_list(c + 1, mwn);
-      __syncthreads();                // ... and every other wave's
+    // two chunks per iteration, so that each step names its buffer statically
+    for (int c = 0; c < n_chunks; c += 2) {
+      chunk_step<0>(c, n_chunks, act, count);
+      if (c + 1 < n_chunks) chunk_step<1>(c + 1, n_chunks, act, count);
     }
 
     const int r = row0 + n;
@@ -342,8 +354,10 @@ template <int D, int N>
 __global__ __launch_bounds__(1024) void attn_key_kernel(AttnParams p) {
   static_assert(KeyCfg<D, N>::W == 16, "launch bounds: 16 waves");
   using K = KeyKernel<D, N>;
-  __shared__ __attribute__((aligned(16))) typename K::Smem sm;
-  K k(p, sm);
+  __shared__ __attribute__((aligned(16))) typename K::Buf b0;
+  __shared__ __attribute__((aligned(16))) typename K::Buf b1;
+  __shared__ __attribute__((aligned(16))) typename K::Lists lists;
+  K k(p, b0, b1, lists);
   k.run();
 }
 

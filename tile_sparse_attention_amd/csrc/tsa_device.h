@@ -106,6 +106,29 @@ __device__ __forceinline__ T lds_load(uint32_t a) {
   return *(const __attribute__((address_space(3))) T*)(uintptr_t)a;
 }
 
+// LDS reads through 32-bit pointers that keep the __shared__ object they
+// point into.  Direct global-to-LDS loads in flight write LDS behind the
+// compiler's back, so before an LDS read it waits for every such load it
+// cannot prove writes elsewhere; with double buffers as two separate objects
+// and reads through pointers into them, a read of one buffer does not wait
+// for the loads into the other.
+typedef const __attribute__((address_space(3))) uint8_t* lds_cptr;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ __forceinline__ lds_cptr to_lds(const uint8_t* p) { return (lds_cptr)p; }
+__device__ __forceinline__ u32x4 lds_read16(lds_cptr a) {
+  return *(const __attribute__((address_space(3))) u32x4*)a;
+}
+__device__ __forceinline__ u32x2 lds_read8(lds_cptr a) {
+  return *(const __attribute__((address_space(3))) u32x2*)a;
+}
+// Transposing read (16-bit elements): within each 16-lane group, lane s
+// points at 4 consecutive elements of row s>>2 of a 4-row block; lane n of
+// the group receives element n of each of the four rows (column n of the
+// 16-column block the four lanes of a row cover).
+__device__ __forceinline__ u32x2 lds_read_tr16(lds_cptr a) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a));
+}
+
 // a * b + c (24-bit operands, b wave-uniform) and (a << 4) + c as single
 // instructions; the compiler otherwise splits both into two.
 __device__ __forceinline__ uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c) {
