@@ -10,7 +10,7 @@ Only the tests, the smoke check and the CPU-baseline leg of the benchmark may
 import it.  It imports nothing from the GPU library, and the library never
 routes through it.
 
-Every function is pinned by tests/test_oracle.py (forward, compaction,
+Every function is pinned by tests/test_oracle.py (forward, compaction, mask diff,
 predictor, FLOP count) and tests/test_oracle_bwd.py (backward) against brute
 force or finite differences, closed
 forms, a library routine for the dense special case, invariants and
@@ -21,3 +21,4 @@ from .compaction import compact  # noqa: F401
 from .predictor import predict_mask, topk_count, pooled_scores  # noqa: F401
 from .flops import kept_flops  # noqa: F401
 from .backward import attention_bwd, attention_bwd_rows  # noqa: F401
+from .mask_reuse import mask_diff  # noqa: F401

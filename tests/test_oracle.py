@@ -398,6 +398,29 @@ def test_predictor_exact_k_with_many_ties():
     assert keep[0].tolist() == [False, True, True, True, False, False]
 
 
+def test_mask_diff_brute_force_and_invariants():
+    """Per-row count of differing keep bits j < T_k, by explicit bit loops."""
+    rng = np.random.default_rng(77)
+    for T_k in (1, 31, 32, 33, 70):
+        nw = -(-T_k // 32)
+        a = rng.integers(0, 2**32, size=(2, 3, 5, nw), dtype=np.uint64).astype(np.uint32)
+        b = rng.integers(0, 2**32, size=(2, 3, 5, nw), dtype=np.uint64).astype(np.uint32)
+        rows, heads = oracle.mask_diff(a, b, T_k)
+        for idx in np.ndindex(2, 3, 5):
+            n = 0
+            for j in range(T_k):
+                wa, wb = int(a[idx + (j // 32,)]), int(b[idx + (j // 32,)])
+                n += ((wa >> (j % 32)) & 1) != ((wb >> (j % 32)) & 1)
+            assert rows[idx] == n
+        assert np.array_equal(heads, rows.sum(axis=-1))
+        # identity, full flip (padding bits are not decisions), symmetry, triangle inequality
+        assert not oracle.mask_diff(a, a, T_k)[0].any()
+        assert np.all(oracle.mask_diff(a, ~a, T_k)[0] == T_k)
+        assert np.array_equal(oracle.mask_diff(b, a, T_k)[0], rows)
+        c = rng.integers(0, 2**32, size=a.shape, dtype=np.uint64).astype(np.uint32)
+        assert np.all(rows <= oracle.mask_diff(a, c, T_k)[0] + oracle.mask_diff(c, b, T_k)[0])
+
+
 # --------------------------------------------------------------------------
 # mutation tests: planted mistakes must be caught by the pins above
 # --------------------------------------------------------------------------
@@ -456,3 +479,15 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
             return orig_keep(bits, L, M, M, rows)
         monkeypatch.setattr(oatt, "keep_matrix", keep_matrix)
     assert not _pins_pass(), f"planted mistake {mutation!r} went unnoticed"
+
+
+def test_mask_diff_planted_mistake_is_caught(monkeypatch):
+    """Counting the padding bits past T_k (a plausible slip) fails the pins."""
+    real = oracle.mask_diff
+
+    def counts_padding(a_bits, b_bits, T_k):
+        return real(a_bits, b_bits, np.asarray(a_bits).shape[-1] * 32)
+
+    monkeypatch.setattr(oracle, "mask_diff", counts_padding)
+    with pytest.raises(AssertionError):
+        test_mask_diff_brute_force_and_invariants()
