@@ -217,6 +217,46 @@ def bench_backward(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws)
     print(json.dumps(rec), flush=True)
 
 
+def bench_mask_diff(args, w, name):
+    """One step = one tsa_mask_diff call between two masks of the workload
+    (the workload's own and one drawn with another seed), both resident in HBM:
+    per-row and per-head counts of differing keep decisions."""
+    import numpy as np
+    import torch
+
+    import tile_sparse_attention_amd as T
+    import workloads as W
+    w2 = W.Workload(w.name + "_next", w.B, w.H, w.L, w.d, w.M, w.N, w.dtype, w.mask, w.seed + 1000)
+    a = torch.from_numpy(np.ascontiguousarray(W.mask_bits(w)).view(np.int32)).cuda()
+    b = torch.from_numpy(np.ascontiguousarray(W.mask_bits(w2)).view(np.int32)).cuda()
+    rows = torch.empty(a.shape[:3], dtype=torch.int64, device="cuda")
+    heads = torch.empty(a.shape[:2], dtype=torch.int64, device="cuda")
+    pr = T.problem(w.B, w.H, w.L, 0, w.M, w.N)
+    lib = T.lib()
+
+    def step():
+        T._check(lib.tsa_mask_diff(T.ctypes.byref(pr), T._ptr(a), T._ptr(b), T._ptr(rows), T._ptr(heads),
+                                   T._stream()))
+
+    ms_step, ms_call, ms_min = time_calls(step, args.steps, args.warmup)
+    nbytes = 2 * a.numel() * 4 + rows.numel() * 8 * 2 + heads.numel() * 8
+    gbs = nbytes / (ms_call * 1e-3) / 1e9
+    changed = int(heads.sum())
+    log(f"mask diff: {ms_step:.4f} ms/step, call mean {ms_call:.4f} ms, {gbs:.0f} GB/s, "
+        f"{changed} of {a.shape[0] * a.shape[1] * a.shape[2] * w.T_k} decisions differ")
+    rec = {"metric": "mask diff HBM throughput (two keep-bitmaps in, per-row and per-head counts out)",
+           "value": round(nbytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
+           "data": "synthetic (two seeded masks of the workload)",
+           "config": {"workload": name, "B": w.B, "H": w.H, "L": w.L, "M": w.M, "N": w.N,
+                      "bitmap_bytes": a.numel() * 4, "changed_decisions": changed},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                        "frac": round(gbs / 8000.0, 4), "traffic": None,
+                        "kernel": "diff_rows_kernel + diff_heads_kernel"}}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +268,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dQ, dK, dV) of the workload instead and print "
                          "its own JSON line")
+    ap.add_argument("--mask-diff", action="store_true",
+                    help="time tsa_mask_diff between the workload's mask and a reseeded one (mask reuse "
+                         "across denoising steps) and print its own JSON line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run one plain device copy of BYTES bytes (calibrates the HBM "
                          "byte counters of a profiler run) and exit")
@@ -253,6 +296,9 @@ def main():
         return
     name = args.workload or W.HEADLINE
     w = W.get(name)
+    if args.mask_diff:
+        bench_mask_diff(args, w, name)
+        return
     log(f"workload {name}: B={w.B} H={w.H} L={w.L} d={w.d} M={w.M} N={w.N} {w.dtype}")
     t0 = time.perf_counter()
     q, k, v = W.make_qkv(w)

@@ -118,6 +118,17 @@ tsa_status_t tsa_attention_bwd(const tsa_problem_t* p,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* Difference of two keep-bitmaps of problem p, for reusing a predicted mask
+ * across denoising steps (FG-Attn abstract: one keep decision per M x N tile):
+ * row_changed[(b*H + h)*T_q + i] = number of key tiles j < T_k whose keep bit
+ * differs between mask_a and mask_b in row (b, h, i) (padding bits ignored);
+ * head_changed[b*H + h] = the sum over the head's rows (NULL skips it).
+ * mask_a, mask_b: [B,H,T_q,W] uint32 device arrays (read only; they may be
+ * the same).  row_changed: [B*H*T_q] int64, head_changed: [B*H] int64, device,
+ * written in full, 8-byte aligned.  No workspace; d and dtype are not read. */
+tsa_status_t tsa_mask_diff(const tsa_problem_t* p, const uint32_t* mask_a, const uint32_t* mask_b,
+                           int64_t* row_changed, int64_t* head_changed, void* stream);
+
 /* Mask compaction (FG-Attn abstract: one skip decision per M x N tile): every
  * bitmap row (b,h,i) becomes the ascending list of its kept key tiles j < T_k.
  * row_ptr: [B*H*T_q + 1] int64, rows in (b,h,i) row-major order, row_ptr[0]=0,

@@ -125,6 +125,21 @@ def test_backward_workspace_and_validation():
     assert _bwd(small, ws=(ctypes.c_void_p(0x900010), need)) == T.ERR_WORKSPACE_TOO_SMALL  # misaligned
 
 
+def test_mask_diff_validation():
+    lib = T.lib()
+    p = lambda x: ctypes.c_void_p(x)  # noqa: E731  (fake, never dereferenced: every call below fails checks)
+    pr = T.problem(1, 2, 512, 0, 16, 8)
+    assert lib.tsa_mask_diff(ctypes.byref(pr), p(0), p(0x20000), p(0x30000), None, None) == T.ERR_INVALID_ARGUMENT
+    assert lib.tsa_mask_diff(ctypes.byref(pr), p(0x10000), p(0x20000), p(0), None, None) == T.ERR_INVALID_ARGUMENT
+    assert lib.tsa_mask_diff(ctypes.byref(pr), p(0x10002), p(0x20000), p(0x30000), None, None) \
+        == T.ERR_INVALID_ARGUMENT
+    assert lib.tsa_mask_diff(ctypes.byref(pr), p(0x10000), p(0x20000), p(0x30004), None, None) \
+        == T.ERR_INVALID_ARGUMENT
+    bad = T.problem(1, 2, 512, 0, 8, 8)
+    assert lib.tsa_mask_diff(ctypes.byref(bad), p(0x10000), p(0x20000), p(0x30000), None, None) \
+        == T.ERR_UNSUPPORTED
+
+
 def test_compact_and_predict_validation():
     lib = T.lib()
     pr = T.problem(1, 2, 512, 64, 16, 16)

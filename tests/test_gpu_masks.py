@@ -147,3 +147,41 @@ def test_structured_maskgen_full_config_sampled():
     rng = np.random.default_rng(3)
     rows = [(0, h, i) for h in range(w.H) for i in {0, w.T_q - 1, int(rng.integers(w.T_q))}]
     assert np.array_equal(_rows_of(m, rows), W.pack_bits(W.mask_rows_bool(w, rows)))
+
+
+@pytest.mark.parametrize("L,M,N", [(1000, 16, 8), (777, 32, 1), (4000, 64, 64), (50, 16, 16), (129, 16, 2)])
+def test_mask_diff_bit_exact(L, M, N):
+    import tile_sparse_attention_amd as T
+    torch = torch_or_skip()
+    rng = np.random.default_rng(L + M + N)
+    T_q, T_k = -(-L // M), -(-L // N)
+    words = -(-T_k // 32)
+    # random words, padding bits included: they must not count
+    a = rng.integers(0, 2**32, size=(2, 3, T_q, words), dtype=np.uint64).astype(np.uint32)
+    flip = rng.random(a.shape) < 0.3
+    b = np.where(flip, a ^ rng.integers(0, 2**32, size=a.shape, dtype=np.uint64).astype(np.uint32), a)
+    say(f"mask diff L={L} M={M} N={N} words={words}")
+    rows, heads = T.mask_diff(to_dev_mask(a), to_dev_mask(b), L, M, N)
+    torch.cuda.synchronize()
+    r_ref, h_ref = oracle.mask_diff(a, b, T_k)
+    assert np.array_equal(rows.cpu().numpy(), r_ref)
+    assert np.array_equal(heads.cpu().numpy(), h_ref)
+    same, _ = T.mask_diff(to_dev_mask(a), to_dev_mask(a), L, M, N)
+    assert int(same.abs().max()) == 0
+
+
+def test_mask_diff_wan480_fine_consecutive_masks():
+    """Two masks of the 16x8 workload drawn with different seeds (a stand-in
+    for masks predicted at two denoising steps): every row and head count
+    equals the oracle's."""
+    import tile_sparse_attention_amd as T
+    torch = torch_or_skip()
+    w = W.get("wan480_fine")
+    w2 = W.Workload(w.name + "_next", w.B, w.H, w.L, w.d, w.M, w.N, w.dtype, w.mask, w.seed + 1000)
+    a, b = W.mask_bits(w), W.mask_bits(w2)
+    say("mask diff wan480_fine vs reseeded")
+    rows, heads = T.mask_diff(to_dev_mask(a), to_dev_mask(b), w.L, w.M, w.N)
+    torch.cuda.synchronize()
+    r_ref, h_ref = oracle.mask_diff(a, b, w.T_k)
+    assert np.array_equal(rows.cpu().numpy(), r_ref)
+    assert np.array_equal(heads.cpu().numpy(), h_ref)

@@ -65,6 +65,7 @@ _SIGS = {
     "tsa_maskgen_hash": (ctypes.c_int, [_PP, ctypes.POINTER(MaskgenParams), _VP, _VP]),
     "tsa_maskgen_structured": (ctypes.c_int, [_PP, ctypes.POINTER(StructuredParams),
                                               ctypes.POINTER(ctypes.c_int32), _VP, _VP]),
+    "tsa_mask_diff": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP]),
     "tsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tsa_last_error": (ctypes.c_char_p, []),
 }
@@ -211,6 +212,26 @@ def attention_bwd(q, k, v, o, do, lse, mask_bits, M: int, N: int, scale: float |
                                    _ptr(lse), _ptr(mask_bits), ctypes.c_float(scale), _ptr(dq),
                                    _ptr(dk), _ptr(dv), _ptr(ws), nws, _stream()))
     return dq, dk, dv
+
+
+def mask_diff(mask_a, mask_b, L: int, M: int, N: int):
+    """(row_changed int64 [B, H, T_q], head_changed int64 [B, H]): per bitmap row
+    and per head, the number of key tiles whose keep bit differs between two
+    masks [B, H, T_q, words] of one problem."""
+    torch = _torch()
+    _need_cuda(mask_a, mask_b)
+    B, H, T_q, words = mask_a.shape
+    if tuple(mask_b.shape) != tuple(mask_a.shape) or words != mask_row_words(L, N) or T_q != -(-L // M):
+        raise TsaError(ERR_INVALID_ARGUMENT, "masks must both be [B, H, T_q, words] of the problem")
+    for m in (mask_a, mask_b):
+        if m.dtype not in (torch.int32, torch.uint32):
+            raise TsaError(ERR_INVALID_ARGUMENT, "masks must be int32/uint32")
+    rows = torch.empty((B, H, T_q), dtype=torch.int64, device=mask_a.device)
+    heads = torch.empty((B, H), dtype=torch.int64, device=mask_a.device)
+    pr = Problem(B, H, L, 0, M, N, DTYPE_BF16)
+    _check(lib().tsa_mask_diff(ctypes.byref(pr), _ptr(mask_a), _ptr(mask_b), _ptr(rows), _ptr(heads),
+                               _stream()))
+    return rows, heads
 
 
 def mask_compact(mask_bits, L: int, M: int, N: int, col_capacity: int | None = None):

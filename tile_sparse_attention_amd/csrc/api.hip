@@ -25,6 +25,8 @@ hipError_t launch_maskgen_structured(const tsa_problem_t* p, const tsa_structure
                                      const int32_t* head_pattern, uint32_t* out, hipStream_t stream);
 hipError_t launch_maskgen_hash(const tsa_problem_t* p, const tsa_maskgen_params_t* g,
                                uint32_t* out, hipStream_t stream);
+hipError_t launch_mask_diff(const tsa_problem_t* p, const uint32_t* a, const uint32_t* b, int64_t* rows_out,
+                            int64_t* heads_out, hipStream_t stream);
 }  // namespace tsa
 
 namespace {
@@ -165,6 +167,22 @@ tsa_status_t tsa_attention_bwd(const tsa_problem_t* p, const void* q, const void
                    static_cast<hipStream_t>(stream)};
   const hipError_t e = tsa::launch_attention_bwd(a);
   if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
+  return TSA_OK;
+}
+
+tsa_status_t tsa_mask_diff(const tsa_problem_t* p, const uint32_t* mask_a, const uint32_t* mask_b,
+                           int64_t* row_changed, int64_t* head_changed, void* stream) {
+  tsa_status_t s = check_problem(p, false);
+  if (s != TSA_OK) return s;
+  if (!mask_a || !mask_b || !row_changed)
+    return fail(TSA_ERR_INVALID_ARGUMENT, "mask_a, mask_b and row_changed must be non-NULL");
+  if (!aligned(mask_a, 4) || !aligned(mask_b, 4) || !aligned(row_changed, 8) ||
+      (head_changed && !aligned(head_changed, 8)))
+    return fail(TSA_ERR_INVALID_ARGUMENT, "masks need 4-byte, counts 8-byte alignment");
+  if ((n_rows(p) + 3) / 4 > kMaxGrid) return fail(TSA_ERR_UNSUPPORTED, "grid too large");
+  const hipError_t e = tsa::launch_mask_diff(p, mask_a, mask_b, row_changed, head_changed,
+                                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mask diff launch");
   return TSA_OK;
 }
 
