@@ -22,3 +22,4 @@ from .predictor import predict_mask, topk_count, pooled_scores  # noqa: F401
 from .flops import kept_flops  # noqa: F401
 from .backward import attention_bwd, attention_bwd_rows  # noqa: F401
 from .mask_reuse import mask_diff  # noqa: F401
+from . import fp8  # noqa: F401
