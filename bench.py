@@ -217,6 +217,42 @@ def bench_backward(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws)
     print(json.dumps(rec), flush=True)
 
 
+def bench_fp8(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws):
+    """One step = one tsa_attention_fwd_fp8 call (Q, K already quantised to e4m3
+    and resident in HBM); the quantisation is timed on its own."""
+    import torch
+
+    import tile_sparse_attention_amd as T
+    if w.dtype != "bf16" or w.d != 128 or w.N < 8:
+        raise SystemExit("the FP8 path takes bf16, d = 128, N >= 8")
+    q8, qs, k8, ks = T.quantize_qk_fp8(qd, kd)
+    torch.cuda.synchronize()
+    qms, qcall, _ = time_calls(lambda: T.quantize_qk_fp8(qd, kd), args.steps, args.warmup)
+
+    def step():
+        T.attention_fwd_fp8(q8, k8, qs, ks, vd, mask, w.M, w.N, w.scale, out=out, workspace=ws)
+
+    ms_step, ms_kernel, ms_min = time_calls(step, args.steps, args.warmup)
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    # half of the kept FLOPs (QK^T) run at the FP8 peak, half (PV) at the bf16 peak
+    peak = 2.0 / (1.0 / 5000.0 + 1.0 / PEAK_TFLOPS["bf16"])
+    log(f"fp8 scores: {ms_step:.3f} ms/step, kernel mean {ms_kernel:.3f} ms, {tflops:.1f} TFLOP/s; "
+        f"quantisation {qcall:.3f} ms")
+    cfg = {"workload": name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "M": w.M, "N": w.N,
+           "mask": w.description, "kept_fraction": round(flops / dense_flops, 6), "kept_flops": flops,
+           "quantise_ms": round(qcall, 4), "peak_tflops": round(peak, 1)}
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
+    rec = {"metric": "FP8-score kept-tile effective TFLOPS (QK^T on e4m3 with per-tile scales, PV bf16)",
+           "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3 scores, bf16 PV",
+           "data": "synthetic (seeded normal Q/K/V, generated masks)", "config": cfg,
+           "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+                        "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                        "kernel": "attn_oct_kernel (FP8 scores)"}}
+    print(json.dumps(rec), flush=True)
+
+
 def bench_mask_diff(args, w, name):
     """One step = one tsa_mask_diff call between two masks of the workload
     (the workload's own and one drawn with another seed), both resident in HBM:
@@ -268,6 +304,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dQ, dK, dV) of the workload instead and print "
                          "its own JSON line")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the FP8-score forward (tsa_attention_fwd_fp8) of the workload, and the "
+                         "quantisation of Q and K separately, and print its own JSON line")
     ap.add_argument("--mask-diff", action="store_true",
                     help="time tsa_mask_diff between the workload's mask and a reseeded one (mask reuse "
                          "across denoising steps) and print its own JSON line")
@@ -317,6 +356,9 @@ def main():
 
     if args.backward:
         bench_backward(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws)
+        return
+    if args.fp8:
+        bench_fp8(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws)
         return
 
     def step():

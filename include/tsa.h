@@ -94,6 +94,35 @@ tsa_status_t tsa_attention_fwd(const tsa_problem_t* p,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* FP8 inputs of tsa_attention_fwd_fp8: q and k (bf16 [B,H,L,128]) as e4m3
+ * bytes (OCP format: 4 exponent bits, bias 7, 3 mantissa bits, largest value
+ * 448) with per-tile scales: q_scale [B,H,ceil(L/16)] fp32, one per 16-row tile
+ * of a head, and k_scale [B,H] fp32, one per head.  A scale is the tile's
+ * largest |x| / 448 (1 for an all-zero tile); a value becomes the e4m3 number
+ * nearest to x / scale, ties to even.  q8, k8: [B,H,L,128] bytes.  p->dtype must
+ * be bf16 and p->d 128; M and N are not read.  No workspace.  The quantisation
+ * is this library's reading of the per-tile scaling named beside the pages'
+ * method (FG-Attn itself fixes no precision). */
+tsa_status_t tsa_quantize_qk_fp8(const tsa_problem_t* p, const void* q, const void* k,
+                                 uint8_t* q8, float* q_scale, uint8_t* k8, float* k_scale,
+                                 void* stream);
+
+/* tsa_attention_fwd with FP8 scores (FG-Attn abstract: scores skipped per
+ * M x N tile, skipped scores excluded from the softmax): the scores are
+ * scale * (q8 . k8) * q_scale[tile of r] * k_scale[head], computed on the
+ * 16x16x128 FP8 matrix cores; V, the probabilities and O are bf16 as in
+ * tsa_attention_fwd.  q8, k8, q_scale, k_scale as tsa_quantize_qk_fp8 writes
+ * them; v, mask_bits, o, lse, scale and the workspace
+ * (tsa_workspace_size(TSA_OP_ATTENTION_FWD)) as in tsa_attention_fwd.
+ * Supported: p->dtype bf16, d = 128, M in {16, 32, 64}, N in {8, 16, 32, 64};
+ * other shapes return TSA_ERR_UNSUPPORTED. */
+tsa_status_t tsa_attention_fwd_fp8(const tsa_problem_t* p,
+                                   const uint8_t* q8, const uint8_t* k8,
+                                   const float* q_scale, const float* k_scale,
+                                   const void* v, const uint32_t* mask_bits, float scale,
+                                   void* o, float* lse,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Gradients of tsa_attention_fwd's output with respect to q, k and v, for an
  * upstream gradient d_o.  The pages define only the forward (FG-Attn abstract:
  * skipped M x N tiles excluded from the softmax); this is its derivative by the

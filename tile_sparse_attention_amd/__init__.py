@@ -66,6 +66,9 @@ _SIGS = {
     "tsa_maskgen_structured": (ctypes.c_int, [_PP, ctypes.POINTER(StructuredParams),
                                               ctypes.POINTER(ctypes.c_int32), _VP, _VP]),
     "tsa_mask_diff": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP]),
+    "tsa_quantize_qk_fp8": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "tsa_attention_fwd_fp8": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP,
+                                             _VP, ctypes.c_size_t, _VP]),
     "tsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tsa_last_error": (ctypes.c_char_p, []),
 }
@@ -176,6 +179,56 @@ def attention_fwd(q, k, v, mask_bits, M: int, N: int, scale: float | None = None
     _check(lib().tsa_attention_fwd(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(mask_bits),
                                    ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(ws), nws,
                                    _stream()))
+    return (out, lse) if return_lse else out
+
+
+def quantize_qk_fp8(q, k):
+    """(q8 uint8, q_scale float32 [B, H, ceil(L/16)], k8 uint8, k_scale float32 [B, H])
+    of bf16 q, k [B, H, L, 128]: e4m3 bytes with per-tile scales."""
+    torch = _torch()
+    _need_cuda(q, k)
+    B, H, L, d = q.shape
+    if k.shape != q.shape or q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
+        raise TsaError(ERR_INVALID_ARGUMENT, "q, k must be bf16 of one shape")
+    q8 = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
+    k8 = torch.empty(k.shape, dtype=torch.uint8, device=q.device)
+    qs = torch.empty((B, H, -(-L // 16)), dtype=torch.float32, device=q.device)
+    ks = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    pr = Problem(B, H, L, d, 16, 16, DTYPE_BF16)
+    _check(lib().tsa_quantize_qk_fp8(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks),
+                                     _stream()))
+    return q8, qs, k8, ks
+
+
+def attention_fwd_fp8(q8, k8, q_scale, k_scale, v, mask_bits, M: int, N: int, scale: float | None = None, *,
+                      out=None, return_lse: bool = False, workspace=None):
+    """O (and optionally LSE) of tile-sparse attention with FP8 scores: q8, k8
+    and the scales as quantize_qk_fp8 returns them, v bf16 [B, H, L, 128]."""
+    torch = _torch()
+    B, H, L, d = v.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(v)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device=v.device) if return_lse else None
+    _need_cuda(q8, k8, q_scale, k_scale, v, mask_bits, out, lse)
+    if q8.shape != v.shape or k8.shape != v.shape or q8.dtype != torch.uint8 or k8.dtype != torch.uint8:
+        raise TsaError(ERR_INVALID_ARGUMENT, "q8, k8 must be uint8 of v's shape")
+    if tuple(q_scale.shape) != (B, H, -(-L // 16)) or tuple(k_scale.shape) != (B, H):
+        raise TsaError(ERR_INVALID_ARGUMENT, "q_scale [B, H, ceil(L/16)], k_scale [B, H] float32")
+    T_q = -(-L // M)
+    if mask_bits.dtype not in (torch.int32, torch.uint32) or \
+            tuple(mask_bits.shape) != (B, H, T_q, mask_row_words(L, N)):
+        raise TsaError(ERR_INVALID_ARGUMENT, "mask_bits must be int32/uint32 [B, H, T_q, words]")
+    pr = Problem(B, H, L, d, M, N, DTYPE_BF16)
+    if workspace is None:
+        ws, nws = _workspace(OP_ATTENTION_FWD, pr, v.device)
+    else:
+        _need_cuda(workspace)
+        ws, nws = workspace, workspace.numel() * workspace.element_size()
+    _check(lib().tsa_attention_fwd_fp8(ctypes.byref(pr), _ptr(q8), _ptr(k8), _ptr(q_scale), _ptr(k_scale),
+                                       _ptr(v), _ptr(mask_bits), ctypes.c_float(scale), _ptr(out), _ptr(lse),
+                                       _ptr(ws), nws, _stream()))
     return (out, lse) if return_lse else out
 
 

@@ -33,7 +33,7 @@ CFLAGS = [
 # Per-source extra flags.  The bf16 attention kernels never see NaN scores
 # (finite inputs), and without NaN handling a running max over MFMA results
 # compiles to three-way max instructions with no operand quieting.
-EXTRA = {"attention_fwd_bf16.hip": ["-fno-honor-nans"], "attention_bwd.hip": ["-fno-honor-nans"]}
+EXTRA = {name: ["-fno-honor-nans"] for name in ("attention_fwd_bf16.hip", "attention_fwd_fp8.hip", "attention_bwd.hip")}
 
 
 def _flags(src: str) -> list:
@@ -53,7 +53,7 @@ def _compile(src: str) -> str:
     return obj
 
 
-SPILL_CHECKED = ("attention_fwd_bf16.hip", "attention_fwd_f32.hip", "attention_bwd.hip")
+SPILL_CHECKED = ("attention_fwd_bf16.hip", "attention_fwd_f32.hip", "attention_fwd_fp8.hip", "attention_bwd.hip")
 
 
 def _check_no_spills(src: str) -> None:

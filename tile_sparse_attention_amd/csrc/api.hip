@@ -139,6 +139,55 @@ tsa_status_t tsa_attention_fwd(const tsa_problem_t* p, const void* q, const void
   return TSA_OK;
 }
 
+tsa_status_t tsa_quantize_qk_fp8(const tsa_problem_t* p, const void* q, const void* k, uint8_t* q8,
+                                 float* q_scale, uint8_t* k8, float* k_scale, void* stream) {
+  tsa_status_t s = check_problem(p, true);
+  if (s != TSA_OK) return s;
+  if (p->dtype != TSA_DTYPE_BF16 || p->d != 128)
+    return fail(TSA_ERR_UNSUPPORTED, "FP8 quantisation takes bf16 q, k with d = 128");
+  if (!q || !k || !q8 || !q_scale || !k8 || !k_scale)
+    return fail(TSA_ERR_INVALID_ARGUMENT, "q, k, q8, q_scale, k8 and k_scale must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q8, 16) || !aligned(k8, 16) || !aligned(q_scale, 4) ||
+      !aligned(k_scale, 4))
+    return fail(TSA_ERR_INVALID_ARGUMENT, "tensors need 16-byte, scales 4-byte alignment");
+  if ((long long)p->B * p->H * (long long)p->L * 16 / 256 > kMaxGrid)
+    return fail(TSA_ERR_UNSUPPORTED, "grid too large");
+  const hipError_t e = tsa::launch_quantize_qk_fp8(p, q, k, q8, q_scale, k8, k_scale,
+                                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "FP8 quantisation launch");
+  return TSA_OK;
+}
+
+tsa_status_t tsa_attention_fwd_fp8(const tsa_problem_t* p, const uint8_t* q8, const uint8_t* k8,
+                                   const float* q_scale, const float* k_scale, const void* v,
+                                   const uint32_t* mask_bits, float scale, void* o, float* lse,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  tsa_status_t s = check_problem(p, true);
+  if (s != TSA_OK) return s;
+  if (p->dtype != TSA_DTYPE_BF16 || p->d != 128 || p->N < 8)
+    return fail(TSA_ERR_UNSUPPORTED, "FP8 attention: bf16 v/o, d = 128 and N >= 8 (got d=%d N=%d)", p->d, p->N);
+  if (!q8 || !k8 || !q_scale || !k_scale || !v || !mask_bits || !o)
+    return fail(TSA_ERR_INVALID_ARGUMENT, "q8, k8, q_scale, k_scale, v, mask_bits and o must be non-NULL");
+  if (!std::isfinite(scale)) return fail(TSA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(mask_bits, 4) ||
+      !aligned(q_scale, 4) || !aligned(k_scale, 4) || (lse && !aligned(lse, 4)))
+    return fail(TSA_ERR_INVALID_ARGUMENT, "q8/k8/v/o need 16-byte, mask/scales/lse 4-byte alignment");
+  if (o == v || o == (const void*)q8 || o == (const void*)k8)
+    return fail(TSA_ERR_INVALID_ARGUMENT, "o aliases an input");
+  const size_t need = tsa::attention_workspace_bytes(p);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(TSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, 256-byte aligned (got %zu)",
+                need, workspace_bytes);
+  const long long blocks = (long long)p->B * p->H * ((p->L + 63) / 64);
+  if (blocks > kMaxGrid) return fail(TSA_ERR_UNSUPPORTED, "grid too large");
+  tsa::AttnLaunch a{p, q8, k8, v, mask_bits, scale, o, lse, workspace, static_cast<hipStream_t>(stream)};
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  const hipError_t e = tsa::launch_attention_fp8(a);
+  if (e != hipSuccess) return hip_fail(e, "FP8 attention kernel launch");
+  return TSA_OK;
+}
+
 tsa_status_t tsa_attention_bwd(const tsa_problem_t* p, const void* q, const void* k, const void* v,
                                const void* o, const void* d_o, const float* lse,
                                const uint32_t* mask_bits, float scale, void* dq, void* dk, void* dv,

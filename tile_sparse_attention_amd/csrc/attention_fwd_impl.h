@@ -67,6 +67,10 @@ struct AttnParams {
   const uint32_t* need;
   const uint32_t* need_flag;
   const uint32_t* need_count;
+  // FP8 scores (q and k hold e4m3 bytes): per (b, h) ceil(L/16) Q tile scales
+  // and one K scale (null otherwise)
+  const float* q_scale;
+  const float* k_scale;
 };
 
 template <typename T> struct ElemTraits;

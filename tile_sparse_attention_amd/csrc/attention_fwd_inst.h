@@ -30,6 +30,8 @@ inline AttnParams attn_params(const AttnLaunch& a, int rows_per_block) {
   p.need = nullptr;
   p.need_flag = nullptr;
   p.need_count = nullptr;
+  p.q_scale = a.q_scale;
+  p.k_scale = a.k_scale;
   return p;
 }
 
@@ -54,14 +56,14 @@ hipError_t launch_attn_cfg(const AttnLaunch& a) {
 // With chunk skipping (at most kMaxChunks chunks), chunk_need_kernel first
 // sorts the work-groups into those that need nearly every chunk (run by the
 // plain kernel) and the rest (run by the skipping kernel).
-template <int D, int N>
+template <int D, int N, bool F8 = false>
 hipError_t launch_attn_oct(const AttnLaunch& a) {
-  using C = OctCfg<D, N>;
+  using C = OctCfg<D, N, F8>;
   AttnParams p = attn_params(a, C::ROWS);
   const long long blocks = (long long)a.p->B * a.p->H * p.n_qblocks;
   launch_vt_pack<bf16_t, D>(a, p);
   if (!attention_skips_chunks(a.p)) {
-    hipLaunchKernelGGL((attn_oct_kernel<D, N, false>), dim3((unsigned)blocks), dim3(64 * C::W), 0,
+    hipLaunchKernelGGL((attn_oct_kernel<D, N, false, F8>), dim3((unsigned)blocks), dim3(64 * C::W), 0,
                        a.stream, p);
     return hipGetLastError();
   }
@@ -75,8 +77,10 @@ hipError_t launch_attn_oct(const AttnLaunch& a) {
   hipLaunchKernelGGL(zero_word_kernel<uint32_t>, dim3(1), dim3(64), 0, a.stream, count);
   hipLaunchKernelGGL((chunk_need_kernel<N>), dim3((unsigned)blocks), dim3(256), 0, a.stream, p, need, flag,
                      count);
-  hipLaunchKernelGGL((attn_oct_kernel<D, N, false>), dim3((unsigned)blocks), dim3(64 * C::W), 0, a.stream, p);
-  hipLaunchKernelGGL((attn_oct_kernel<D, N, true>), dim3((unsigned)blocks), dim3(64 * C::W), 0, a.stream, p);
+  hipLaunchKernelGGL((attn_oct_kernel<D, N, false, F8>), dim3((unsigned)blocks), dim3(64 * C::W), 0, a.stream,
+                     p);
+  hipLaunchKernelGGL((attn_oct_kernel<D, N, true, F8>), dim3((unsigned)blocks), dim3(64 * C::W), 0, a.stream,
+                     p);
   return hipGetLastError();
 }
 

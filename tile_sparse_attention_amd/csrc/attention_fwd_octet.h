@@ -50,7 +50,7 @@
 
 namespace tsa {
 
-template <int D, int N>
+template <int D, int N, bool F8 = false>
 struct OctCfg {
   static constexpr int KC = 128;                   // keys per chunk
   static constexpr int W = 16;                     // waves per work-group
@@ -58,9 +58,12 @@ struct OctCfg {
   static constexpr int OPC = KC / 8;               // octets per chunk
   static constexpr int TPC = KC / N;               // key tiles per chunk (<= 16)
   static constexpr int LOG2R = ilog2(N / 8);       // octets per key tile, log2
-  static constexpr int NSLAB = D / 32;             // 32-wide d slabs of the QK^T contraction
+  // Q/K elements: bf16, or FP8 (e4m3) whose 16x16x128 matrix-core step
+  // takes a whole 128-wide d range: then the Q fragment is two 16-byte halves
+  static constexpr int ESZ = F8 ? 1 : 2;           // bytes per Q / K element
+  static constexpr int NSLAB = F8 ? 2 : D / 32;    // 32-wide d slabs of the QK^T contraction
   static constexpr int NDB = D / 16;               // 16-wide d blocks of O^T
-  static constexpr int KRB = D * 2;                // K row bytes in memory
+  static constexpr int KRB = D * ESZ;              // K row bytes in memory
   // K row stride in LDS: with 32 padding bytes, the 16 key rows of a score
   // block (two octets, eight consecutive rows each) read 16 bytes per lane
   // without bank conflicts whatever the octets; V^T rows take 16 padding
@@ -76,6 +79,7 @@ struct OctCfg {
   static constexpr int NI_W = (NI + W - 1) / W;
   static_assert(N >= 8 && N <= 64 && (N & (N - 1)) == 0, "octet kernel: N in {8,16,32,64}");
   static_assert(D % 32 == 0, "head dim");
+  static_assert(!F8 || D == 128, "FP8 scores: d = 128 (one 16x16x128 step)");
   static_assert(TPC <= 16, "tile bits of a chunk fit one mask word");
 };
 
@@ -119,12 +123,22 @@ __device__ __forceinline__ uint32_t octet_mask(uint32_t tb) {
   }
 }
 
+// One 16x16x128 FP8 (e4m3) matrix-core step, block scales 2^0: lane (g, n)
+// supplies 32 bytes of A's row n and of B's column n (a0|a1, b0|b1), the
+// same 32 k positions of the contraction in both.
+__device__ __forceinline__ f32x4 mac_fp8(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x4 c) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 // SKIP: the work-group visits only the chunks its bitmap marks as needed
 // (work-groups flagged by chunk_need_kernel); otherwise every chunk (the
 // work-groups not flagged).
-template <int D, int N, bool SKIP>
+template <int D, int N, bool SKIP, bool F8 = false>
 struct OctKernel {
-  using C = OctCfg<D, N>;
+  using C = OctCfg<D, N, F8>;
   static constexpr float RESCALE_STEP = 8.f;  // log2 units the max may grow before rescaling
 
   struct SmemPlain {
@@ -139,7 +153,7 @@ struct OctKernel {
   const AttnParams& p;
   Smem& sm;
   int lane, g, n, wave, L;
-  const bf16_t* __restrict__ kg;
+  const uint8_t* __restrict__ kg;   // K rows of this (b, h), bytes
   const bf16_t* __restrict__ vtg;
   const uint32_t* __restrict__ mrow;
   u32x4 qf[C::NSLAB];
@@ -176,7 +190,7 @@ struct OctKernel {
     const int kbase = c * C::KC;
     const int rows = L - kbase < C::KC ? L - kbase : C::KC;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kg + (size_t)kbase * D), (short)0, rows * C::KRB, kBufferFlags);
+        (void*)(kg + (size_t)kbase * C::KRB), (short)0, rows * C::KRB, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vtg + kbase), (short)0, (C::VROWS * p.L_pad - kbase) * 2, kBufferFlags);
     const bool full = rows == C::KC;
@@ -226,7 +240,18 @@ struct OctKernel {
     // that reaches its score block is preferred over waves in their PV
     // phase, which spreads the waves of a SIMD over the phases of a pass.
     __builtin_amdgcn_s_setprio(1);
-    if (single) {
+    if constexpr (F8) {
+      // one 16x16x128 FP8 step per score block: 32 bytes of the K row per lane
+      if (single) {
+        s0 = mac_fp8(lds_load<u32x4>(ka0), lds_load<u32x4>(ka0 + 16), qf[0], qf[1], s0);
+        s1 = s0;
+      } else {
+        const u32x4 a0 = lds_load<u32x4>(ka0), a1 = lds_load<u32x4>(ka0 + 16);
+        const u32x4 b0 = lds_load<u32x4>(ka1), b1 = lds_load<u32x4>(ka1 + 16);
+        s0 = mac_fp8(a0, a1, qf[0], qf[1], s0);
+        s1 = mac_fp8(b0, b1, qf[0], qf[1], s1);
+      }
+    } else if (single) {
 #pragma unroll
       for (int sl = 0; sl < C::NSLAB; ++sl)
         s0 = Mma<bf16_t>::mac8(lds_load<u32x4>(ka0 + 64 * sl), qf[sl], s0);
@@ -349,7 +374,7 @@ struct OctKernel {
   // lane extracts the entries it needs.
   __device__ __forceinline__ void run_list(int buf, const List& li, int lim) {
     const uint32_t shq = 4u * (uint32_t)(n >> 3), shv = 4u * (uint32_t)(g >> 1);
-    const uint32_t kb = lds_addr(sm.k[buf]) + (uint32_t)((n & 7) * C::KRS + 16 * g);
+    const uint32_t kb = lds_addr(sm.k[buf]) + (uint32_t)((n & 7) * C::KRS + (F8 ? 32 : 16) * g);
     uint64_t rest = li.w;
     for (int q0 = 0; q0 < li.count; q0 += 4) {
       const uint32_t w = (uint32_t)rest & 0xffffu;
@@ -387,25 +412,33 @@ struct OctKernel {
     const int qb = lb - bh * p.n_qblocks;
     L = p.L;
     const size_t head_off = (size_t)bh * (size_t)L * D;
-    const bf16_t* __restrict__ qg = reinterpret_cast<const bf16_t*>(p.q) + head_off;
-    kg = reinterpret_cast<const bf16_t*>(p.k) + head_off;
+    kg = reinterpret_cast<const uint8_t*>(p.k) + head_off * C::ESZ;
     vtg = reinterpret_cast<const bf16_t*>(p.vt) + (size_t)bh * C::VROWS * p.L_pad;
 
     const int row0 = qb * C::ROWS + 16 * wave;
     const bool act = row0 < L;
     mrow = p.mask + ((size_t)bh * p.T_q + (size_t)(act ? row0 / p.M : 0)) * p.words;
     const int rq = row0 + n < L ? row0 + n : L - 1;
+    // lane (g, n): row n of the tile, d = 8g.. of each 32-wide slab (bf16),
+    // or d = 32g..32g+31 (FP8)
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(p.q) + (head_off + (size_t)rq * D) * C::ESZ;
 #pragma unroll
     for (int s = 0; s < C::NSLAB; ++s)
-      qf[s] = *reinterpret_cast<const u32x4*>(qg + (size_t)rq * D + 32 * s + 8 * g);
+      qf[s] = *reinterpret_cast<const u32x4*>(qrow + (F8 ? 32 * g + 16 * s : 64 * s + 16 * g));
     if (row0 + n >= L)
 #pragma unroll
       for (int s = 0; s < C::NSLAB; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
     cs = p.scale_log2;
-    if (cs < 0.f) {
+    if (cs < 0.f) {  // c * s = |c| * ((-q) . k), and negating bf16 / FP8 is exact
       cs = -cs;
+      constexpr uint32_t SIGN = F8 ? 0x80808080u : 0x80008000u;
 #pragma unroll
-      for (int s = 0; s < C::NSLAB; ++s) qf[s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      for (int s = 0; s < C::NSLAB; ++s) qf[s] ^= u32x4{SIGN, SIGN, SIGN, SIGN};
+    }
+    if constexpr (F8) {
+      // scores in FP8 units: the Q tile's and the head's K scale join c
+      const int t16 = (L + 15) >> 4;
+      cs *= p.q_scale[(size_t)bh * t16 + (act ? row0 >> 4 : 0)] * p.k_scale[bh];
     }
     // The fragment is complete here: later code sees registers written by
     // this statement, not loads in flight, so no load wait lands in the
@@ -512,11 +545,11 @@ struct OctKernel {
   }
 };
 
-template <int D, int N, bool SKIP>
+template <int D, int N, bool SKIP, bool F8 = false>
 __global__ __launch_bounds__(1024) void attn_oct_kernel(AttnParams p) {
-  static_assert(OctCfg<D, N>::W == 16, "launch bounds: 16 waves");
-  static_assert(OctCfg<D, N>::KC == kChunkKeys && OctCfg<D, N>::ROWS == kRowsPerGroup, "chunk layout");
-  using K = OctKernel<D, N, SKIP>;
+  static_assert(OctCfg<D, N, F8>::W == 16, "launch bounds: 16 waves");
+  static_assert(OctCfg<D, N, F8>::KC == kChunkKeys && OctCfg<D, N, F8>::ROWS == kRowsPerGroup, "chunk layout");
+  using K = OctKernel<D, N, SKIP, F8>;
   __shared__ __attribute__((aligned(16))) typename K::Smem sm;
   K k(p, sm);
   k.run();

@@ -20,6 +20,9 @@ struct AttnLaunch {
   float* lse;
   void* workspace;  // packed V^T, then chunk bitmaps: attention_workspace_bytes()
   hipStream_t stream;
+  // FP8 scores: q and k hold e4m3 bytes with these scales (null otherwise)
+  const float* q_scale = nullptr;
+  const float* k_scale = nullptr;
 };
 
 // Row length of the packed V^T and its size in bytes.
@@ -72,6 +75,9 @@ inline size_t attention_bwd_workspace_bytes(const tsa_problem_t* p) {
 hipError_t launch_attention_bwd(const BwdLaunch& a);
 
 hipError_t launch_attention_bf16(const AttnLaunch& a);
+hipError_t launch_attention_fp8(const AttnLaunch& a);
+hipError_t launch_quantize_qk_fp8(const tsa_problem_t* p, const void* q, const void* k, uint8_t* q8,
+                                  float* q_scale, uint8_t* k8, float* k_scale, hipStream_t stream);
 hipError_t launch_attention_f32(const AttnLaunch& a);
 
 }  // namespace tsa
