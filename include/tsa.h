@@ -100,7 +100,8 @@ tsa_status_t tsa_attention_fwd(const tsa_problem_t* p,
  * of a head, and k_scale [B,H] fp32, one per head.  A scale is the tile's
  * largest |x| / 448 (1 for an all-zero tile); a value becomes the e4m3 number
  * nearest to x / scale, ties to even.  q8, k8: [B,H,L,128] bytes.  p->dtype must
- * be bf16 and p->d 128; M and N are not read.  No workspace.  The quantisation
+ * be bf16, p->d 128 and B*H <= 65535; M and N are not read.  No workspace
+ * (k8 serves as scratch for the per-head maxima before it is written).  The quantisation
  * is this library's reading of the per-tile scaling named beside the pages'
  * method (FG-Attn itself fixes no precision). */
 tsa_status_t tsa_quantize_qk_fp8(const tsa_problem_t* p, const void* q, const void* k,

@@ -27,7 +27,7 @@ def _e4m3_values(bytes_u8):
     return bytes_u8.cpu().view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("L", [1000, 13, 256, 4099])
+@pytest.mark.parametrize("L", [1000, 13, 256, 4099, 1])
 def test_quantize_bit_exact(L):
     torch = torch_or_skip()
     w = small_workload(f"q8_{L}", L, 128, 16, 8, seed=700 + L)

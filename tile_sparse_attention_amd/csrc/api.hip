@@ -150,8 +150,8 @@ tsa_status_t tsa_quantize_qk_fp8(const tsa_problem_t* p, const void* q, const vo
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q8, 16) || !aligned(k8, 16) || !aligned(q_scale, 4) ||
       !aligned(k_scale, 4))
     return fail(TSA_ERR_INVALID_ARGUMENT, "tensors need 16-byte, scales 4-byte alignment");
-  if ((long long)p->B * p->H * (long long)p->L * 16 / 256 > kMaxGrid)
-    return fail(TSA_ERR_UNSUPPORTED, "grid too large");
+  if ((long long)p->B * p->H * (long long)p->L * 16 / 256 > kMaxGrid || (long long)p->B * p->H > 65535)
+    return fail(TSA_ERR_UNSUPPORTED, "grid too large (B*H <= 65535 for the FP8 quantisation)");
   const hipError_t e = tsa::launch_quantize_qk_fp8(p, q, k, q8, q_scale, k8, k_scale,
                                                    static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "FP8 quantisation launch");

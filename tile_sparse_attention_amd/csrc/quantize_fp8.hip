@@ -6,7 +6,7 @@
 // the largest value of a tile maps to 448, the largest e4m3 value.  Each
 // value becomes the e4m3 number nearest to x / s (ties to even), from an
 // IEEE float32 division and the hardware's round-to-nearest conversion.
-// All three passes read their input once and are bound by HBM bandwidth.
+// The passes read their input once and are bound by HBM bandwidth.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -66,14 +66,20 @@ __global__ __launch_bounds__(256) void quantize_q_kernel(const bf16_t* __restric
   *reinterpret_cast<u32x4*>(q8 + off + 16) = y[1];
 }
 
-// Largest |k| of one (b, h): one work-group per head.
-__global__ __launch_bounds__(1024) void k_amax_kernel(const bf16_t* __restrict__ k, int L,
-                                                      float* __restrict__ k_scale) {
-  __shared__ float part[16];
+// Largest |k| of one slice of a (b, h): work-group (slice, b*H + h) of a
+// grid of S slices per head writes the maximum of its slice to
+// partial[(b*H + h) * S + slice].
+constexpr int kKSlices = 64;  // slices per head (fewer for L < 2)
+
+__global__ __launch_bounds__(256) void k_amax_kernel(const bf16_t* __restrict__ k, int L,
+                                                     float* __restrict__ partial) {
+  __shared__ float part[4];
+  const int slice = blockIdx.x, bh = blockIdx.y, S = gridDim.x;
   const size_t n8 = (size_t)L * kD / 8;
-  const u32x4* kh = reinterpret_cast<const u32x4*>(k + (size_t)blockIdx.x * L * kD);
+  const size_t lo = n8 * slice / S, hi = n8 * (slice + 1) / S;
+  const u32x4* kh = reinterpret_cast<const u32x4*>(k + (size_t)bh * L * kD);
   float m = 0.f;
-  for (size_t i = threadIdx.x; i < n8; i += 1024) {
+  for (size_t i = lo + threadIdx.x; i < hi; i += 256) {
     const u32x4 x = kh[i];
 #pragma unroll
     for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(bf16_lo(x[e])), fabsf(bf16_hi(x[e]))));
@@ -82,11 +88,18 @@ __global__ __launch_bounds__(1024) void k_amax_kernel(const bf16_t* __restrict__
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float mm = 0.f;
-    for (int i = 0; i < 16; ++i) mm = fmaxf(mm, part[i]);
-    k_scale[blockIdx.x] = mm > 0.f ? mm / kE4m3Max : 1.f;
-  }
+  if (threadIdx.x == 0)
+    partial[(size_t)bh * S + slice] = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+}
+
+// k_scale[b*H + h] from the head's partial maxima.
+__global__ __launch_bounds__(256) void k_scale_kernel(const float* __restrict__ partial, int S, long long bh,
+                                                      float* __restrict__ k_scale) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= bh) return;
+  float m = 0.f;
+  for (int s = 0; s < S; ++s) m = fmaxf(m, partial[i * S + s]);
+  k_scale[i] = m > 0.f ? m / kE4m3Max : 1.f;
 }
 
 // K / its head's scale -> e4m3: eight values per thread.
@@ -114,8 +127,16 @@ hipError_t launch_quantize_qk_fp8(const tsa_problem_t* p, const void* q, const v
                      static_cast<const bf16_t*>(q), p->L, t16, tiles, q8, q_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_amax_kernel, dim3((unsigned)bh), dim3(1024), 0, stream, static_cast<const bf16_t*>(k),
-                     p->L, k_scale);
+  // The slice maxima go through k8 as scratch: B*H*S floats with S <= 32 L,
+  // at most the B*H*L*128 bytes of k8, which quantize_k_kernel overwrites
+  // only after k_scale_kernel has read them.
+  const int S = p->L >= 2 ? kKSlices : 32;
+  float* partial = reinterpret_cast<float*>(k8);
+  hipLaunchKernelGGL(k_amax_kernel, dim3((unsigned)S, (unsigned)bh), dim3(256), 0, stream,
+                     static_cast<const bf16_t*>(k), p->L, partial);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_scale_kernel, dim3((unsigned)((bh + 255) / 256)), dim3(256), 0, stream, partial, S, bh,
+                     k_scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long per_head8 = (long long)p->L * kD / 8;
   const long long total8 = bh * per_head8;
