@@ -15,8 +15,8 @@
 //   * bwd_prep_kernel: D and lse2 = LSE * log2(e) per row, written per
 //     128-row chunk (128 lse2 values, then 128 D values).  A row past L or
 //     with no kept key gets lse2 = +inf, which makes its probabilities 0.
-//   * bwd_dkdv_kernel: a work-group owns 128 consecutive keys of one (b, h),
-//     eight waves of 16.  Query rows stream through LDS in double-buffered
+//   * bwd_dkdv_kernel: a work-group owns 192 consecutive keys of one (b, h),
+//     twelve waves of 16.  Query rows stream through LDS in double-buffered
 //     chunks of 128 rows (Q rows, dO rows and the chunk's lse2 / D).  Per
 //     chunk each wave lists the 16-row query units in which a tile of one of
 //     its keys is kept (M is a multiple of 16, so a unit lies in one mask
@@ -117,7 +117,9 @@ template <int D>
 struct DkdvCfg {
   static constexpr int QC = kBwdChunk;          // query rows per chunk
   static constexpr int UNITS = QC / 16;         // 16-row query units per chunk
-  static constexpr int W = 8;                   // waves per work-group
+  // waves per work-group: 12 (three per SIMD), which leaves each wave the
+  // 168 registers its fragments, accumulators and pass need
+  static constexpr int W = 12;
   static constexpr int KEYS = 16 * W;           // keys per work-group
   static constexpr int NSLAB = D / 32;          // 32-wide d slabs of S and dP
   static constexpr int NDB = D / 16;            // 16-wide d blocks of dK^T, dV^T
@@ -162,7 +164,6 @@ struct DkdvKernel {
   u32x4 kf[C::NSLAB], vf[C::NSLAB];
   f32x4 dk[C::NDB], dv[C::NDB];
   float cs;
-  uint32_t doff[C::NI_W];
 
   __device__ __forceinline__ DkdvKernel(const BwdParams& pp, Buf& b0, Buf& b1) : p(pp), bf0(b0), bf1(b1) {}
 
@@ -200,7 +201,8 @@ struct DkdvKernel {
     for (int u = 0; u < C::NI_W; ++u) {
       const int I = wave + C::W * u;
       if (C::NI % C::W == 0 || I < C::NI) {
-        const uint32_t off = full ? doff[u] : dma_offset(I, lane, rows);
+        // (offsets recomputed per chunk: registers are tight)
+        const uint32_t off = dma_offset(I, lane, full ? C::QC : rows);
         if (I < C::NI_T)
           dma16(rq, bufr<B>().q + I * 1024, off);
         else if (I < 2 * C::NI_T)
@@ -231,48 +233,24 @@ struct DkdvKernel {
     return un;
   }
 
-  // A operands of S and dP for query units u0 and u1: 16-byte reads of the
-  // Q and dO rows (block 1 skipped when u1 is padding)
-  struct Ops {
-    u32x4 q0[C::NSLAB], q1[C::NSLAB], o0[C::NSLAB], o1[C::NSLAB];
-  };
-
+  // Query units u0 and u1 of the chunk in buffer B (single: u1 is padding).
   template <int B>
-  __device__ __forceinline__ void load_ops(Ops& op, int u0, int u1, bool single) const {
-    const lds_cptr qa = to_lds(bufr<B>().q) + 16 * g;
-    const lds_cptr oa = to_lds(bufr<B>().o) + 16 * g;
-    const uint32_t r0 = (uint32_t)(16 * u0 + n) * C::RS, r1 = (uint32_t)(16 * u1 + n) * C::RS;
-#pragma unroll
-    for (int sl = 0; sl < C::NSLAB; ++sl) {
-      op.q0[sl] = lds_read16(qa + r0 + 64 * sl);
-      op.o0[sl] = lds_read16(oa + r0 + 64 * sl);
-    }
-    if (!single)
-#pragma unroll
-      for (int sl = 0; sl < C::NSLAB; ++sl) {
-        op.q1[sl] = lds_read16(qa + r1 + 64 * sl);
-        op.o1[sl] = lds_read16(oa + r1 + 64 * sl);
-      }
-  }
-
-  // Query units u0 and u1 of the chunk in buffer buf (single: u1 is padding),
-  // with their S / dP operands already in `op`; `next` issues the next
-  // pass's operand reads once the score MFMAs have taken these.
-  template <int B, typename F>
-  __device__ __forceinline__ void pass(int u0, int u1, bool single, uint32_t keep, const Ops& op, F&& next) {
+  __device__ __forceinline__ void pass(int u0, int u1, bool single, uint32_t keep) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, d0 = s0, d1 = s0;
-#pragma unroll
-    for (int sl = 0; sl < C::NSLAB; ++sl) {
-      s0 = Mma<bf16_t>::mac8(op.q0[sl], kf[sl], s0);
-      d0 = Mma<bf16_t>::mac8(op.o0[sl], vf[sl], d0);
-    }
-    if (!single)
+    {
+      const lds_cptr qa = to_lds(bufr<B>().q) + 16 * g;
+      const lds_cptr oa = to_lds(bufr<B>().o) + 16 * g;
+      const uint32_t r0 = (uint32_t)(16 * u0 + n) * C::RS, r1 = (uint32_t)(16 * u1 + n) * C::RS;
 #pragma unroll
       for (int sl = 0; sl < C::NSLAB; ++sl) {
-        s1 = Mma<bf16_t>::mac8(op.q1[sl], kf[sl], s1);
-        d1 = Mma<bf16_t>::mac8(op.o1[sl], vf[sl], d1);
+        s0 = Mma<bf16_t>::mac8(lds_read16(qa + r0 + 64 * sl), kf[sl], s0);
+        d0 = Mma<bf16_t>::mac8(lds_read16(oa + r0 + 64 * sl), vf[sl], d0);
+        if (!single) {
+          s1 = Mma<bf16_t>::mac8(lds_read16(qa + r1 + 64 * sl), kf[sl], s1);
+          d1 = Mma<bf16_t>::mac8(lds_read16(oa + r1 + 64 * sl), vf[sl], d1);
+        }
       }
-    next();
+    }
     // lse2 and D of the four query rows each accumulator lane holds
     const float* lb = bufr<B>().ld;
     const f32x4 l0 = *reinterpret_cast<const f32x4*>(lb + 16 * u0 + 4 * g);
@@ -299,58 +277,28 @@ struct DkdvKernel {
     const uint32_t t1 = (uint32_t)(16 * u1 + 4 * g + (n >> 2)) * C::RS + tb;
     const lds_cptr qt = to_lds(bufr<B>().q);
     const lds_cptr ot = to_lds(bufr<B>().o);
-    // d block j + 1's operands are read while block j multiplies
     auto tr = [&](lds_cptr base, int j) {
       const u32x2 x = lds_read_tr16(base + t0 + 32u * j), y = lds_read_tr16(base + t1 + 32u * j);
       return u32x4{x[0], x[1], y[0], y[1]};
     };
-    u32x4 av = tr(ot, 0), ak = tr(qt, 0);
 #pragma unroll
     for (int j = 0; j < C::NDB; ++j) {
-      u32x4 nav = av, nak = ak;
-      if (j + 1 < C::NDB) {
-        nav = tr(ot, j + 1);
-        nak = tr(qt, j + 1);
-      }
-      dv[j] = Mma<bf16_t>::mac8(av, pbo, dv[j]);
-      dk[j] = Mma<bf16_t>::mac8(ak, sbo, dk[j]);
-      av = nav;
-      ak = nak;
+      dv[j] = Mma<bf16_t>::mac8(tr(ot, j), pbo, dv[j]);
+      dk[j] = Mma<bf16_t>::mac8(tr(qt, j), sbo, dk[j]);
     }
   }
 
-  // The chunk's units two at a time (ascending; an odd last one alone), each
-  // pass's S / dP operands read during the previous pass.
+  // The chunk's units two at a time (ascending; an odd last one alone).
   template <int B>
   __device__ __forceinline__ void run_units(const Units& un) {
     uint32_t m = un.units;
-    if (m == 0u) return;
-    auto take = [&](int& a, int& b, bool& single) {
-      a = __builtin_ctz(m);
+    while (m != 0u) {
+      const int u0 = __builtin_ctz(m);
       m &= m - 1u;
-      single = m == 0u;
-      b = single ? a : __builtin_ctz(m);
+      const bool single = m == 0u;
+      const int u1 = single ? u0 : __builtin_ctz(m);
       if (!single) m &= m - 1u;
-    };
-    int u0, u1;
-    bool single;
-    take(u0, u1, single);
-    Ops op;
-    load_ops<B>(op, u0, u1, single);
-    for (;;) {
-      const bool more = m != 0u;
-      int nu0 = 0, nu1 = 0;
-      bool nsingle = true;
-      if (more) take(nu0, nu1, nsingle);
-      Ops nop;
-      pass<B>(u0, u1, single, un.keep, op, [&] {
-        if (more) load_ops<B>(nop, nu0, nu1, nsingle);
-      });
-      if (!more) break;
-      u0 = nu0;
-      u1 = nu1;
-      single = nsingle;
-      op = nop;
+      pass<B>(u0, u1, single, un.keep);
     }
   }
 
@@ -417,11 +365,6 @@ struct DkdvKernel {
       dk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       dv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-#pragma unroll
-    for (int u = 0; u < C::NI_W; ++u) {
-      const int I = wave + C::W * u;
-      doff[u] = I < C::NI ? dma_offset(I, lane, C::QC) : 0u;
-    }
     const int n_chunks = p.n_qc;
     const uint32_t mw0 = issue_chunk<0>(0);
     __builtin_amdgcn_s_waitcnt(0);
@@ -452,8 +395,8 @@ struct DkdvKernel {
 };
 
 template <int D, int N>
-__global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
-  static_assert(DkdvCfg<D>::W == 8, "launch bounds: 8 waves");
+__global__ __launch_bounds__(768) void bwd_dkdv_kernel(BwdParams p) {
+  static_assert(DkdvCfg<D>::W == 12, "launch bounds: 12 waves");
   using K = DkdvKernel<D, N>;
   __shared__ __attribute__((aligned(16))) typename K::Buf b0;
   __shared__ __attribute__((aligned(16))) typename K::Buf b1;
