@@ -57,7 +57,7 @@ struct BwdParams {
   float* ld;             // [B*H][n_qc][256]: lse2 of a chunk's 128 rows, then D
   int L, M, T_q, words;
   int n_qc;              // 128-row chunks per (b, h)
-  int n_kblocks;         // 128-key blocks per (b, h) (dK/dV grid)
+  int n_kblocks;         // key blocks per (b, h) (dK/dV grid)
   int n_qblocks;         // 256-row blocks per (b, h) (dQ grid)
   float scale;           // as passed by the caller
   float cs;              // |scale| * log2(e)
@@ -288,27 +288,41 @@ struct DkdvKernel {
     }
   }
 
-  // The chunk's units two at a time (ascending; an odd last one alone).
-  template <int B>
-  __device__ __forceinline__ void run_units(const Units& un) {
+  // The chunk's units two at a time (ascending; an odd last one alone);
+  // after_first runs after the first pass, or at once when there is none.
+  template <int B, typename F>
+  __device__ __forceinline__ void run_units(const Units& un, F&& after_first) {
     uint32_t m = un.units;
-    while (m != 0u) {
+    auto step = [&] {
       const int u0 = __builtin_ctz(m);
       m &= m - 1u;
       const bool single = m == 0u;
       const int u1 = single ? u0 : __builtin_ctz(m);
       if (!single) m &= m - 1u;
       pass<B>(u0, u1, single, un.keep);
-    }
+    };
+    if (m != 0u) step();
+    after_first();
+    while (m != 0u) step();
   }
 
-  // Chunk c from buffer B while chunk c+1 loads into the other buffer.
+  // Chunk c from buffer B while chunk c+1 loads into the other buffer.  A
+  // wave issues its share of chunk c+1's loads after its first pass: issued
+  // by every wave at the chunk start, they fill the compute unit's load
+  // queue and each wave stalls until its share is accepted, while after one
+  // pass the queue drains behind the matrix-core work.
   template <int B>
   __device__ __forceinline__ void chunk_step(int c, int n_chunks, bool act, bool kvalid, Units& cur) {
     const bool more = c + 1 < n_chunks;
     // buffer B^1 was last read in the previous step, which every wave has left
-    const uint32_t mwn = more ? issue_chunk<B ^ 1>(c + 1) : 0u;
-    if (act) run_units<B>(cur);
+    uint32_t mwn = 0u;
+    auto issue = [&] {
+      if (more) mwn = issue_chunk<B ^ 1>(c + 1);
+    };
+    if (act)
+      run_units<B>(cur, issue);
+    else
+      issue();
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c+1 have landed
     if (act && more) cur = make_units(c + 1, mwn, kvalid);
     __syncthreads();                // ... and every other wave's
