@@ -1,6 +1,7 @@
 // Per-CU throughput microbenchmarks for the resources the tile-sparse
 // attention kernel depends on (gfx950): LDS reads (b128, b64, transposing
-// b64), bf16 16x16x32 MFMA, v_exp_f32 and fp32 FMA.  Every kernel is
+// b64), bf16 16x16x32 / 16x16x16 and FP8 16x16x32 / 16x16x128 MFMA,
+// v_exp_f32 and fp32 FMA.  Every kernel is
 // in-bounds and exits after a fixed number of iterations.
 //
 //   hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops micro/rates.hip -o micro_rates
@@ -217,6 +218,36 @@ __global__ __launch_bounds__(kThreads) void mfma_bf16_k16(unsigned* out, float s
   if (s.x + s.y + s.z + s.w == 1.2345f) out[0] = 1;
 }
 
+// FP8 (e4m3) steps: the 32-deep one that gfx950 inherits and its 128-deep
+// one (block scales 2^0)
+__global__ __launch_bounds__(kThreads) void mfma_fp8_k32(unsigned* out, float seed) {
+  const long a = (long)(seed * 1000.f) * 0x0101010101010101L, b = a ^ 0x1122334455667788L;
+  f32x4 c0 = {0, 0, 0, 0}, c1 = c0, c2 = c0, c3 = c0;
+  for (int it = 0; it < kIters / 4; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c3, 0, 0, 0);
+  }
+  const f32x4 s = c0 + c1 + c2 + c3;
+  if (s.x + s.y + s.z + s.w == 1.2345f) out[0] = 1;
+}
+
+__global__ __launch_bounds__(kThreads) void mfma_fp8_k128(unsigned* out, float seed) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  i32x8 a, b;
+  for (int i = 0; i < 8; ++i) { a[i] = (int)(seed * 1000.f) * (i + 1); b[i] = a[i] ^ 0x11223344; }
+  f32x4 c0 = {0, 0, 0, 0}, c1 = c0, c2 = c0, c3 = c0;
+  for (int it = 0; it < kIters / 4; ++it) {
+    c0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c0, 0, 0, 0, 127, 0, 127);
+    c1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c1, 0, 0, 0, 127, 0, 127);
+    c2 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c2, 0, 0, 0, 127, 0, 127);
+    c3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c3, 0, 0, 0, 127, 0, 127);
+  }
+  const f32x4 s = c0 + c1 + c2 + c3;
+  if (s.x + s.y + s.z + s.w == 1.2345f) out[0] = 1;
+}
+
 __global__ __launch_bounds__(kThreads) void valu_exp(unsigned* out, float seed) {
   float x0 = seed * threadIdx.x, x1 = x0 + 1.f, x2 = x0 + 2.f, x3 = x0 + 3.f;
   for (int it = 0; it < kIters / 4; ++it) {
@@ -318,6 +349,12 @@ int main() {
   t = time_ms([&] { hipLaunchKernelGGL(mfma_bf16_k16, dim3(blocks), dim3(kThreads), 0, 0, out, 0.5f); });
   printf("mfma 16x16x16 bf16: %7.1f FLOP/clk/CU (%.3f ms)\n",
          per_cu_clk(waves * kIters * 16.0 * 16 * 16 * 2, t), t);
+  t = time_ms([&] { hipLaunchKernelGGL(mfma_fp8_k32, dim3(blocks), dim3(kThreads), 0, 0, out, 0.5f); });
+  printf("mfma 16x16x32 fp8 : %7.1f FLOP/clk/CU (%.3f ms)\n",
+         per_cu_clk(waves * kIters * 16.0 * 16 * 32 * 2, t), t);
+  t = time_ms([&] { hipLaunchKernelGGL(mfma_fp8_k128, dim3(blocks), dim3(kThreads), 0, 0, out, 0.5f); });
+  printf("mfma 16x16x128 f8 : %7.1f FLOP/clk/CU (%.3f ms)\n",
+         per_cu_clk(waves * kIters * 16.0 * 16 * 128 * 2, t), t);
   t = time_ms([&] { hipLaunchKernelGGL(valu_exp, dim3(blocks), dim3(kThreads), 0, 0, out, 0.01f); });
   printf("v_exp_f32         : %7.1f lane-ops/clk/CU (%.3f ms)\n", per_cu_clk(waves * 64 * kIters, t), t);
   t = time_ms([&] { hipLaunchKernelGGL(valu_fma, dim3(blocks), dim3(kThreads), 0, 0, out, 0.01f); });
