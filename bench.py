@@ -8,7 +8,8 @@ inputs resident in HBM.  Prints one JSON line.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 
 With --backward it times the backward pass (tsa_attention_bwd) of the same
-workload instead and prints that line.
+workload instead and prints that line; --fp8, --mask-diff and --compact time
+the FP8 forward, the mask diff and the mask compaction likewise.
 """
 from __future__ import annotations
 
@@ -293,6 +294,52 @@ def bench_mask_diff(args, w, name):
     print(json.dumps(rec), flush=True)
 
 
+def bench_compact(args, w, name):
+    """One step = one tsa_mask_compact call (the workload's bitmap in, CSR
+    row_ptr and col_idx out, capacity exact), all resident in HBM."""
+    import torch
+
+    import tile_sparse_attention_amd as T
+    import workloads as W
+    qd = kd = None
+    if w.mask.kind == "predicted":
+        q, k, _ = W.make_qkv(w)
+        qd, kd = q.cuda(), k.cuda()
+    mask = make_mask(w, qd, kd)
+    del qd, kd
+    pr = T.problem(w.B, w.H, w.L, 0, w.M, w.N)
+    rows = w.B * w.H * w.T_q
+    nnz = int(T.mask_compact(mask, w.L, w.M, w.N, col_capacity=0)[0][-1])
+    row_ptr = torch.empty(rows + 1, dtype=torch.int64, device="cuda")
+    col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device="cuda")
+    ws, nws = T._workspace(T.OP_MASK_COMPACT, pr, mask.device)
+    lib = T.lib()
+
+    def step():
+        T._check(lib.tsa_mask_compact(T.ctypes.byref(pr), T._ptr(mask), T._ptr(row_ptr), T._ptr(col_idx),
+                                      nnz, T._ptr(ws), nws, T._stream()))
+
+    ms_step, ms_call, ms_min = time_calls(step, args.steps, args.warmup)
+    if int(row_ptr[-1]) != nnz:
+        raise SystemExit("compaction: list length differs from the count-only call")
+    # algorithmic bytes: the bitmap read once, row_ptr and col_idx written once
+    nbytes = mask.numel() * 4 + (rows + 1) * 8 + nnz * 4
+    gbs = nbytes / (ms_call * 1e-3) / 1e9
+    log(f"compaction: {ms_step:.4f} ms/step, call mean {ms_call:.4f} ms, {gbs:.0f} GB/s, "
+        f"{nnz} kept tiles in {rows} rows")
+    rec = {"metric": "mask compaction HBM throughput (keep-bitmap in, CSR row_ptr / col_idx out)",
+           "value": round(nbytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
+           "data": "synthetic (the workload's seeded mask)",
+           "config": {"workload": name, "B": w.B, "H": w.H, "L": w.L, "M": w.M, "N": w.N,
+                      "bitmap_bytes": mask.numel() * 4, "kept_tiles": nnz, "algorithmic_bytes": nbytes},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                        "frac": round(gbs / 8000.0, 4), "traffic": None,
+                        "kernel": "compact_count_kernel + scan_groups_kernel + compact_fill_kernel"}}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -307,6 +354,8 @@ def main():
     ap.add_argument("--fp8", action="store_true",
                     help="time the FP8-score forward (tsa_attention_fwd_fp8) of the workload, and the "
                          "quantisation of Q and K separately, and print its own JSON line")
+    ap.add_argument("--compact", action="store_true",
+                    help="time tsa_mask_compact (bitmap -> CSR lists) on the workload's mask instead")
     ap.add_argument("--mask-diff", action="store_true",
                     help="time tsa_mask_diff between the workload's mask and a reseeded one (mask reuse "
                          "across denoising steps) and print its own JSON line")
@@ -337,6 +386,9 @@ def main():
     w = W.get(name)
     if args.mask_diff:
         bench_mask_diff(args, w, name)
+        return
+    if args.compact:
+        bench_compact(args, w, name)
         return
     log(f"workload {name}: B={w.B} H={w.H} L={w.L} d={w.d} M={w.M} N={w.N} {w.dtype}")
     t0 = time.perf_counter()

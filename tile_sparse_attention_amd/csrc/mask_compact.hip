@@ -5,19 +5,24 @@
 // this turns each query-tile row of decisions into the ascending list of kept
 // key tiles.  Three passes, all bandwidth-bound scans of the bitmap:
 //   1. count:  one wave per row sums the popcounts of its words (padding bits
-//              past T_k cleared) and each work-group sums its rows;
+//              past T_k cleared) and each work-group sums its 16 rows;
 //   2. scan:   one work-group turns the per-group sums into int64 offsets;
-//   3. fill:   one wave per row writes row_ptr and walks its row in 64-tile
-//              windows with wave_compact64, the same routine the attention
-//              kernel uses on the fly, clipping writes at col_capacity.
+//   3. fill:   one wave per row writes row_ptr, then takes its row 64 words
+//              at a time: one coalesced load (a word per lane), a wave prefix
+//              sum of the words' popcounts for each lane's first slot, each
+//              lane's kept tiles into the wave's LDS staging area in
+//              ascending order, and from there contiguous coalesced stores,
+//              clipped at col_capacity.  A row that starts at or past
+//              col_capacity (a count-only call) reads no bits at all.
 #include "tsa_device.h"
 #include "tsa.h"
 
 namespace tsa {
 
-constexpr int kRowsPerGroup = 4;  // one wave per row, 4 waves per work-group
+constexpr int kRowsPerGroup = 16;  // rows per count work-group (one wave each) and per scan entry
+constexpr int kFillWaves = 4;      // rows per fill work-group (one wave each)
 
-__global__ __launch_bounds__(256) void compact_count_kernel(const uint32_t* __restrict__ mask,
+__global__ __launch_bounds__(64 * kRowsPerGroup) void compact_count_kernel(const uint32_t* __restrict__ mask,
                                                             long long rows, int words, int T_k,
                                                             int32_t* __restrict__ counts,
                                                             long long* __restrict__ group_sums) {
@@ -74,28 +79,66 @@ __global__ __launch_bounds__(1024) void scan_groups_kernel(long long* __restrict
   if (t == 1023) total[0] = part[1023];
 }
 
-__global__ __launch_bounds__(256) void compact_fill_kernel(
+// Orders this wave's LDS accesses on either side of it (a wave's LDS
+// operations complete in issue order; this keeps the compiler from moving
+// them across).
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ __launch_bounds__(64 * kFillWaves) void compact_fill_kernel(
     const uint32_t* __restrict__ mask, long long rows, int words, int T_k,
     const int32_t* __restrict__ counts, const long long* __restrict__ group_offsets,
     const long long* __restrict__ total, long long* __restrict__ row_ptr,
     int32_t* __restrict__ col_idx, long long col_capacity) {
+  __shared__ int32_t stage[kFillWaves][64 * 32];  // a block's kept tiles, per wave
   const int wave = wave_uniform(threadIdx.x >> 6);
-  const long long row = (long long)blockIdx.x * kRowsPerGroup + wave;
+  const long long row = (long long)blockIdx.x * kFillWaves + wave;
   if (row >= rows) return;
-  long long start = group_offsets[blockIdx.x];
-  for (int i = 0; i < wave; ++i) start += counts[row - wave + i];
+  // the row's count group's offset plus the counts of the group's earlier rows
+  const long long grp = row / kRowsPerGroup, first = grp * kRowsPerGroup;
+  long long start = group_offsets[grp];
+  for (long long i = first; i < row; ++i) start += counts[i];
   if (lane_id() == 0) {
     row_ptr[row] = start;
     if (row == rows - 1) row_ptr[rows] = total[0];
   }
+  if (start >= col_capacity) return;
   const uint32_t* r = mask + row * (long long)words;
-  uint32_t done = 0;
-  for (int first = 0; first < T_k; first += 64) {
-    const uint64_t bits = row_bits(r, first, 64, T_k);
-    done += wave_compact64(bits, first, done, [&](uint32_t pos, int val) {
-      const long long at = start + (long long)pos;
-      if (at < col_capacity) col_idx[at] = val;
-    });
+  const int lane = lane_id();
+  int32_t* st = stage[wave];
+  long long base = start;  // output slot of the block's first kept tile
+  // each block's words are loaded while the previous block is written
+  uint32_t xn = lane < words ? r[lane] : 0u;
+  for (int w0 = 0; w0 < words && base < col_capacity; w0 += 64) {
+    const int w = w0 + lane;
+    uint32_t x = xn;
+    xn = w + 64 < words ? r[w + 64] : 0u;
+    if (w < words) {
+      const int valid = T_k - 32 * w;  // 1..32 in the last word
+      if (valid < 32) x &= (1u << valid) - 1u;
+    }
+    const int c = __builtin_popcount(x);
+    int incl = c;  // inclusive prefix sum of the popcounts over the lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    int at = incl - c;
+    while (x != 0u) {
+      const int b = __builtin_ctz(x);
+      x &= x - 1u;
+      st[at++] = 32 * w + b;
+    }
+    wave_sync_lds();  // the staging writes of every lane precede the reads
+    const int total_blk = __shfl(incl, 63);
+    for (int j = lane; j < total_blk; j += 64)
+      if (base + j < col_capacity) col_idx[base + j] = st[j];
+    wave_sync_lds();  // ... and the reads precede the next block's writes
+    base += total_blk;
   }
 }
 
@@ -114,10 +157,11 @@ hipError_t launch_mask_compact(const tsa_problem_t* p, const uint32_t* mask, int
   off += ((size_t)groups * sizeof(long long) + 255) & ~(size_t)255;
   long long* total = reinterpret_cast<long long*>(ws + off);
 
-  hipLaunchKernelGGL(compact_count_kernel, dim3((unsigned)groups), dim3(256), 0, stream, mask, rows,
-                     words, T_k, counts, gsum);
+  const long long fill_groups = (rows + kFillWaves - 1) / kFillWaves;
+  hipLaunchKernelGGL(compact_count_kernel, dim3((unsigned)groups), dim3(64 * kRowsPerGroup), 0, stream, mask,
+                     rows, words, T_k, counts, gsum);
   hipLaunchKernelGGL(scan_groups_kernel, dim3(1), dim3(1024), 0, stream, gsum, groups, total);
-  hipLaunchKernelGGL(compact_fill_kernel, dim3((unsigned)groups), dim3(256), 0, stream, mask, rows,
+  hipLaunchKernelGGL(compact_fill_kernel, dim3((unsigned)fill_groups), dim3(64 * kFillWaves), 0, stream, mask, rows,
                      words, T_k, counts, gsum, total, reinterpret_cast<long long*>(row_ptr), col_idx,
                      (long long)col_capacity);
   return hipGetLastError();
