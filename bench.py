@@ -425,6 +425,19 @@ def main():
            "mask": w.description, "kept_fraction": round(flops / dense_flops, 6),
            "kept_flops": flops, "pct_of_peak": round(100 * tflops / peak, 2),
            "peak_tflops": peak}
+    if w.mask.kind == "predicted":
+        # the predictor is timed on its own and reported beside the attention call
+        mask2 = torch.empty_like(mask)
+
+        def predict_step():
+            T.predict_mask(qd, kd, w.M, w.N, w.mask.sparsity_percent, out=mask2)
+        p_step, p_call, _ = time_calls(predict_step, max(3, args.steps // 4), 1)
+        if not torch.equal(mask2, mask):
+            raise SystemExit("predictor: repeated calls gave different masks")
+        cfg["predictor_ms"] = round(p_step, 4)
+        cfg["attention_plus_predictor_ms"] = round(ms_step + p_step, 4)
+        log(f"predictor: {p_step:.3f} ms/step; attention + predictor {ms_step + p_step:.3f} ms")
+        del mask2
     if not args.no_dense:
         ones = torch.full_like(mask, -1)
         out2 = torch.empty_like(qd)
