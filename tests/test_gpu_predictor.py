@@ -43,7 +43,8 @@ def _run(q, k, M, N, sp):
 @pytest.mark.parametrize("dtype,d,L,M,N,sp", [
     ("bf16", 128, 1000, 16, 16, 85), ("bf16", 128, 777, 16, 8, 70), ("f32", 64, 512, 16, 16, 50),
     ("bf16", 64, 300, 32, 1, 90), ("bf16", 128, 16, 16, 16, 85), ("f32", 128, 2000, 64, 64, 0),
-    ("bf16", 128, 4100, 16, 4, 99)])
+    ("bf16", 128, 4100, 16, 4, 99),
+    ("bf16", 64, 9000, 64, 1, 85)])   # 9000 key tiles: rows too long to be held in LDS
 def test_predictor_small(dtype, d, L, M, N, sp):
     torch_or_skip()
     w = W.Workload("p", 2, 2, L, d, M, N, dtype, W.MaskRecipe("predicted", sparsity_percent=sp),
@@ -57,10 +58,11 @@ def test_predictor_small(dtype, d, L, M, N, sp):
             _check_rows(bits[b, h], s, sp)
 
 
-def test_predictor_ties_go_to_smaller_tile():
+@pytest.mark.parametrize("L,M,N", [(256, 16, 16), (8320, 64, 1)])  # row in LDS / row too long for it
+def test_predictor_ties_go_to_smaller_tile(L, M, N):
     torch = torch_or_skip()
-    say("predictor ties")
-    L, d, M, N = 256, 64, 16, 16
+    say(f"predictor ties L={L} {M}x{N}")
+    d = 64
     q = torch.randn(1, 1, L, d).to(torch.bfloat16)
     k = torch.randn(1, 1, N, d).repeat(1, 1, L // N, 1).to(torch.bfloat16)   # all key tiles equal
     bits = _run(q, k, M, N, 50)
