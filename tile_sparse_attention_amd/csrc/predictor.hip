@@ -7,7 +7,7 @@
 //               of the keys of key tile j (fp32 sums of the input elements);
 //   2. score:   s_ij = Qbar_i . Kbar_j for a block of query-tile rows, an fp32
 //               matrix-core product (16x16x4 MFMA) staged through LDS;
-//   3. select:  per row (held in LDS when it has at most 8192 key tiles), an
+//   3. select:  per row (held in registers when it has at most 8192 key tiles), an
 //               exact radix select of the k-th largest score on
 //               order-preserving 32-bit keys, then keep everything above it
 //               plus the first (by ascending j) of the scores equal to it, so
@@ -98,11 +98,12 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Rows of up to this many key tiles are held in LDS (32 KB) while they are
-// selected; longer rows are read from the score block on every pass.
+// Rows of up to this many key tiles are held in registers while they are
+// selected (32 keys per thread: thread t owns tiles t, t + 256, ...); longer
+// rows are read from the score block on every pass.
 constexpr int kSelectRowMax = 8192;
 
-template <bool IN_LDS>
+template <bool IN_REG>
 __global__ __launch_bounds__(256) void select_pack_kernel(const float* __restrict__ scores,
                                                           uint32_t* __restrict__ mask, int T_q,
                                                           int T_k, int T_kp, int words, int i0,
@@ -117,7 +118,6 @@ __global__ __launch_bounds__(256) void select_pack_kernel(const float* __restric
   __shared__ uint32_t sh_prefix;
   __shared__ int sh_kr, sh_eqn;
   __shared__ int sh_eq[4];
-  __shared__ uint32_t rowkey[IN_LDS ? kSelectRowMax : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int z = blockIdx.x / rows, il = blockIdx.x % rows;
   const float* srow = scores + ((size_t)z * R + il) * T_kp;
@@ -126,27 +126,24 @@ __global__ __launch_bounds__(256) void select_pack_kernel(const float* __restric
     for (int w = tid; w < words; w += 256) out[w] = 0u;
     return;
   }
-  if constexpr (IN_LDS) {
-    // the row's keys, read from the score block once: every load of a thread
-    // is issued before the first one is waited for
-    constexpr int NPT = kSelectRowMax / 256;
-    float v[NPT];
+  // the thread's keys, read from the score block once (every load issued
+  // before the first is waited for); every later access of the thread is to
+  // one of its own tiles t + 256 i
+  constexpr int NPT = IN_REG ? kSelectRowMax / 256 : 1;
+  uint32_t rk[NPT];
+  if constexpr (IN_REG) {
 #pragma unroll
     for (int t = 0; t < NPT; ++t) {
       const int j = tid + 256 * t;
-      v[t] = j < T_k ? srow[j] : 0.f;
+      rk[t] = order_key(j < T_k ? srow[j] : 0.f);
     }
-#pragma unroll
-    for (int t = 0; t < NPT; ++t) {
-      const int j = tid + 256 * t;
-      if (j < T_k) rowkey[j] = order_key(v[t]);
-    }
-    __syncthreads();
   }
-  auto key_at = [&](int j) -> uint32_t {
-    if constexpr (IN_LDS) return rowkey[j];
+  // key of tile j = tid + 256 * t
+  auto key_at = [&](int t, int j) -> uint32_t {
+    if constexpr (IN_REG) return rk[t];
     else return order_key(srow[j]);
   };
+  constexpr int TMAX = IN_REG ? NPT : 0x7fffffff;  // bound of t (the real bound is j < T_k)
 
   // -- radix select of the k-th largest key, 8 bits at a time --
   uint32_t prefix = 0, pmask = 0;
@@ -155,8 +152,11 @@ __global__ __launch_bounds__(256) void select_pack_kernel(const float* __restric
     for (int e = tid; e < HC * HS; e += 256) hist16[e] = 0;
     __syncthreads();
     int* hl = hist16 + (lane & (HC - 1)) * HS;
-    for (int j = tid; j < T_k; j += 256) {
-      const uint32_t key = key_at(j);
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      const int j = tid + 256 * t;
+      if (j >= T_k) break;
+      const uint32_t key = key_at(t, j);
       if ((key & pmask) == prefix) atomicAdd(&hl[(key >> shift) & 255], 1);
     }
     __syncthreads();
@@ -203,9 +203,11 @@ __global__ __launch_bounds__(256) void select_pack_kernel(const float* __restric
   if (sh_eqn == kr) {
     // every key equal to the k-th largest is kept (the usual case: no ties),
     // so each wave packs 64-key runs on its own, with no ranks to count
-    for (int base = 64 * wave; base < T_k; base += 256) {
-      const int j = base + lane;
-      const uint64_t kb = __ballot(j < T_k && key_at(j) >= prefix);
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      const int base = 64 * wave + 256 * t, j = base + lane;
+      if (base >= T_k) break;
+      const uint64_t kb = __ballot(j < T_k && key_at(t, j) >= prefix);
       const int w0 = base >> 5;
       if (lane == 0) out[w0] = (uint32_t)kb;
       if (lane == 1 && w0 + 1 < words) out[w0 + 1] = (uint32_t)(kb >> 32);
@@ -213,9 +215,11 @@ __global__ __launch_bounds__(256) void select_pack_kernel(const float* __restric
     return;
   }
   int eq_before = 0;  // equal keys at smaller j, across earlier rounds
-  for (int base = 0; base < T_k; base += 256) {
-    const int j = base + tid;
-    const uint32_t key = j < T_k ? key_at(j) : 0u;
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) {
+    const int base = 256 * t, j = base + tid;
+    if (base >= T_k) break;
+    const uint32_t key = j < T_k ? key_at(t, j) : 0u;
     const bool eq = j < T_k && key == prefix;
     const uint64_t eqb = __ballot(eq);
     if (lane == 0) sh_eq[wave] = __builtin_popcountll(eqb);
@@ -307,7 +311,7 @@ hipError_t launch_predict_mask(const tsa_problem_t* p, const void* q, const void
       else
         hipLaunchKernelGGL(pooled_scores_kernel<64>, grid, dim3(256), 0, stream, qbar, kbar, sc,
                            pl.T_q, pl.T_k, pl.T_kp, i0, rows, pl.R, bh0);
-      if (pl.T_k <= kSelectRowMax)
+      if (pl.T_k <= kSelectRowMax)  // rows held in registers
         hipLaunchKernelGGL(select_pack_kernel<true>, dim3((unsigned)(G * rows)), dim3(256), 0, stream, sc,
                            mask_out, pl.T_q, pl.T_k, pl.T_kp, pl.words, i0, rows, pl.R, bh0, kk);
       else
