@@ -34,6 +34,7 @@ __global__ __launch_bounds__(256) void pool_tiles_kernel(const E* __restrict__ x
   const int r1 = r0 + tile < L ? r0 + tile : L;
   const E* src = x + ((size_t)bh * L + r0) * d + dd;
   float s = 0.f;
+#pragma unroll 8
   for (int r = r0; r < r1; ++r, src += d) {
     if constexpr (sizeof(E) == 2) s += bf16_to_f32(*reinterpret_cast<const bf16_t*>(src));
     else s += *src;
@@ -56,12 +57,17 @@ __global__ __launch_bounds__(256) void pooled_scores_kernel(const float* __restr
   const int rbase = 64 * blockIdx.y;  // row within the block of rows
   const int cbase = 64 * blockIdx.x;
   constexpr int CH = D / 4;           // float4 chunks per row
+  // loads from clamped rows, out-of-range ones zeroed after: no branch
+  // between them, so four iterations' loads are in flight together
+#pragma unroll 4
   for (int e = tid; e < 64 * CH; e += 256) {
     const int rr = e / CH, c4 = e % CH;
     const int r = rbase + rr, j = cbase + rr;
-    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-    if (r < rows) a = *reinterpret_cast<const f32x4*>(qbar + ((size_t)bh * T_q + i0 + r) * D + 4 * c4);
-    if (j < T_k) b = *reinterpret_cast<const f32x4*>(kbar + ((size_t)bh * T_k + j) * D + 4 * c4);
+    const int rc = r < rows ? r : rows - 1, jc = j < T_k ? j : T_k - 1;
+    f32x4 a = *reinterpret_cast<const f32x4*>(qbar + ((size_t)bh * T_q + i0 + rc) * D + 4 * c4);
+    f32x4 b = *reinterpret_cast<const f32x4*>(kbar + ((size_t)bh * T_k + jc) * D + 4 * c4);
+    if (r >= rows) a = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (j >= T_k) b = f32x4{0.f, 0.f, 0.f, 0.f};
     *reinterpret_cast<f32x4*>(&qs[rr * S + 4 * c4]) = a;
     *reinterpret_cast<f32x4*>(&ks[rr * S + 4 * c4]) = b;
   }
