@@ -603,10 +603,21 @@ struct DqKernel {
   __device__ __forceinline__ void chunk_step(int c, int n_chunks, bool act, int& count) {
     const bool more = c + 1 < n_chunks;
     uint32_t mwn[MW];
-    // buffer B^1 was last read in the previous step, which every wave has left
-    if (more) issue_chunk<B ^ 1>(c + 1, mwn);
+    // buffer B^1 was last read in the previous step, which every wave has
+    // left.  A wave issues its share of chunk c+1's loads after its first
+    // pass (as the dK/dV kernel does), so the compute unit's load queue
+    // drains behind matrix-core work instead of stalling every wave at the
+    // chunk start.
+    bool issued = !more;
     if (act)
-      for (int q0 = 0; q0 < count; q0 += 32) pass<B>(q0, count - q0);
+      for (int q0 = 0; q0 < count; q0 += 32) {
+        pass<B>(q0, count - q0);
+        if (!issued) {
+          issue_chunk<B ^ 1>(c + 1, mwn);
+          issued = true;
+        }
+      }
+    if (!issued) issue_chunk<B ^ 1>(c + 1, mwn);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c+1 have landed
     if (act && more) count = make_list(c + 1, mwn);
     __syncthreads();                // ... and every other wave's
