@@ -28,8 +28,9 @@
 //                                         LDS reads of the same rows).
 //     The accumulator layout of S and dP (lane: four query rows of each
 //     unit, one key) is directly the B operand of the two updates.
-//   * bwd_dq_kernel: a work-group owns 256 query rows (16 waves of 16), as
-//     in the forward; K and V rows stream through LDS in double-buffered
+//   * bwd_dq_kernel: a work-group owns 256 query rows (16 waves of 16; 8
+//     waves for N = 1 at d = 128), as in the forward; K and V rows stream
+//     through LDS in double-buffered
 //     chunks of 128 keys.  Per chunk each wave lists its kept keys (one byte
 //     each, in LDS) and takes them 32 per pass:
 //       S^T = K Q^T, dP^T = V dO^T   (A = K / V rows, B = the wave's Q / dO
