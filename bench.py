@@ -41,6 +41,12 @@ def kernel_name(w) -> str:
     return "attn_oct_kernel" if w.N >= 8 else "attn_key_kernel"
 
 
+def sig(x: float, digits: int = 5) -> float:
+    """x rounded to `digits` significant digits: a small but measured rate never
+    prints as 0."""
+    return float(f"{x:.{digits}g}")
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -282,14 +288,14 @@ def bench_mask_diff(args, w, name):
     log(f"mask diff: {ms_step:.4f} ms/step, call mean {ms_call:.4f} ms, {gbs:.0f} GB/s, "
         f"{changed} of {a.shape[0] * a.shape[1] * a.shape[2] * w.T_k} decisions differ")
     rec = {"metric": "mask diff HBM throughput (two keep-bitmaps in, per-row and per-head counts out)",
-           "value": round(nbytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+           "value": sig(nbytes / (ms_step * 1e-3) / 1e9), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": sig(ms_step),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
            "data": "synthetic (two seeded masks of the workload)",
            "config": {"workload": name, "B": w.B, "H": w.H, "L": w.L, "M": w.M, "N": w.N,
                       "bitmap_bytes": a.numel() * 4, "changed_decisions": changed},
-           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
-                        "frac": round(gbs / 8000.0, 4), "traffic": None,
+           "roofline": {"bound": "hbm", "achieved": sig(gbs), "peak": 8000.0, "unit": "GB/s",
+                        "frac": sig(gbs / 8000.0), "traffic": None,
                         "kernel": "diff_rows_kernel + diff_heads_kernel"}}
     print(json.dumps(rec), flush=True)
 
@@ -328,14 +334,14 @@ def bench_compact(args, w, name):
     log(f"compaction: {ms_step:.4f} ms/step, call mean {ms_call:.4f} ms, {gbs:.0f} GB/s, "
         f"{nnz} kept tiles in {rows} rows")
     rec = {"metric": "mask compaction HBM throughput (keep-bitmap in, CSR row_ptr / col_idx out)",
-           "value": round(nbytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+           "value": sig(nbytes / (ms_step * 1e-3) / 1e9), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": sig(ms_step),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
            "data": "synthetic (the workload's seeded mask)",
            "config": {"workload": name, "B": w.B, "H": w.H, "L": w.L, "M": w.M, "N": w.N,
                       "bitmap_bytes": mask.numel() * 4, "kept_tiles": nnz, "algorithmic_bytes": nbytes},
-           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
-                        "frac": round(gbs / 8000.0, 4), "traffic": None,
+           "roofline": {"bound": "hbm", "achieved": sig(gbs), "peak": 8000.0, "unit": "GB/s",
+                        "frac": sig(gbs / 8000.0), "traffic": None,
                         "kernel": "compact_count_kernel + scan_groups_kernel + compact_fill_kernel"}}
     print(json.dumps(rec), flush=True)
 

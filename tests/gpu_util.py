@@ -67,13 +67,16 @@ def small_workload(name, L, d, M, N, dtype="bf16", H=2, p=0.3, diag=True, seed=7
                       W.MaskRecipe("hash", p_near=p, p_far=p, force_diag=diag), seed)
 
 
-def full_compare(w: W.Workload, bits: np.ndarray, case: str):
-    """GPU vs oracle on every row of a small workload."""
+def full_compare(w: W.Workload, bits: np.ndarray, case: str, scale: float | None = None):
+    """GPU vs oracle on every row of a small workload (scale: the workload's
+    1/sqrt(d) unless given)."""
     import torch
-    say(f"{case}: B={w.B} H={w.H} L={w.L} d={w.d} M={w.M} N={w.N} {w.dtype} seed={w.seed}")
+    scale = w.scale if scale is None else scale
+    say(f"{case}: B={w.B} H={w.H} L={w.L} d={w.d} M={w.M} N={w.N} {w.dtype} seed={w.seed} "
+        f"scale={scale}")
     q, k, v = W.make_qkv(w)
-    o, lse = gpu_attention(q.cuda(), k.cuda(), v.cuda(), to_dev_mask(bits), w.M, w.N, w.scale)
-    ro, rl = oracle.attention(q, k, v, bits, w.M, w.N, w.scale)
+    o, lse = gpu_attention(q.cuda(), k.cuda(), v.cuda(), to_dev_mask(bits), w.M, w.N, scale)
+    ro, rl = oracle.attention(q, k, v, bits, w.M, w.N, scale)
     return compare(case, o.float().cpu().numpy(), ro, w.dtype, lse.cpu().numpy(), rl)
 
 
@@ -87,6 +90,8 @@ def sampled_compare(w: W.Workload, q, k, v, o_dev, lse_dev, bits_rows, tiles, he
     o_host = o_dev.float().cpu().numpy()
     l_host = lse_dev.cpu().numpy()
     for h in heads:
+        if len(heads) > 4 and h % 8 == 0:
+            say(f"{case}: oracle head {h} of {len(heads)}")
         rows, ro, rl = oracle.attention_rows(q[0, h], k[0, h], v[0, h], bits_rows(0, h), w.M, w.N,
                                              w.scale, tiles[0, h])
         errs.append((o_host[0, h, rows], ro, l_host[0, h, rows], rl))

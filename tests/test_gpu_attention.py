@@ -168,3 +168,14 @@ def test_multi_batch_heads():
     w = W.Workload("bh", 2, 3, 500, 128, 16, 8, "bf16",
                    W.MaskRecipe("hash", p_near=0.35, p_far=0.35), 23)
     full_compare(w, W.mask_bits(w), "bf16 B=2 H=3 16x8 L=500")
+
+
+@pytest.mark.parametrize("dtype,d,N", [("bf16", 128, 8), ("bf16", 128, 16), ("bf16", 128, 1),
+                                       ("bf16", 64, 1), ("f32", 64, 16), ("f32", 128, 8)])
+def test_negative_scale(dtype, d, N):
+    torch_or_skip()
+    # A negative scale flips the sign of every logit; the bf16 kernels take it
+    # by negating Q (exact), the f32 kernel by the signed scale.  Both the
+    # octet kernel (N >= 8) and the key kernel (N < 8) are reached.
+    w = small_workload(f"neg_{dtype}_{d}_{N}", 1000, d, 16, N, dtype=dtype, p=0.4, seed=61 + d + N)
+    full_compare(w, _hash_bits(w), f"{dtype} d{d} 16x{N} L=1000 scale<0", scale=-w.scale)

@@ -1,8 +1,11 @@
 """The benchmark's output contract on the GPU, on the tiny workload (1x2x512x64,
 fp32, 16x16 tiles): one JSON line on stdout with the fields the measurement
 relies on, for the forward line and the compaction and mask-diff lines.  The
-kept-tile counts it reports are checked against the host generator's mask."""
+kept-tile counts it reports are checked against the host generator's mask.
+The file name sorts after every parity file, so a failure here never hides a
+parity test in a run that stops at the first failure."""
 import json
+import math
 import os
 import subprocess
 import sys
@@ -36,7 +39,10 @@ def _bench(*argv):
     rec = json.loads(lines[0])
     assert KEYS <= rec.keys()
     assert rec["n_gpus"] == 1 and rec["steps"] == 3 and rec["warmup"] == 1
-    assert rec["value"] > 0 and rec["ms_per_step"] > 0
+    # what the bench guarantees: a measured time, and a rate that is finite and
+    # not negative (a tiny workload's rate may be small)
+    assert rec["ms_per_step"] > 0
+    assert math.isfinite(rec["value"]) and rec["value"] >= 0
     roof = rec["roofline"]
     assert {"bound", "achieved", "peak", "unit", "frac", "traffic"} <= roof.keys()
     assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], rel=1e-3, abs=1e-4)

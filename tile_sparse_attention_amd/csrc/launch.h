@@ -1,4 +1,4 @@
-// Kernel launchers called by the C ABI layer (api.cpp).  Each returns the
+// Kernel launchers called by the C ABI layer (api.hip).  Each returns the
 // launch status; arguments were validated by the caller.
 #pragma once
 
