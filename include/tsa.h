@@ -94,6 +94,26 @@ tsa_status_t tsa_attention_fwd(const tsa_problem_t* p,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* tsa_attention_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Arguments, layouts, results and errors
+ * are those of tsa_attention_fwd; the workspace it would take
+ * (tsa_workspace_size(TSA_OP_ATTENTION_FWD)) lives instead in a static device
+ * array of 64 MiB that the library holds on every GPU it runs on until the
+ * process ends.  A problem that needs more (at d = 128, bf16: about
+ * B*H*L > 250 000, e.g. 5 heads at L = 32760 fit) returns
+ * TSA_ERR_UNSUPPORTED and enqueues nothing.  The call allocates nothing:
+ * the array's device address is looked up once per device, with that device
+ * current, on the first call.  The GPU is the current device, which must be
+ * the stream's.  All calls on one GPU share the array: calls that overlap on
+ * one GPU (other streams, other threads) race and give wrong results;
+ * calls ordered on one stream are safe, and every call rewrites all of the
+ * scratch it reads. */
+tsa_status_t tsa_attention_fwd_noalloc(const tsa_problem_t* p,
+                                       const void* q, const void* k, const void* v,
+                                       const uint32_t* mask_bits, float scale,
+                                       void* o, float* lse, void* stream);
+
 /* FP8 inputs of tsa_attention_fwd_fp8: q and k (bf16 [B,H,L,128]) as e4m3
  * bytes (OCP format: 4 exponent bits, bias 7, 3 mantissa bits, largest value
  * 448) with per-tile scales: q_scale [B,H,ceil(L/16)] fp32, one per 16-row tile

@@ -206,3 +206,22 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(T, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="missing"):
         T.lib()
+
+
+def _noalloc(pr, q=1, k=2, v=3, m=4, o=5, scale=1.0):
+    def p(x):
+        return ctypes.c_void_p(0x10000 * x) if x else ctypes.c_void_p(0)
+    return T.lib().tsa_attention_fwd_noalloc(ctypes.byref(pr), p(q), p(k), p(v), p(m),
+                                             ctypes.c_float(scale), p(o), None, None)
+
+
+def test_noalloc_forward_validates_before_touching_the_gpu():
+    pr = T.problem(1, 2, 512, 64, 16, 16, T.DTYPE_F32)
+    assert _noalloc(pr, q=0) == T.ERR_INVALID_ARGUMENT
+    assert _noalloc(pr, o=1) == T.ERR_INVALID_ARGUMENT          # aliases q
+    assert _noalloc(pr, scale=float("nan")) == T.ERR_INVALID_ARGUMENT
+    bad = T.problem(1, 2, 512, 96, 16, 16)
+    assert _noalloc(bad) == T.ERR_UNSUPPORTED
+    # beyond the 64 MiB scratch (about 338 MB of workspace): refused, nothing enqueued
+    big = T.problem(1, 40, 32760, 128, 16, 8)
+    assert _noalloc(big) == T.ERR_UNSUPPORTED and "scratch" in T.last_error()

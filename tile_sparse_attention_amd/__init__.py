@@ -56,6 +56,7 @@ _SIGS = {
     "tsa_workspace_size": (ctypes.c_int, [ctypes.c_int, _PP, ctypes.POINTER(ctypes.c_size_t)]),
     "tsa_attention_fwd": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP, _VP,
                                          ctypes.c_size_t, _VP]),
+    "tsa_attention_fwd_noalloc": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP, _VP]),
     "tsa_attention_bwd": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_float,
                                          _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     "tsa_mask_compact": (ctypes.c_int, [_PP, _VP, _VP, _VP, ctypes.c_int64, _VP, ctypes.c_size_t,
@@ -147,6 +148,21 @@ def _workspace(op: int, pr: Problem, device):
     return _torch().empty(n, dtype=_torch().uint8, device=device), n
 
 
+def _check_fwd_args(q, k, v, mask_bits, M, N, out, lse):
+    torch = _torch()
+    B, H, L, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or out.shape != q.shape:
+        raise TsaError(ERR_INVALID_ARGUMENT, "q, k, v, out must have one shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
+        raise TsaError(ERR_INVALID_ARGUMENT, "q, k, v, out must have one dtype")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L)):
+        raise TsaError(ERR_INVALID_ARGUMENT, "lse must be float32 [B, H, L]")
+    T_q = -(-L // M)
+    if mask_bits.dtype not in (torch.int32, torch.uint32) or \
+            tuple(mask_bits.shape) != (B, H, T_q, mask_row_words(L, N)):
+        raise TsaError(ERR_INVALID_ARGUMENT, "mask_bits must be int32/uint32 [B, H, T_q, words]")
+
+
 def attention_fwd(q, k, v, mask_bits, M: int, N: int, scale: float | None = None, *,
                   out=None, return_lse: bool = False, workspace=None):
     """O (and optionally LSE) of tile-sparse attention; q, k, v: [B, H, L, d].
@@ -162,14 +178,7 @@ def attention_fwd(q, k, v, mask_bits, M: int, N: int, scale: float | None = None
         out = torch.empty_like(q)
     lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if return_lse else None
     _need_cuda(q, k, v, mask_bits, out, lse)
-    if k.shape != q.shape or v.shape != q.shape or out.shape != q.shape:
-        raise TsaError(ERR_INVALID_ARGUMENT, "q, k, v, out must have one shape")
-    if k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
-        raise TsaError(ERR_INVALID_ARGUMENT, "q, k, v, out must have one dtype")
-    T_q = -(-L // M)
-    if mask_bits.dtype not in (torch.int32, torch.uint32) or \
-            tuple(mask_bits.shape) != (B, H, T_q, mask_row_words(L, N)):
-        raise TsaError(ERR_INVALID_ARGUMENT, "mask_bits must be int32/uint32 [B, H, T_q, words]")
+    _check_fwd_args(q, k, v, mask_bits, M, N, out, lse)
     pr = Problem(B, H, L, d, M, N, _dtype_code(q))
     if workspace is None:
         ws, nws = _workspace(OP_ATTENTION_FWD, pr, q.device)
@@ -180,6 +189,22 @@ def attention_fwd(q, k, v, mask_bits, M: int, N: int, scale: float | None = None
                                    ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(ws), nws,
                                    _stream()))
     return (out, lse) if return_lse else out
+
+
+def attention_fwd_noalloc(q, k, v, mask_bits, M: int, N: int, scale: float | None = None, *,
+                          out, lse=None):
+    """tsa_attention_fwd_noalloc: O (and LSE when `lse` is given) written into
+    the caller's tensors, with the library's static scratch instead of a
+    workspace; the call allocates nothing, so `out` (and `lse`) are required."""
+    B, H, L, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _need_cuda(q, k, v, mask_bits, out, lse)
+    _check_fwd_args(q, k, v, mask_bits, M, N, out, lse)
+    pr = Problem(B, H, L, d, M, N, _dtype_code(q))
+    _check(lib().tsa_attention_fwd_noalloc(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(mask_bits),
+                                           ctypes.c_float(scale), _ptr(out), _ptr(lse), _stream()))
+    return (out, lse) if lse is not None else out
 
 
 def quantize_qk_fp8(q, k):

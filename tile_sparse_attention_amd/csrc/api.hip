@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "launch.h"
 #include "tsa.h"
@@ -78,6 +79,69 @@ long long n_rows(const tsa_problem_t* p) {
   return (long long)p->B * p->H * ((p->L + p->M - 1) / p->M);
 }
 
+// Argument checks of the forward, shared by its two entry points.
+tsa_status_t check_fwd(const tsa_problem_t* p, const void* q, const void* k, const void* v,
+                       const uint32_t* mask_bits, float scale, const void* o, const float* lse) {
+  tsa_status_t s = check_problem(p, true);
+  if (s != TSA_OK) return s;
+  if (!q || !k || !v || !mask_bits || !o)
+    return fail(TSA_ERR_INVALID_ARGUMENT, "q, k, v, mask_bits and o must be non-NULL");
+  if (!std::isfinite(scale)) return fail(TSA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(mask_bits, 4) || (lse && !aligned(lse, 4)))
+    return fail(TSA_ERR_INVALID_ARGUMENT, "q/k/v/o need 16-byte, mask/lse 4-byte alignment");
+  if (o == q || o == k || o == v) return fail(TSA_ERR_INVALID_ARGUMENT, "o aliases an input");
+  const long long blocks = (long long)p->B * p->H * ((p->L + 63) / 64);
+  if (blocks > kMaxGrid) return fail(TSA_ERR_UNSUPPORTED, "grid too large");
+  return TSA_OK;
+}
+
+tsa_status_t launch_fwd(const tsa_problem_t* p, const void* q, const void* k, const void* v,
+                        const uint32_t* mask_bits, float scale, void* o, float* lse, void* workspace,
+                        void* stream) {
+  tsa::AttnLaunch a{p, q, k, v, mask_bits, scale, o, lse, workspace, static_cast<hipStream_t>(stream)};
+  const hipError_t e = p->dtype == TSA_DTYPE_BF16 ? tsa::launch_attention_bf16(a)
+                                                  : tsa::launch_attention_f32(a);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  return TSA_OK;
+}
+
+// Scratch of tsa_attention_fwd_noalloc: the forward's workspace (packed V^T
+// and the chunk-skip words) for callers that cannot allocate.  Every GPU the
+// library runs on holds its own copy until the process ends; calls on one GPU
+// share it.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's copy of `scratch`, looked up once per device
+// with that device current (the array's name is not a device address in host
+// code).
+tsa_status_t scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(TSA_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr || !aligned(ptr, 256)) return fail(TSA_ERR_HIP, "scratch has no usable address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -116,27 +180,28 @@ tsa_status_t tsa_workspace_size(tsa_op_t op, const tsa_problem_t* p, size_t* byt
 tsa_status_t tsa_attention_fwd(const tsa_problem_t* p, const void* q, const void* k, const void* v,
                                const uint32_t* mask_bits, float scale, void* o, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  tsa_status_t s = check_problem(p, true);
+  tsa_status_t s = check_fwd(p, q, k, v, mask_bits, scale, o, lse);
   if (s != TSA_OK) return s;
-  if (!q || !k || !v || !mask_bits || !o)
-    return fail(TSA_ERR_INVALID_ARGUMENT, "q, k, v, mask_bits and o must be non-NULL");
-  if (!std::isfinite(scale)) return fail(TSA_ERR_INVALID_ARGUMENT, "scale is not finite");
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(mask_bits, 4) || (lse && !aligned(lse, 4)))
-    return fail(TSA_ERR_INVALID_ARGUMENT, "q/k/v/o need 16-byte, mask/lse 4-byte alignment");
-  if (o == q || o == k || o == v) return fail(TSA_ERR_INVALID_ARGUMENT, "o aliases an input");
   const size_t need = tsa::attention_workspace_bytes(p);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
     return fail(TSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, 256-byte aligned (got %zu)",
                 need, workspace_bytes);
-  const long long blocks = (long long)p->B * p->H * ((p->L + 63) / 64);
-  if (blocks > kMaxGrid) return fail(TSA_ERR_UNSUPPORTED, "grid too large");
-  tsa::AttnLaunch a{p, q, k, v, mask_bits, scale, o, lse, workspace,
-                    static_cast<hipStream_t>(stream)};
-  const hipError_t e = p->dtype == TSA_DTYPE_BF16 ? tsa::launch_attention_bf16(a)
-                                                  : tsa::launch_attention_f32(a);
-  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
-  return TSA_OK;
+  return launch_fwd(p, q, k, v, mask_bits, scale, o, lse, workspace, stream);
+}
+
+tsa_status_t tsa_attention_fwd_noalloc(const tsa_problem_t* p, const void* q, const void* k,
+                                       const void* v, const uint32_t* mask_bits, float scale, void* o,
+                                       float* lse, void* stream) {
+  tsa_status_t s = check_fwd(p, q, k, v, mask_bits, scale, o, lse);
+  if (s != TSA_OK) return s;
+  const size_t need = tsa::attention_workspace_bytes(p);
+  if (need > kScratchBytes)
+    return fail(TSA_ERR_UNSUPPORTED,
+                "problem needs %zu bytes of scratch; tsa_attention_fwd_noalloc holds at most %zu "
+                "(call tsa_attention_fwd with a workspace instead)", need, kScratchBytes);
+  void* ws = nullptr;
+  if ((s = scratch_for_current_device(&ws)) != TSA_OK) return s;
+  return launch_fwd(p, q, k, v, mask_bits, scale, o, lse, ws, stream);
 }
 
 tsa_status_t tsa_quantize_qk_fp8(const tsa_problem_t* p, const void* q, const void* k, uint8_t* q8,
