@@ -147,9 +147,33 @@ def cpu_baseline(w, q, k, v, mask, budget_s=20.0):
         secs += time.perf_counter() - t0
     n = per_head * len(heads)
     return {"value": kept / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "blas": blas_name(),
             "sample": f"{per_head} sampled query tiles per head x {len(heads)} heads ({n} tiles, "
                       f"{n * w.M} query rows) against all {w.L} keys, fp64 numpy, {secs:.1f} s; "
                       f"kept FLOPs of those rows / time"}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def blas_name() -> str:
+    """numpy's BLAS library and version, as numpy reports them."""
+    import numpy as np
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:  # older numpy without mode="dicts"
+        return "unknown"
 
 
 def traffic_for(workload: str, sha: str):

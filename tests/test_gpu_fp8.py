@@ -2,7 +2,18 @@
 against the oracle's (oracle/fp8.py), and FP8-score attention matches the
 float64 oracle applied to the dequantised Q and K (V in bf16) within the
 bf16 path's tolerance: the arithmetic after quantisation is the bf16 path's
-(fp32 accumulation, probabilities rounded to bf16, O stored in bf16)."""
+(fp32 accumulation, probabilities rounded to bf16, O stored in bf16).
+
+The quantisation's own error, against the float64 oracle on the unquantised
+inputs, is bounded for N(0,1) Q, K, V at scale 1/sqrt(d) by this arithmetic:
+rounding to e4m3 (3 mantissa bits) leaves a relative error of at most 2^-4
+per element, RMS at most 2^-4/sqrt(3) = 0.036; a score q.k*scale then moves by
+sigma_s = scale * sqrt(2 d E[q^2 k^2]) * 0.036 = 0.051 RMS (d = 128).  An
+output element sum_j p_j v_j moves by about sigma_s * sqrt(sum_j p_j^2) *
+sigma_v <= sigma_s, since sum_j p_j^2 <= 1 and sigma_v = 1.  So max-abs
+<= 6 sigma_s = 0.31 and mean-abs <= 0.8 sigma_s = 0.041 (the mean-abs of a
+normal of that RMS).  Sharper logits (the x8 case) are outside this bound
+and only printed."""
 import numpy as np
 import pytest
 
@@ -41,7 +52,10 @@ def test_quantize_bit_exact(L):
     assert np.array_equal(_e4m3_values(q8), rq) and np.array_equal(_e4m3_values(k8), rk)
 
 
-def _run(w, bits, case, scale=None, q=None, k=None, v=None):
+UNQUANTISED_TOL = dict(max_abs=0.31, mean_abs=0.041)
+
+
+def _run(w, bits, case, scale=None, q=None, k=None, v=None, normal_inputs=True):
     import tile_sparse_attention_amd as T
     torch = torch_or_skip()
     say(f"{case}: B={w.B} H={w.H} L={w.L} M={w.M} N={w.N} seed={w.seed}")
@@ -65,6 +79,8 @@ def _run(w, bits, case, scale=None, q=None, k=None, v=None):
           f"vs unquantised oracle max_abs={qerr.max():.3e} mean_abs={qerr.mean():.3e}", flush=True)
     assert np.all(np.isfinite(got))
     assert mx <= TOL["bf16"]["max_abs"] and mean <= TOL["bf16"]["mean_abs"]
+    if normal_inputs:
+        assert qerr.max() <= UNQUANTISED_TOL["max_abs"] and qerr.mean() <= UNQUANTISED_TOL["mean_abs"]
     fin = np.isfinite(rl)
     gl = lse.cpu().numpy()
     assert np.array_equal(np.isfinite(gl), fin)
@@ -93,7 +109,7 @@ def test_fp8_attention_large_logits_and_empty_rows():
     keep = W.mask_rows_bool(w, np.array([(0, h, i) for h in range(2) for i in range(w.T_q)]))
     keep = keep.reshape(1, 2, w.T_q, w.T_k)
     keep[0, 1, ::4] = False
-    _run(w, W.pack_bits(keep), "fp8 16x8 logits x8, empty rows", q=q, k=k, v=v)
+    _run(w, W.pack_bits(keep), "fp8 16x8 logits x8, empty rows", q=q, k=k, v=v, normal_inputs=False)
 
 
 def test_fp8_rejects_unsupported_shapes():

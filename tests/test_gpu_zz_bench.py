@@ -62,6 +62,7 @@ def test_forward_line_with_cpu_baseline():
     rec = _bench("--workload", "tiny", "--steps", "3", "--warmup", "1", "--no-dense")
     cb = rec["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    assert cb["cpu_model"] and cb["blas"]
 
 
 def test_compaction_line():
