@@ -94,24 +94,39 @@ def kept_flops_device(w, mask) -> int:
     return int(4 * w.d * (keys * m).sum().item())
 
 
-def time_calls(fn, steps, warmup):
-    """(ms per step over the bracketed region, mean per-call ms from events)."""
+def time_calls(fn, steps, warmup, kernel_events=False):
+    """(ms per step over the bracketed region, mean per-call ms from events,
+    min per-call ms); with kernel_events also the mean ms of the attention
+    kernels proper, from events the library records around them on the same
+    stream (tsa_set_timing_events)."""
     import torch
+
+    import tile_sparse_attention_amd as T
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)] if kernel_events else None
     t0 = time.perf_counter()
-    for a, b in ev:
+    for i, (a, b) in enumerate(ev):
+        if kev is not None:
+            T.set_timing_events(*kev[i])
         a.record(stream)
         fn()
         b.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3
+    if kev is not None:
+        T.set_timing_events(None, None)
     per = [a.elapsed_time(b) for a, b in ev]
-    return wall / steps, sum(per) / len(per), min(per)
+    out = (wall / steps, sum(per) / len(per), min(per))
+    if kev is not None:
+        kern = [a.elapsed_time(b) for a, b in kev]
+        out = out + (sum(kern) / len(kern),)
+    return out
 
 
 def cpu_baseline(w, q, k, v, mask, budget_s=20.0):
@@ -263,7 +278,7 @@ def bench_fp8(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws):
     def step():
         T.attention_fwd_fp8(q8, k8, qs, ks, vd, mask, w.M, w.N, w.scale, out=out, workspace=ws)
 
-    ms_step, ms_kernel, ms_min = time_calls(step, args.steps, args.warmup)
+    ms_step, ms_call, ms_min, ms_kernel = time_calls(step, args.steps, args.warmup, kernel_events=True)
     tflops = flops / (ms_step * 1e-3) / 1e12
     # half of the kept FLOPs (QK^T) run at the FP8 peak, half (PV) at the bf16 peak
     peak = 2.0 / (1.0 / 5000.0 + 1.0 / PEAK_TFLOPS["bf16"])
@@ -446,10 +461,10 @@ def main():
     def step():
         T.attention_fwd(qd, kd, vd, mask, w.M, w.N, w.scale, out=out, workspace=ws)
 
-    ms_step, ms_kernel, ms_min = time_calls(step, args.steps, args.warmup)
+    ms_step, ms_call, ms_min, ms_kernel = time_calls(step, args.steps, args.warmup, kernel_events=True)
     tflops = flops / (ms_step * 1e-3) / 1e12
-    log(f"sparse: {ms_step:.3f} ms/step, kernel mean {ms_kernel:.3f} ms (min {ms_min:.3f}), "
-        f"{tflops:.1f} TFLOP/s")
+    log(f"sparse: {ms_step:.3f} ms/step, call mean {ms_call:.3f} ms (min {ms_min:.3f}), attention "
+        f"kernels {ms_kernel:.3f} ms, {tflops:.1f} TFLOP/s")
     peak = PEAK_TFLOPS[w.dtype]
     cfg = {"workload": name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "M": w.M, "N": w.N,
            "mask": w.description, "kept_fraction": round(flops / dense_flops, 6),
@@ -485,7 +500,8 @@ def main():
     sha = kernel_sha()
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic_for(name, sha),
-            "kernel": kernel_name(w), "kernel_sha": sha}
+            "kernel": kernel_name(w), "kernel_ms": round(ms_kernel, 4), "call_ms": round(ms_call, 4),
+            "kernel_sha": sha}
     rec = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

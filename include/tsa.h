@@ -114,6 +114,17 @@ tsa_status_t tsa_attention_fwd_noalloc(const tsa_problem_t* p,
                                        const uint32_t* mask_bits, float scale,
                                        void* o, float* lse, void* stream);
 
+/* Measurement hook: the forward calls made afterwards by this thread
+ * (tsa_attention_fwd, tsa_attention_fwd_noalloc, tsa_attention_fwd_fp8)
+ * record start_event on their stream right before the attention kernel(s)
+ * proper and stop_event right after them, so that hipEventElapsedTime gives the
+ * kernels' time without the V^T pack and the chunk pre-pass that the call
+ * also enqueues.  Both are hipEvent_t handles created by the caller, passed
+ * as void*; NULL, NULL switches recording off (the default).  Giving only one
+ * returns TSA_ERR_INVALID_ARGUMENT.  The events must outlive the calls that
+ * record them. */
+tsa_status_t tsa_set_timing_events(void* start_event, void* stop_event);
+
 /* FP8 inputs of tsa_attention_fwd_fp8: q and k (bf16 [B,H,L,128]) as e4m3
  * bytes (OCP format: 4 exponent bits, bias 7, 3 mantissa bits, largest value
  * 448) with per-tile scales: q_scale [B,H,ceil(L/16)] fp32, one per 16-row tile

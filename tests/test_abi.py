@@ -225,3 +225,10 @@ def test_noalloc_forward_validates_before_touching_the_gpu():
     # beyond the 64 MiB scratch (about 338 MB of workspace): refused, nothing enqueued
     big = T.problem(1, 40, 32760, 128, 16, 8)
     assert _noalloc(big) == T.ERR_UNSUPPORTED and "scratch" in T.last_error()
+
+
+def test_timing_events_need_both_or_neither():
+    lib = T.lib()
+    assert lib.tsa_set_timing_events(ctypes.c_void_p(0x1000), None) == T.ERR_INVALID_ARGUMENT
+    assert lib.tsa_set_timing_events(None, ctypes.c_void_p(0x1000)) == T.ERR_INVALID_ARGUMENT
+    assert lib.tsa_set_timing_events(None, None) == T.OK

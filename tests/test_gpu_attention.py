@@ -179,3 +179,28 @@ def test_negative_scale(dtype, d, N):
     # octet kernel (N >= 8) and the key kernel (N < 8) are reached.
     w = small_workload(f"neg_{dtype}_{d}_{N}", 1000, d, 16, N, dtype=dtype, p=0.4, seed=61 + d + N)
     full_compare(w, _hash_bits(w), f"{dtype} d{d} 16x{N} L=1000 scale<0", scale=-w.scale)
+
+
+def test_timing_events_bracket_the_attention_kernels():
+    torch = torch_or_skip()
+    import tile_sparse_attention_amd as T
+    # events recorded around the attention kernels proper: same results, and
+    # their span lies inside the whole call's
+    w = small_workload("tev", 3000, 128, 16, 8, H=4, p=0.3, seed=91)
+    say("timing events bf16 16x8 L=3000")
+    q, k, v = (x.cuda() for x in W.make_qkv(w))
+    m = to_dev_mask(W.mask_bits(w))
+    o1 = T.attention_fwd(q, k, v, m, 16, 8, w.scale)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    T.set_timing_events(a, b)
+    try:
+        c0.record()
+        o2 = T.attention_fwd(q, k, v, m, 16, 8, w.scale)
+        c1.record()
+    finally:
+        T.set_timing_events(None, None)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    kern, call = a.elapsed_time(b), c0.elapsed_time(c1)
+    assert 0 < kern <= call

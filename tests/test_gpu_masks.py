@@ -185,3 +185,32 @@ def test_mask_diff_wan480_fine_consecutive_masks():
     r_ref, h_ref = oracle.mask_diff(a, b, w.T_k)
     assert np.array_equal(rows.cpu().numpy(), r_ref)
     assert np.array_equal(heads.cpu().numpy(), h_ref)
+
+
+@pytest.mark.parametrize("shift", [1, 2, 3])
+def test_compaction_into_a_list_not_16_byte_aligned(shift):
+    """col_idx at 4-byte but not 16-byte alignment (the fill stores aligned
+    16-byte runs, so its alignment follows the list's address), with a
+    capacity that clips inside a run; the slots around the list stay intact."""
+    torch = torch_or_skip()
+    import ctypes
+
+    import tile_sparse_attention_amd as T
+    w = W.Workload("c", 2, 3, 1000, 64, 16, 1, "bf16", W.MaskRecipe("hash", p_near=0.3, p_far=0.3), 15)
+    say(f"compaction col_idx offset {shift} ints")
+    bits = W.mask_bits(w)
+    orp, oci = oracle.compact(bits, w.T_k)
+    nnz = int(orp[-1])
+    cap = nnz - 5
+    buf = torch.full((nnz + 8,), -7, dtype=torch.int32, device="cuda")
+    rp = torch.empty(orp.size, dtype=torch.int64, device="cuda")
+    m = to_dev_mask(bits)
+    pr = T.problem(w.B, w.H, w.L, 0, w.M, w.N)
+    ws, nws = T._workspace(T.OP_MASK_COMPACT, pr, m.device)
+    T._check(T.lib().tsa_mask_compact(ctypes.byref(pr), T._ptr(m), T._ptr(rp),
+                                      ctypes.c_void_p(buf.data_ptr() + 4 * shift), cap, T._ptr(ws), nws,
+                                      T._stream()))
+    got = buf.cpu().numpy()
+    assert np.array_equal(rp.cpu().numpy(), orp)
+    assert np.array_equal(got[shift:shift + cap], oci[:cap])
+    assert np.all(got[:shift] == -7) and np.all(got[shift + cap:] == -7)

@@ -70,6 +70,7 @@ _SIGS = {
     "tsa_quantize_qk_fp8": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "tsa_attention_fwd_fp8": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP,
                                              _VP, ctypes.c_size_t, _VP]),
+    "tsa_set_timing_events": (ctypes.c_int, [_VP, _VP]),
     "tsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tsa_last_error": (ctypes.c_char_p, []),
 }
@@ -205,6 +206,16 @@ def attention_fwd_noalloc(q, k, v, mask_bits, M: int, N: int, scale: float | Non
     _check(lib().tsa_attention_fwd_noalloc(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(mask_bits),
                                            ctypes.c_float(scale), _ptr(out), _ptr(lse), _stream()))
     return (out, lse) if lse is not None else out
+
+
+def set_timing_events(start=None, stop=None):
+    """Record torch.cuda.Event `start` / `stop` around the attention kernels of
+    the forward calls that follow (None, None: off)."""
+    for e in (start, stop):
+        if e is not None and not e.cuda_event:
+            e.record()   # torch creates the HIP event on its first record
+    _check(lib().tsa_set_timing_events(ctypes.c_void_p(start.cuda_event) if start is not None else None,
+                                       ctypes.c_void_p(stop.cuda_event) if stop is not None else None))
 
 
 def quantize_qk_fp8(q, k):

@@ -33,6 +33,9 @@ hipError_t launch_mask_diff(const tsa_problem_t* p, const uint32_t* a, const uin
 namespace {
 
 thread_local char g_err[512] = "";
+// events of tsa_set_timing_events, used by the forward calls of this thread
+thread_local hipEvent_t g_ev_start = nullptr;
+thread_local hipEvent_t g_ev_stop = nullptr;
 
 tsa_status_t fail(tsa_status_t s, const char* fmt, ...) {
   va_list ap;
@@ -100,6 +103,8 @@ tsa_status_t launch_fwd(const tsa_problem_t* p, const void* q, const void* k, co
                         const uint32_t* mask_bits, float scale, void* o, float* lse, void* workspace,
                         void* stream) {
   tsa::AttnLaunch a{p, q, k, v, mask_bits, scale, o, lse, workspace, static_cast<hipStream_t>(stream)};
+  a.ev_start = g_ev_start;
+  a.ev_stop = g_ev_stop;
   const hipError_t e = p->dtype == TSA_DTYPE_BF16 ? tsa::launch_attention_bf16(a)
                                                   : tsa::launch_attention_f32(a);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
@@ -248,6 +253,8 @@ tsa_status_t tsa_attention_fwd_fp8(const tsa_problem_t* p, const uint8_t* q8, co
   tsa::AttnLaunch a{p, q8, k8, v, mask_bits, scale, o, lse, workspace, static_cast<hipStream_t>(stream)};
   a.q_scale = q_scale;
   a.k_scale = k_scale;
+  a.ev_start = g_ev_start;
+  a.ev_stop = g_ev_stop;
   const hipError_t e = tsa::launch_attention_fp8(a);
   if (e != hipSuccess) return hip_fail(e, "FP8 attention kernel launch");
   return TSA_OK;
@@ -380,6 +387,14 @@ tsa_status_t tsa_maskgen_structured(const tsa_problem_t* p, const tsa_structured
   const hipError_t e = tsa::launch_maskgen_structured(p, g, head_pattern, mask_out,
                                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mask generator launch");
+  return TSA_OK;
+}
+
+tsa_status_t tsa_set_timing_events(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(TSA_ERR_INVALID_ARGUMENT, "give both events or neither");
+  g_ev_start = static_cast<hipEvent_t>(start_event);
+  g_ev_stop = static_cast<hipEvent_t>(stop_event);
   return TSA_OK;
 }
 

@@ -47,8 +47,10 @@ hipError_t launch_attn_cfg(const AttnLaunch& a) {
   const AttnParams p = attn_params(a, 16 * TPW * W);
   const long long blocks = (long long)a.p->B * a.p->H * p.n_qblocks;
   launch_vt_pack<T, D>(a, p);
+  mark_event(a.ev_start, a.stream);
   hipLaunchKernelGGL((attn_fwd_kernel<T, D, N, KC, W, TPW>), dim3((unsigned)blocks), dim3(64 * W), 0,
                      a.stream, p);
+  mark_event(a.ev_stop, a.stream);
   return hipGetLastError();
 }
 
@@ -63,8 +65,10 @@ hipError_t launch_attn_oct(const AttnLaunch& a) {
   const long long blocks = (long long)a.p->B * a.p->H * p.n_qblocks;
   launch_vt_pack<bf16_t, D>(a, p);
   if (!attention_skips_chunks(a.p)) {
+    mark_event(a.ev_start, a.stream);
     hipLaunchKernelGGL((attn_oct_kernel<D, N, false, F8>), dim3((unsigned)blocks), dim3(64 * C::W), 0,
                        a.stream, p);
+    mark_event(a.ev_stop, a.stream);
     return hipGetLastError();
   }
   uint32_t* need = reinterpret_cast<uint32_t*>(static_cast<char*>(a.workspace) +
@@ -77,10 +81,12 @@ hipError_t launch_attn_oct(const AttnLaunch& a) {
   hipLaunchKernelGGL(zero_word_kernel<uint32_t>, dim3(1), dim3(64), 0, a.stream, count);
   hipLaunchKernelGGL((chunk_need_kernel<N>), dim3((unsigned)blocks), dim3(256), 0, a.stream, p, need, flag,
                      count);
+  mark_event(a.ev_start, a.stream);
   hipLaunchKernelGGL((attn_oct_kernel<D, N, false, F8>), dim3((unsigned)blocks), dim3(64 * C::W), 0, a.stream,
                      p);
   hipLaunchKernelGGL((attn_oct_kernel<D, N, true, F8>), dim3((unsigned)blocks), dim3(64 * C::W), 0, a.stream,
                      p);
+  mark_event(a.ev_stop, a.stream);
   return hipGetLastError();
 }
 
@@ -91,7 +97,9 @@ hipError_t launch_attn_key(const AttnLaunch& a) {
   using C = KeyCfg<D, N>;
   const AttnParams p = attn_params(a, C::ROWS);
   const long long blocks = (long long)a.p->B * a.p->H * p.n_qblocks;
+  mark_event(a.ev_start, a.stream);
   hipLaunchKernelGGL((attn_key_kernel<D, N>), dim3((unsigned)blocks), dim3(64 * C::W), 0, a.stream, p);
+  mark_event(a.ev_stop, a.stream);
   return hipGetLastError();
 }
 

@@ -23,7 +23,15 @@ struct AttnLaunch {
   // FP8 scores: q and k hold e4m3 bytes with these scales (null otherwise)
   const float* q_scale = nullptr;
   const float* k_scale = nullptr;
+  // when set, recorded on `stream` right before and right after the attention
+  // kernel(s) proper (not the V^T pack or the chunk pre-pass)
+  hipEvent_t ev_start = nullptr;
+  hipEvent_t ev_stop = nullptr;
 };
+
+inline void mark_event(hipEvent_t e, hipStream_t s) {
+  if (e != nullptr) (void)hipEventRecord(e, s);
+}
 
 // Row length of the packed V^T and its size in bytes.
 inline int attention_l_pad(int L) { return (L + 127) / 128 * 128; }

@@ -11,8 +11,8 @@
 //              at a time: one coalesced load (a word per lane), a wave prefix
 //              sum of the words' popcounts for each lane's first slot, each
 //              lane's kept tiles into the wave's LDS staging area in
-//              ascending order, and from there contiguous coalesced stores,
-//              clipped at col_capacity.  A row that starts at or past
+//              ascending order (placed at the output's alignment), and from
+//              there 16-byte stores of aligned runs, clipped at col_capacity.  A row that starts at or past
 //              col_capacity (a count-only call) reads no bits at all.
 #include "tsa_device.h"
 #include "tsa.h"
@@ -33,11 +33,22 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void compact_count_kernel(const
   int cnt = 0;
   if (row < rows) {
     const uint32_t* r = mask + row * (long long)words;
-    for (int w = lane; w < words; w += 64) {
-      uint32_t x = r[w];
-      const int valid = T_k - 32 * w;
-      if (valid < 32) x &= (1u << valid) - 1u;
-      cnt += __builtin_popcount(x);
+    // eight independent loads in flight per lane: the row's words are read
+    // at the memory system's rate, not at one load latency per 256 bytes
+    for (int w0 = 0; w0 < words; w0 += 64 * 8) {
+      uint32_t x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int w = w0 + 64 * u + lane;
+        x[u] = w < words ? r[w] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int w = w0 + 64 * u + lane;
+        const int valid = T_k - 32 * w;
+        if (valid < 32) x[u] &= valid > 0 ? (1u << valid) - 1u : 0u;
+        cnt += __builtin_popcount(x[u]);
+      }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
@@ -93,7 +104,8 @@ __global__ __launch_bounds__(64 * kFillWaves) void compact_fill_kernel(
     const int32_t* __restrict__ counts, const long long* __restrict__ group_offsets,
     const long long* __restrict__ total, long long* __restrict__ row_ptr,
     int32_t* __restrict__ col_idx, long long col_capacity) {
-  __shared__ int32_t stage[kFillWaves][64 * 32];  // a block's kept tiles, per wave
+  // a block's kept tiles per wave (up to 64 * 32), after up to 3 alignment slots
+  __shared__ __attribute__((aligned(16))) int32_t stage[kFillWaves][64 * 32 + 4];
   const int wave = wave_uniform(threadIdx.x >> 6);
   const long long row = (long long)blockIdx.x * kFillWaves + wave;
   if (row >= rows) return;
@@ -127,7 +139,11 @@ __global__ __launch_bounds__(64 * kFillWaves) void compact_fill_kernel(
       const int y = __shfl_up(incl, off);
       if (lane >= off) incl += y;
     }
-    int at = incl - c;
+    // staged at the output's alignment: stage slot a + s holds output slot
+    // base + s, with a = (address of col_idx[base] / 4) mod 4, so every four
+    // stage slots 4m..4m+3 are one 16-byte-aligned run of col_idx
+    const int a = (int)((reinterpret_cast<uintptr_t>(col_idx + base) >> 2) & 3);
+    int at = a + incl - c;
     while (x != 0u) {
       const int b = __builtin_ctz(x);
       x &= x - 1u;
@@ -135,8 +151,20 @@ __global__ __launch_bounds__(64 * kFillWaves) void compact_fill_kernel(
     }
     wave_sync_lds();  // the staging writes of every lane precede the reads
     const int total_blk = __shfl(incl, 63);
-    for (int j = lane; j < total_blk; j += 64)
-      if (base + j < col_capacity) col_idx[base + j] = st[j];
+    const long long g0 = base - a;  // output slot of stage slot 0 (16-byte aligned)
+    const int end = a + total_blk;  // stage slots a .. end-1 are this block's
+    for (int m = lane; 4 * m < end; m += 64) {
+      const int s0 = 4 * m;
+      const long long gs = g0 + s0;
+      if (s0 >= a && s0 + 4 <= end && gs + 4 <= col_capacity) {
+        const int4 v = *reinterpret_cast<const int4*>(&st[s0]);
+        *reinterpret_cast<int4*>(col_idx + gs) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (s0 + e >= a && s0 + e < end && gs + e < col_capacity) col_idx[gs + e] = st[s0 + e];
+      }
+    }
     wave_sync_lds();  // ... and the reads precede the next block's writes
     base += total_blk;
   }
