@@ -79,8 +79,6 @@ template <> struct ElemTraits<bf16_t> { static constexpr int VEC = 8; };
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 
-// Fourth word of a raw (unformatted, unswizzled) buffer resource on gfx9.
-constexpr int kBufferFlags = 0x00020000;
 
 template <typename T, int D, int N, int KC, int W, int TPW>
 struct AttnCfg {

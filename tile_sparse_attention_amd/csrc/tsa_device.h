@@ -23,6 +23,9 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 typedef uint16_t bf16_t;  // storage type of bf16 elements in memory
 
+// Fourth word of a raw (unformatted, unswizzled) buffer resource on gfx9.
+constexpr int kBufferFlags = 0x00020000;
+
 __device__ __forceinline__ int lane_id() {
   return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 }
