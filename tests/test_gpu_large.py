@@ -117,3 +117,28 @@ def test_predicted_mask_config():
         return out
     say(f"large hunyuan720: oracle on {len(heads)} heads")
     sampled_compare(w, q, k, v, o, lse, head_bits, tiles, heads, "hunyuan720")
+
+
+@pytest.mark.timeout(600)
+def test_long_sequence_past_the_chunk_skip_limit():
+    """L = 300007 (2344 key chunks, above the 2048 the chunk-skipping path
+    handles, so only the plain kernel runs), 16x8 tiles, i.i.d. 10% keep with
+    the diagonal kept: 256 sampled query tiles of both heads, including the
+    last, partial one."""
+    torch_or_skip()
+    w = W.Workload("long", 1, 2, 300007, 128, 16, 8, "bf16",
+                   W.MaskRecipe("hash", p_near=0.1, p_far=0.1), 1234)
+    say("large L=300007 16x8: generating inputs")
+    q, k, v = W.make_qkv(w)
+    import tile_sparse_attention_amd as T
+    mask = T.maskgen_hash(w.B, w.H, w.L, w.M, w.N, **W.hash_params(w))
+    say("large L=300007 16x8: attention on GPU")
+    o, lse = _attn(w, q.cuda(), k.cuda(), v.cuda(), mask)
+    tiles = W.sample_tiles(w)
+    mnp = mask_to_np(mask)
+    bits = {}
+    for h in range(w.H):
+        bits[h] = _head_bits_from_rows(w, h, tiles[0, h])
+        assert np.array_equal(mnp[0, h, tiles[0, h]], bits[h][tiles[0, h]])
+    say("large L=300007 16x8: oracle on 2 heads x 256 tiles")
+    sampled_compare(w, q, k, v, o, lse, lambda b, h: bits[h], tiles, list(range(w.H)), "long L=300007")
