@@ -31,6 +31,11 @@
 //     that both reads are free of LDS bank conflicts for any octets.
 //   * The softmax denominator l comes from the same MFMA pipeline, with a
 //     constant all-ones A operand in registers.
+//   * A chunk's last pass with one or two real octets (the rest padding)
+//     forms one score block and runs PV on the 16-key 16x16x16 step, whose
+//     operands are that block's probabilities and the first V^T read of
+//     each d block: half the V^T reads and exponentials of a full pass, for
+//     the same matrix-core time.
 //   * Online softmax in base 2 with c = |scale| * log2(e) (a negative scale
 //     negates the Q fragment, which is exact).  Every score accumulator
 //     starts from -m/c, m the running reference max, so a probability costs
@@ -212,27 +217,21 @@ struct OctKernel {
     return mrow[wi < p.words ? wi : p.words - 1];
   }
 
-  // One pass over the four kept octets at list positions q0..q0+3.  Score
-  // block b (0, 1) holds the octets at positions q0+2b and q0+2b+1, eight key
-  // rows each: lane (g, n) reads row n&7 of octet oq[b] (oq[b] = the octet at
-  // position q0+2b+(n>>3)).  The score accumulators leave lane group g with
-  // keys 4(g&1)..4(g&1)+3 of octet ovx (position q0+(g>>1)) and of octet ovy
-  // (position q0+2+(g>>1)), so its PV operand is two 8-byte V^T reads.
-  // single: list positions 2 and 3 are padding; the second score block is
-  // then a copy of the first (real kept scores, multiplied by zero V^T
-  // columns), which saves its four MFMAs and K reads.
   // One pass over the four list positions q0..q0+3 (rem = entries left from
   // q0; positions >= rem are padding).  Score block b (0, 1) holds the octets
   // at positions q0+2b and q0+2b+1, eight key rows each: lane (g, n) reads
   // row n&7 of the octet at position q0+2b+(n>>3), at LDS address ka<b>.
   // The score accumulators leave lane group g with keys 4(g&1)..4(g&1)+3 of
   // octet ovx (position q0+(g>>1)) and of octet ovy (position q0+2+(g>>1)),
-  // so its PV operand is two 8-byte V^T reads.  When positions 2 and 3 are
-  // padding (rem <= 2) the second score block is a copy of the first, which
-  // saves its four MFMAs and K reads.  lim: keys of the chunk that exist.
+  // so its PV operand is two 8-byte V^T reads.  lim: keys of the chunk that
+  // exist.  SINGLE (rem <= 2: positions 2 and 3 are padding): one score
+  // block, and PV on the 16-key 16x16x16 matrix-core step, whose A operand
+  // (keys 4g..4g+3 of the block for lane group g) is the ovx read alone and
+  // whose B operand is block 0's probabilities: half the V^T reads and half
+  // the exponentials, for the same matrix-core time.
+  template <bool SINGLE>
   __device__ __forceinline__ void pass(int buf, uint32_t ka0, uint32_t ka1, int ovx, int ovy, int rem,
-                                       int lim) {
-    const bool single = rem <= 2;
+                                            int lim) {
     // keeps the ones operand in registers instead of rebuilding it per pass
     asm volatile("" : "+v"(ones));
     f32x4 s0 = nm4, s1 = nm4;
@@ -242,20 +241,18 @@ struct OctKernel {
     __builtin_amdgcn_s_setprio(1);
     if constexpr (F8) {
       // one 16x16x128 FP8 step per score block: 32 bytes of the K row per lane
-      if (single) {
+      if constexpr (SINGLE) {
         s0 = mac_fp8(lds_load<u32x4>(ka0), lds_load<u32x4>(ka0 + 16), qf[0], qf[1], s0);
-        s1 = s0;
       } else {
         const u32x4 a0 = lds_load<u32x4>(ka0), a1 = lds_load<u32x4>(ka0 + 16);
         const u32x4 b0 = lds_load<u32x4>(ka1), b1 = lds_load<u32x4>(ka1 + 16);
         s0 = mac_fp8(a0, a1, qf[0], qf[1], s0);
         s1 = mac_fp8(b0, b1, qf[0], qf[1], s1);
       }
-    } else if (single) {
+    } else if constexpr (SINGLE) {
 #pragma unroll
       for (int sl = 0; sl < C::NSLAB; ++sl)
         s0 = Mma<bf16_t>::mac8(lds_load<u32x4>(ka0 + 64 * sl), qf[sl], s0);
-      s1 = s0;
     } else {
 #pragma unroll
       for (int sl = 0; sl < C::NSLAB; ++sl) {
@@ -273,25 +270,34 @@ struct OctKernel {
     const uint32_t vx = shl4_add((uint32_t)ovx, vb);
     const uint32_t vy = shl4_add((uint32_t)ovy, vb);
     u32x4 av[C::NDB];
-    auto vread = [&](int off) {
-      const u32x2 x = lds_load<u32x2>(vx + off);
-      const u32x2 y = lds_load<u32x2>(vy + off);
-      return u32x4{x[0], x[1], y[0], y[1]};
+    u32x2 ax[C::NDB];
+    auto vread = [&](int j) {
+      if constexpr (SINGLE) {
+        ax[j] = lds_load<u32x2>(vx + 16 * j * C::VRS);
+      } else {
+        const u32x2 x = lds_load<u32x2>(vx + 16 * j * C::VRS);
+        const u32x2 y = lds_load<u32x2>(vy + 16 * j * C::VRS);
+        av[j] = u32x4{x[0], x[1], y[0], y[1]};
+      }
     };
 #pragma unroll
-    for (int j = 0; j < EARLY; ++j) av[j] = vread(16 * j * C::VRS);
+    for (int j = 0; j < EARLY; ++j) vread(j);
+    float mr;
+    if constexpr (SINGLE) {
+      mr = fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3]));
+    } else {
+      const float ma = fmaxf(fmaxf(s0[0], s0[1]), s0[2]);
+      const float mb = fmaxf(fmaxf(s0[3], s1[0]), s1[1]);
+      mr = fmaxf(fmaxf(ma, mb), fmaxf(s1[2], s1[3]));
+    }
     // (built with NaNs assumed absent, these fold into three-way max
     // instructions without operand quieting)
-    const float ma = fmaxf(fmaxf(s0[0], s0[1]), s0[2]);
-    const float mb = fmaxf(fmaxf(s0[3], s1[0]), s1[1]);
-    const float mr = fmaxf(fmaxf(ma, mb), fmaxf(s1[2], s1[3]));
     if (__builtin_amdgcn_ballot_w64(mr > thr) != 0ull) {
       const float mx = max_across_groups(mr) * cs;
       const float delta = fmaxf(mx, thr == -INFINITY ? -INFINITY : 0.f);
       const float alpha = exp2_fast(fminf(-delta, 0.f));
 #pragma unroll
       for (int j = 0; j <= C::NDB; ++j) oacc[j] *= alpha;
-      // (scale 0: every score is 0 and one pass fixes the reference for good)
       const float ic = cs > 0.f ? 1.f / cs : 0.f;
       thr = cs > 0.f ? RESCALE_STEP * ic : INFINITY;
       m_ref += delta;
@@ -299,15 +305,15 @@ struct OctKernel {
       nm4 = f32x4{nmu, nmu, nmu, nmu};
       const float du = delta * ic;
       s0 -= du;
-      s1 -= du;
+      if constexpr (!SINGLE) s1 -= du;
     }
     s0 *= cs;
-    s1 *= cs;
+    if constexpr (!SINGLE) s1 *= cs;
     f32x4 e0, e1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       e0[i] = exp2_fast(s0[i]);
-      e1[i] = exp2_fast(s1[i]);
+      if constexpr (!SINGLE) e1[i] = exp2_fast(s1[i]);
     }
     // keys past the end of the sequence (in the last, partial octet) carry no
     // probability
@@ -316,29 +322,46 @@ struct OctKernel {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (k0 + i >= lim) e0[i] = 0.f;
-        if (k1 + i >= lim) e1[i] = 0.f;
+        if constexpr (!SINGLE)
+          if (k1 + i >= lim) e1[i] = 0.f;
       }
     }
-    bf16x8 pb;
+    if constexpr (SINGLE) {
+      bf16x4 pb;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pb[i] = (__bf16)e0[i];
-      pb[4 + i] = (__bf16)e1[i];
-    }
-    u32x4 bop = __builtin_bit_cast(u32x4, pb);
-    // padding list positions (the last pass of a list) carry no probability
-    if (rem < 4) {
-      if ((g >> 1) >= rem) { bop[0] = 0u; bop[1] = 0u; }
-      if (2 + (g >> 1) >= rem) { bop[2] = 0u; bop[3] = 0u; }
-    }
-    __builtin_amdgcn_s_setprio(0);
+      for (int i = 0; i < 4; ++i) pb[i] = (__bf16)e0[i];
+      u32x2 bop = __builtin_bit_cast(u32x2, pb);
+      // position 1 is padding when rem == 1
+      if ((g >> 1) >= rem) bop = u32x2{0u, 0u};
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-    for (int j = EARLY; j < C::NDB; ++j) av[j] = vread(16 * j * C::VRS);
+      for (int j = EARLY; j < C::NDB; ++j) vread(j);
+      const bf16x4 b4 = __builtin_bit_cast(bf16x4, bop);
 #pragma unroll
-    for (int j = 0; j < C::NDB; ++j) {
-      oacc[j] = Mma<bf16_t>::mac8(av[j], bop, oacc[j]);
+      for (int j = 0; j < C::NDB; ++j)
+        oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, ax[j]), b4, oacc[j], 0, 0, 0);
+      const u32x2 o2 = u32x2{ones[0], ones[1]};
+      oacc[C::NDB] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, o2), b4, oacc[C::NDB], 0, 0, 0);
+    } else {
+      bf16x8 pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pb[i] = (__bf16)e0[i];
+        pb[4 + i] = (__bf16)e1[i];
+      }
+      u32x4 bop = __builtin_bit_cast(u32x4, pb);
+      // padding list positions (the last pass of a list) carry no probability
+      if (rem < 4) {
+        if ((g >> 1) >= rem) { bop[0] = 0u; bop[1] = 0u; }
+        if (2 + (g >> 1) >= rem) { bop[2] = 0u; bop[3] = 0u; }
+      }
+      __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int j = EARLY; j < C::NDB; ++j) vread(j);
+#pragma unroll
+      for (int j = 0; j < C::NDB; ++j) oacc[j] = Mma<bf16_t>::mac8(av[j], bop, oacc[j]);
+      oacc[C::NDB] = Mma<bf16_t>::mac8(ones, bop, oacc[C::NDB]);
     }
-    oacc[C::NDB] = Mma<bf16_t>::mac8(ones, bop, oacc[C::NDB]);
   }
 
   // kept-octet list of one chunk as a wave-uniform value: entry j (an octet
@@ -376,14 +399,22 @@ struct OctKernel {
     const uint32_t shq = 4u * (uint32_t)(n >> 3), shv = 4u * (uint32_t)(g >> 1);
     const uint32_t kb = lds_addr(sm.k[buf]) + (uint32_t)((n & 7) * C::KRS + (F8 ? 32 : 16) * g);
     uint64_t rest = li.w;
-    for (int q0 = 0; q0 < li.count; q0 += 4) {
+    int q0 = 0;
+    // passes with at least three real octets, then at most one with one or two
+    for (; li.count - q0 > 2; q0 += 4) {
       const uint32_t w = (uint32_t)rest & 0xffffu;
       rest >>= 16;
       const uint32_t ka0 = mad_u24(__builtin_amdgcn_ubfe(w, shq, 4), 8u * C::KRS, kb);
       const uint32_t ka1 = mad_u24(__builtin_amdgcn_ubfe(w, shq + 8u, 4), 8u * C::KRS, kb);
       const int ovx = (int)__builtin_amdgcn_ubfe(w, shv, 4);
       const int ovy = (int)__builtin_amdgcn_ubfe(w, shv + 8u, 4);
-      pass(buf, ka0, ka1, ovx, ovy, li.count - q0, lim);
+      pass<false>(buf, ka0, ka1, ovx, ovy, li.count - q0, lim);
+    }
+    if (q0 < li.count) {
+      const uint32_t w = (uint32_t)rest & 0xffffu;
+      const uint32_t ka0 = mad_u24(__builtin_amdgcn_ubfe(w, shq, 4), 8u * C::KRS, kb);
+      const int ovx = (int)__builtin_amdgcn_ubfe(w, shv, 4);
+      pass<true>(buf, ka0, ka0, ovx, ovx, li.count - q0, lim);
     }
   }
 
