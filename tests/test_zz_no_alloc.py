@@ -73,3 +73,42 @@ def test_noalloc_rejects_problems_beyond_its_scratch():
     with pytest.raises(T.TsaError) as e:
         T.attention_fwd_noalloc(q, k, v, m, 16, 8, out=o)
     assert e.value.status == T.ERR_UNSUPPORTED and "scratch" in e.value.detail
+
+
+def test_noalloc_forward_replays_in_a_captured_graph():
+    """The use the entry point is for: one call captured in a HIP graph (after
+    an eager call has looked up the scratch's address), replayed three times
+    with eager no-alloc calls on another problem in between, which overwrite
+    the shared scratch; every replay must equal the eager result bit for bit."""
+    torch = torch_or_skip()
+    import tile_sparse_attention_amd as T
+    w = small_workload("nag", 3000, 128, 16, 8, H=2, seed=74)
+    say("no-alloc graph capture: bf16 16x8 L=3000, three replays")
+    qh, kh, vh = W.make_qkv(w)
+    q, k, v = qh.cuda(), kh.cuda(), vh.cuda()
+    m = to_dev_mask(_banded(w, 4))
+    o_ref, l_ref = T.attention_fwd(q, k, v, m, w.M, w.N, w.scale, return_lse=True)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device="cuda")
+    T.attention_fwd_noalloc(q, k, v, m, w.M, w.N, w.scale, out=o, lse=lse)
+    # another problem for the eager calls between the replays
+    w2 = small_workload("nag2", 1500, 128, 16, 16, H=3, seed=75)
+    q2, k2, v2 = (x.cuda() for x in W.make_qkv(w2))
+    m2 = to_dev_mask(W.mask_bits(w2))
+    o2 = torch.empty_like(q2)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        T.attention_fwd_noalloc(q, k, v, m, w.M, w.N, w.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    for i in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        T.attention_fwd_noalloc(q2, k2, v2, m2, w2.M, w2.N, w2.scale, out=o2)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), f"replay {i}: O differs"
+        assert torch.equal(lse, l_ref), f"replay {i}: LSE differs"
