@@ -94,11 +94,12 @@ def kept_flops_device(w, mask) -> int:
     return int(4 * w.d * (keys * m).sum().item())
 
 
-def time_calls(fn, steps, warmup, kernel_events=False):
+def time_calls(fn, steps, warmup, kernel_events=False, stats=None):
     """(ms per step over the bracketed region, mean per-call ms from events,
     min per-call ms); with kernel_events also the mean ms of the attention
     kernels proper, from events the library records around them on the same
-    stream (tsa_set_timing_events)."""
+    stream (tsa_set_timing_events).  A `stats` dict receives the median
+    per-call ms."""
     import torch
 
     import tile_sparse_attention_amd as T
@@ -122,6 +123,9 @@ def time_calls(fn, steps, warmup, kernel_events=False):
     if kev is not None:
         T.set_timing_events(None, None)
     per = [a.elapsed_time(b) for a, b in ev]
+    if stats is not None:
+        stats["median_ms"] = sorted(per)[len(per) // 2] if len(per) % 2 else \
+            0.5 * (sorted(per)[len(per) // 2 - 1] + sorted(per)[len(per) // 2])
     out = (wall / steps, sum(per) / len(per), min(per))
     if kev is not None:
         kern = [a.elapsed_time(b) for a, b in kev]
@@ -129,7 +133,7 @@ def time_calls(fn, steps, warmup, kernel_events=False):
     return out
 
 
-def cpu_baseline(w, q, k, v, mask, budget_s=20.0):
+def cpu_baseline(w, q, k, v, mask, budget_s=20.0, kept_total=None):
     """fp64 oracle on a bounded sample of the workload, in the metric's unit: the
     first `per_head` of each head's sampled query tiles (tile 0, the last tile and
     random ones), over all heads, with `per_head` sized to the time budget."""
@@ -161,11 +165,45 @@ def cpu_baseline(w, q, k, v, mask, budget_s=20.0):
         kept += run(b, h, tiles[b, h, :per_head])
         secs += time.perf_counter() - t0
     n = per_head * len(heads)
-    return {"value": kept / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "cpu_model": cpu_model(), "blas": blas_name(),
+    rate = kept / secs
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "nproc": os.cpu_count(), "cpu_model": cpu_model(), "blas": blas_name(),
+            # the whole call's kept FLOPs at the sampled rate (not measured)
+            "extrapolated_ms_per_call": round(kept_total / rate * 1e3, 1) if kept_total else None,
             "sample": f"{per_head} sampled query tiles per head x {len(heads)} heads ({n} tiles, "
                       f"{n * w.M} query rows) against all {w.L} keys, fp64 numpy, {secs:.1f} s; "
                       f"kept FLOPs of those rows / time"}
+
+
+FLOP_PER_CLK_PER_CU = {"bf16": 4096, "f32": 256}  # dense matrix cores (16x16x32 bf16, 16x16x4 f32)
+
+
+def derived_peak_tflops(dtype="bf16"):
+    """The dense matrix-core peak re-derived from the device: compute units
+    (torch) x the GPU agent's maximum clock (rocminfo) x the matrix cores'
+    FLOP per clock per compute unit for `dtype`; None when rocminfo is not
+    there."""
+    import subprocess
+
+    import torch
+    try:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    mhz, in_gpu = None, False
+    for line in txt.splitlines():
+        t = line.strip()
+        if t.startswith("Name:"):
+            in_gpu = t.split(":", 1)[1].strip().startswith("gfx")
+        elif in_gpu and t.startswith("Max Clock Freq. (MHz):"):
+            mhz = float(t.split(":", 1)[1].strip())
+            break
+    if mhz is None:
+        return None
+    f = FLOP_PER_CLK_PER_CU[dtype]
+    return {"tflops": round(cus * mhz * 1e6 * f / 1e12, 1), "cus": cus, "max_mhz": mhz,
+            "flop_per_clk_per_cu": f}
 
 
 def cpu_model() -> str:
@@ -461,7 +499,9 @@ def main():
     def step():
         T.attention_fwd(qd, kd, vd, mask, w.M, w.N, w.scale, out=out, workspace=ws)
 
-    ms_step, ms_call, ms_min, ms_kernel = time_calls(step, args.steps, args.warmup, kernel_events=True)
+    st = {}
+    ms_step, ms_call, ms_min, ms_kernel = time_calls(step, args.steps, args.warmup, kernel_events=True,
+                                                     stats=st)
     tflops = flops / (ms_step * 1e-3) / 1e12
     log(f"sparse: {ms_step:.3f} ms/step, call mean {ms_call:.3f} ms (min {ms_min:.3f}), attention "
         f"kernels {ms_kernel:.3f} ms, {tflops:.1f} TFLOP/s")
@@ -501,7 +541,8 @@ def main():
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic_for(name, sha),
             "kernel": kernel_name(w), "kernel_ms": round(ms_kernel, 4), "call_ms": round(ms_call, 4),
-            "kernel_sha": sha}
+            "call_median_ms": round(st["median_ms"], 4), "kernel_sha": sha,
+            "peak_derived": derived_peak_tflops(w.dtype)}
     rec = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -509,7 +550,7 @@ def main():
            "config": cfg, "roofline": roof}
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
-        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, mask)
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, mask, kept_total=flops)
     print(json.dumps(rec), flush=True)
 
 

@@ -56,13 +56,18 @@ def test_forward_line():
     kept, total = _kept_tiles()   # L = 512 is a whole number of 16x16 tiles
     assert rec["config"]["kept_fraction"] == pytest.approx(kept / total, abs=1e-6)
     assert rec["config"]["speedup_vs_all_ones"] > 0
+    roof = rec["roofline"]
+    assert roof["call_median_ms"] > 0
+    pd = roof["peak_derived"]   # 256 CUs x 2400 MHz x 256 FLOP/clk for f32 matrix cores
+    assert pd is None or pd["tflops"] == pytest.approx(roof["peak"], rel=0.05)
 
 
 def test_forward_line_with_cpu_baseline():
     rec = _bench("--workload", "tiny", "--steps", "3", "--warmup", "1", "--no-dense")
     cb = rec["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
-    assert cb["cpu_model"] and cb["blas"]
+    assert cb["cpu_model"] and cb["blas"] and cb["nproc"] >= 1
+    assert cb["extrapolated_ms_per_call"] > 0
 
 
 def test_compaction_line():
