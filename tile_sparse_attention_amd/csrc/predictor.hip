@@ -204,13 +204,10 @@ __global__ __launch_bounds__(256) void select_pack_kernel(const float* __restric
                                                           uint32_t* __restrict__ mask, int T_q,
                                                           int T_k, int T_kp, int words, int i0,
                                                           int rows, int R, int bh0, int k) {
-  // Per-pass histogram in 16 copies, one per lane index mod 16, 257 ints
-  // apart so the copies of a bin sit in different banks: score digits
-  // crowd into a few bins (the top byte holds the sign and exponent), and
-  // one shared copy would serialise a wave's atomics on them.
-  constexpr int HC = 16, HS = 257;
-  __shared__ int hist16[HC * HS];
-  __shared__ int hist[256];
+  // Histogram of one digit (4096 bins for the first, 1024 for the others),
+  // wave totals of its scan, and the pass's result.
+  __shared__ int hbin[4096];
+  __shared__ int wsum[4];
   __shared__ uint32_t sh_prefix;
   __shared__ int sh_kr, sh_eqn;
   __shared__ int sh_eq[4];
@@ -241,58 +238,59 @@ __global__ __launch_bounds__(256) void select_pack_kernel(const float* __restric
   };
   constexpr int TMAX = IN_REG ? NPT : 0x7fffffff;  // bound of t (the real bound is j < T_k)
 
-  // -- radix select of the k-th largest key, 8 bits at a time --
+  // -- radix select of the k-th largest key: digits of 12, 10 and 10 bits.
+  // The first digit (sign, exponent and three mantissa bits) spreads scores
+  // over many bins; later digits count only the keys under the prefix found
+  // so far, a few dozen at most. --
   uint32_t prefix = 0, pmask = 0;
   int kr = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int e = tid; e < HC * HS; e += 256) hist16[e] = 0;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 20 : pass == 1 ? 10 : 0;
+    const int nb = pass == 0 ? 4096 : 1024;
+    const uint32_t dmask = (uint32_t)nb - 1u;
+    for (int e = tid; e < nb; e += 256) hbin[e] = 0;
     __syncthreads();
-    int* hl = hist16 + (lane & (HC - 1)) * HS;
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
       const int j = tid + 256 * t;
       if (j >= T_k) break;
       const uint32_t key = key_at(t, j);
-      if ((key & pmask) == prefix) atomicAdd(&hl[(key >> shift) & 255], 1);
+      if ((key & pmask) == prefix) atomicAdd(&hbin[(key >> shift) & dmask], 1);
     }
     __syncthreads();
-    {
-      int sum = 0;
+    // thread t owns the digits nb-1-t*per .. nb-per-t*per (descending)
+    const int per = nb >> 8;
+    int s = 0;
+    for (int q = 0; q < per; ++q) s += hbin[nb - 1 - tid * per - q];
+    int inc = s;
 #pragma unroll
-      for (int c = 0; c < HC; ++c) sum += hist16[c * HS + tid];
-      hist[tid] = sum;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(inc, off);
+      if (lane >= off) inc += y;
     }
+    if (lane == 63) wsum[wave] = inc;
     __syncthreads();
-    if (wave == 0) {
-      // lane l owns bins 255-4l .. 252-4l (descending); inclusive scan over lanes
-      int c[4], s = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) { c[q] = hist[255 - 4 * lane - q]; s += c[q]; }
-      int inc = s;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(inc, off);
-        if (lane >= off) inc += y;
-      }
-      const int exc = inc - s;
-      if (exc < kr && inc >= kr) {
-        int cum = exc;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (cum + c[q] >= kr) {
-            sh_prefix = prefix | ((uint32_t)(255 - 4 * lane - q) << shift);
-            sh_kr = kr - cum;
-            sh_eqn = c[q];  // after the last digit: the keys equal to the k-th largest
-            break;
-          }
-          cum += c[q];
+    for (int w = 0; w < wave; ++w) inc += wsum[w];
+    const int exc = inc - s;
+    if (exc < kr && inc >= kr) {
+      int cum = exc;
+      for (int q = 0; q < per; ++q) {
+        const int dgt = nb - 1 - tid * per - q;
+        const int c = hbin[dgt];
+        if (cum + c >= kr) {
+          sh_prefix = prefix | ((uint32_t)dgt << shift);
+          sh_kr = kr - cum;
+          sh_eqn = c;  // after the last digit: the keys equal to the k-th largest
+          break;
         }
+        cum += c;
       }
     }
     __syncthreads();
     prefix = sh_prefix;
     kr = sh_kr;
-    pmask |= 255u << shift;
+    pmask |= dmask << shift;
     __syncthreads();
   }
   // prefix = k-th largest key; keep key > prefix, and the first kr keys == prefix.
