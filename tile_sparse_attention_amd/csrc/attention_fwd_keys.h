@@ -25,6 +25,13 @@
 //     of the S^T accumulators (rows 4g..4g+3 of each score block).
 //   * l comes from a register ones operand; probabilities of padding
 //     positions and of keys past L are set to zero.
+//   * A chunk's last pass with at most 16 real positions forms one score
+//     block and runs PV on the 16-key 16x16x16 step (half the V reads and
+//     exponentials, the same matrix-core time); at 16 x 1 tiles and 80%
+//     sparsity that is the second pass a wave needs in about one chunk in
+//     twelve, the one the chunk barrier waits for.
+//   * Mask words are read with scalar loads, so they sit in scalar registers
+//     and do not queue behind the chunk's LDS loads.
 // LDS bank conflicts: K and V rows are 288 bytes apart (160 for d = 64), so
 // eight keys read together are conflict-free when their indices differ
 // modulo 8; kept keys are arbitrary, so some reads take two or three rounds.
@@ -133,10 +140,14 @@ struct KeyKernel {
       }
     }
     const int w0 = (c * C::TPC) >> 5;
+    // scalar loads (the mask is read-only here): the words land in scalar
+    // registers
+    const __attribute__((address_space(4))) uint32_t* m4 =
+        (const __attribute__((address_space(4))) uint32_t*)mrow;
 #pragma unroll
     for (int i = 0; i < C::MW; ++i) {
       const int wi = w0 + i;
-      mw[i] = mrow[wi < p.words ? wi : p.words - 1];
+      mw[i] = m4[wi < p.words ? wi : p.words - 1];
     }
   }
 
@@ -174,31 +185,34 @@ struct KeyKernel {
   // positions >= rem are padding).  Score block b holds positions
   // q0+16b..q0+16b+15; the S^T accumulators leave lane group g with the keys
   // at positions q0+4g..q0+4g+3 (block 0) and q0+16+4g.. (block 1), whose V
-  // values at d = n two transposing reads per d block deliver.  When
-  // positions 16..31 are all padding (rem <= 16) the second score block is a
-  // copy of the first.
-  template <int B>
+  // values at d = n two transposing reads per d block deliver.  SINGLE
+  // (rem <= 16: positions 16..31 are padding): one score block, and PV on the
+  // 16-key 16x16x16 matrix-core step, whose A operand is the block-0 read
+  // alone and whose B operand is block 0's four probabilities: half the V
+  // reads and half the exponentials, for the same matrix-core time.
+  template <int B, bool SINGLE>
   __device__ __forceinline__ void pass(int q0, int rem) {
-    const bool single = rem <= 16;
     // keeps the ones operand in registers instead of rebuilding it per pass
     asm volatile("" : "+v"(ones));
     const uint8_t* lst = ls.list[wave];
-    const uint32_t kk0 = lst[q0 + n], kk1 = lst[q0 + 16 + n];
+    const uint32_t kk0 = lst[q0 + n];
     const int vp = q0 + 4 * g + (n >> 2);
-    const uint32_t kv0 = lst[vp], kv1 = lst[vp + 16];
+    const uint32_t kv0 = lst[vp];
     const lds_cptr kb = to_lds(bufr<B>().k) + 16 * g;
     const lds_cptr ka0 = kb + kk0 * C::RS;
-    const lds_cptr ka1 = kb + kk1 * C::RS;
     f32x4 s0 = nm4, s1 = nm4;
+    uint32_t kv1 = 0;
     // raised wave priority from the score MFMAs through the softmax (as in
     // the octet kernel)
     __builtin_amdgcn_s_setprio(1);
-    if (single) {
+    if constexpr (SINGLE) {
 #pragma unroll
       for (int sl = 0; sl < C::NSLAB; ++sl)
         s0 = Mma<bf16_t>::mac8(lds_read16(ka0 + 64 * sl), qf[sl], s0);
-      s1 = s0;
     } else {
+      const uint32_t kk1 = lst[q0 + 16 + n];
+      kv1 = lst[vp + 16];
+      const lds_cptr ka1 = kb + kk1 * C::RS;
 #pragma unroll
       for (int sl = 0; sl < C::NSLAB; ++sl) {
         const u32x4 a0 = lds_read16(ka0 + 64 * sl);
@@ -209,20 +223,31 @@ struct KeyKernel {
     }
     // V operands: lane (g, n) points at d = 4(n&3)..4(n&3)+3 of its V-side
     // key; the transposing read returns d = n of the group's four keys.
-    constexpr int EARLY = C::NDB / 2 - 1;
+    constexpr int EARLY = C::NDB / 2 - 2;
     const lds_cptr vb = to_lds(bufr<B>().v) + 8 * (n & 3);
     const lds_cptr va0 = vb + kv0 * C::RS;
     const lds_cptr va1 = vb + kv1 * C::RS;
-    u32x4 av[C::NDB];
+    // SINGLE: block-0 reads only (ax); else both blocks (av)
+    u32x4 av[SINGLE ? 1 : C::NDB];
+    u32x2 ax[SINGLE ? C::NDB : 1];
     auto vread = [&](int j) {
-      const u32x2 x = lds_read_tr16(va0 + 32 * j), y = lds_read_tr16(va1 + 32 * j);
-      return u32x4{x[0], x[1], y[0], y[1]};
+      if constexpr (SINGLE) {
+        ax[j] = lds_read_tr16(va0 + 32 * j);
+      } else {
+        const u32x2 x = lds_read_tr16(va0 + 32 * j), y = lds_read_tr16(va1 + 32 * j);
+        av[j] = u32x4{x[0], x[1], y[0], y[1]};
+      }
     };
 #pragma unroll
-    for (int j = 0; j < EARLY; ++j) av[j] = vread(j);
-    const float ma = fmaxf(fmaxf(s0[0], s0[1]), s0[2]);
-    const float mb = fmaxf(fmaxf(s0[3], s1[0]), s1[1]);
-    const float mr = fmaxf(fmaxf(ma, mb), fmaxf(s1[2], s1[3]));
+    for (int j = 0; j < EARLY; ++j) vread(j);
+    float mr;
+    if constexpr (SINGLE) {
+      mr = fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3]));
+    } else {
+      const float ma = fmaxf(fmaxf(s0[0], s0[1]), s0[2]);
+      const float mb = fmaxf(fmaxf(s0[3], s1[0]), s1[1]);
+      mr = fmaxf(fmaxf(ma, mb), fmaxf(s1[2], s1[3]));
+    }
     if (__builtin_amdgcn_ballot_w64(mr > thr) != 0ull) {
       const float mx = max_across_groups(mr) * cs;
       const float delta = fmaxf(mx, thr == -INFINITY ? -INFINITY : 0.f);
@@ -236,35 +261,50 @@ struct KeyKernel {
       nm4 = f32x4{nmu, nmu, nmu, nmu};
       const float du = delta * ic;
       s0 -= du;
-      s1 -= du;
+      if constexpr (!SINGLE) s1 -= du;
     }
     f32x4 e0, e1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       e0[i] = exp2_fast(s0[i] * cs);
-      e1[i] = exp2_fast(s1[i] * cs);
+      if constexpr (!SINGLE) e1[i] = exp2_fast(s1[i] * cs);
     }
     // padding list positions (the last pass of a list) carry no probability
     if (rem < 32) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (4 * g + i >= rem) e0[i] = 0.f;
-        if (16 + 4 * g + i >= rem) e1[i] = 0.f;
+        if constexpr (!SINGLE)
+          if (16 + 4 * g + i >= rem) e1[i] = 0.f;
       }
     }
-    bf16x8 pb;
+    if constexpr (SINGLE) {
+      bf16x4 pb;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pb[i] = (__bf16)e0[i];
-      pb[4 + i] = (__bf16)e1[i];
+      for (int i = 0; i < 4; ++i) pb[i] = (__bf16)e0[i];
+      __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int j = EARLY; j < C::NDB; ++j) vread(j);
+#pragma unroll
+      for (int j = 0; j < C::NDB; ++j)
+        oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, ax[j]), pb, oacc[j], 0, 0, 0);
+      oacc[C::NDB] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+          __builtin_bit_cast(bf16x4, u32x2{ones[0], ones[1]}), pb, oacc[C::NDB], 0, 0, 0);
+    } else {
+      bf16x8 pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pb[i] = (__bf16)e0[i];
+        pb[4 + i] = (__bf16)e1[i];
+      }
+      const u32x4 bop = __builtin_bit_cast(u32x4, pb);
+      __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int j = EARLY; j < C::NDB; ++j) vread(j);
+#pragma unroll
+      for (int j = 0; j < C::NDB; ++j) oacc[j] = Mma<bf16_t>::mac8(av[j], bop, oacc[j]);
+      oacc[C::NDB] = Mma<bf16_t>::mac8(ones, bop, oacc[C::NDB]);
     }
-    const u32x4 bop = __builtin_bit_cast(u32x4, pb);
-    __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-    for (int j = EARLY; j < C::NDB; ++j) av[j] = vread(j);
-#pragma unroll
-    for (int j = 0; j < C::NDB; ++j) oacc[j] = Mma<bf16_t>::mac8(av[j], bop, oacc[j]);
-    oacc[C::NDB] = Mma<bf16_t>::mac8(ones, bop, oacc[C::NDB]);
   }
 
   // Chunk c from buffer B while chunk c+1 loads into the other buffer.
@@ -274,8 +314,11 @@ struct KeyKernel {
     uint32_t mwn[C::MW];
     // buffer B^1 was last read in the previous step, which every wave has left
     if (more) issue_chunk<B ^ 1>(c + 1, mwn);
-    if (act)
-      for (int q0 = 0; q0 < count; q0 += 32) pass<B>(q0, count - q0);
+    if (act) {
+      int q0 = 0;
+      for (; count - q0 > 16; q0 += 32) pass<B, false>(q0, count - q0);
+      if (q0 < count) pass<B, true>(q0, count - q0);
+    }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c+1 have landed
     if (act && more) count = make_list(c + 1, mwn);
     __syncthreads();                // ... and every other wave's

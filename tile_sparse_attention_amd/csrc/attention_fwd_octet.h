@@ -214,7 +214,9 @@ struct OctKernel {
       }
     }
     const int wi = (c * C::TPC) >> 5;
-    return mrow[wi < p.words ? wi : p.words - 1];
+    // a scalar load (the mask is read-only here): it does not queue behind
+    // the chunk's LDS loads
+    return ((const __attribute__((address_space(4))) uint32_t*)mrow)[wi < p.words ? wi : p.words - 1];
   }
 
   // One pass over the four list positions q0..q0+3 (rem = entries left from
