@@ -8,8 +8,10 @@ inputs resident in HBM.  Prints one JSON line.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 
 With --backward it times the backward pass (tsa_attention_bwd) of the same
-workload instead and prints that line; --fp8, --mask-diff and --compact time
-the FP8 forward, the mask diff and the mask compaction likewise.
+workload instead and prints that line; --fp8, --mask-diff, --compact and
+--predict time the FP8 forward, the mask diff, the mask compaction and the
+mask predictor likewise.  Each line carries the fp64 CPU oracle timed on a
+bounded sample of the same workload (cpu_baseline) unless --no-cpu.
 """
 from __future__ import annotations
 
@@ -178,6 +180,101 @@ def cpu_baseline(w, q, k, v, mask, budget_s=20.0, kept_total=None):
 FLOP_PER_CLK_PER_CU = {"bf16": 4096, "f32": 256}  # dense matrix cores (16x16x32 bf16, 16x16x4 f32)
 
 
+def _sampled(units, run_one, budget_s):
+    """Runs run_one(u) over `units` in order (every unit at least once for the
+    first, then until budget_s of wall time is spent); returns (units run,
+    summed work, seconds).  run_one returns the unit's work."""
+    done, work, secs = 0, 0, 0.0
+    for u in units:
+        t0 = time.perf_counter()
+        work += run_one(u)
+        secs += time.perf_counter() - t0
+        done += 1
+        if secs >= budget_s:
+            break
+    return done, work, secs
+
+
+def _oracle_env():
+    return {"cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), "kind": "oracle",
+            "nproc": os.cpu_count(), "cpu_model": cpu_model(), "blas": blas_name()}
+
+
+def cpu_baseline_backward(w, q, k, v, do, mask, budget_s=20.0):
+    """fp64 backward oracle on a bounded sample: dQ rows of each head's sampled
+    query tiles (S, dP and dQ for those rows: 3 of the 5 GEMMs), credited with
+    1.5x the rows' kept forward FLOPs, in TFLOP/s."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+    tiles = W.sample_tiles(w)
+    bits = mask.cpu().numpy().view(np.uint32)
+    nj = np.minimum(w.N, w.L - np.arange(w.T_k) * w.N)
+    per = 8
+    units = [(b, h, i0) for i0 in range(0, tiles.shape[2], per) for b in range(w.B) for h in range(w.H)]
+
+    def run(u):
+        b, h, i0 = u
+        t = tiles[b, h, i0:i0 + per]
+        oracle.attention_bwd_rows(q[b, h], k[b, h], v[b, h], do[b, h], bits[b, h], w.M, w.N, w.scale,
+                                  q_tiles=t)
+        keep = oracle.unpack_mask(bits[b, h][t], w.T_k)
+        m = np.minimum(w.M, w.L - t * w.M)
+        return 1.5 * 4 * w.d * int((m[:, None] * keep * nj[None, :]).sum())
+
+    n, work, secs = _sampled(units, run, budget_s)
+    return {"value": work / secs / 1e12, "unit": "TFLOP/s", **_oracle_env(),
+            "sample": f"dQ rows of {n * per} sampled query tiles over {min(n, w.B * w.H)} heads (S, dP, dQ: "
+                      f"3 of the 5 GEMMs, credited 1.5x their kept forward FLOPs), fp64 numpy, {secs:.1f} s"}
+
+
+def cpu_baseline_rows(w, bits_list, fn, per_row_bytes, budget_s=10.0):
+    """An oracle over bitmap rows (compaction, mask diff) on a bounded sample
+    of the flattened rows, in GB/s of the line's algorithmic bytes.
+    per_row_bytes(rows, result) gives the bytes those rows account for."""
+    import numpy as np
+    flat = [np.ascontiguousarray(x).reshape(-1, x.shape[-1]) for x in bits_list]
+    R = flat[0].shape[0]
+    chunk = max(1, min(R, 4096))
+    units = list(range(0, R, chunk))
+
+    def run(r0):
+        part = [f[r0:r0 + chunk][None, None] for f in flat]
+        return per_row_bytes(part[0].shape[2], fn(*part, w.T_k))
+
+    n, work, secs = _sampled(units, run, budget_s)
+    rows = min(R, n * chunk)
+    return {"value": work / secs / 1e9, "unit": "GB/s", **_oracle_env(),
+            "sample": f"the first {rows} of {R} bitmap rows, numpy, {secs:.2f} s"}
+
+
+def cpu_baseline_predict(w, q, k, budget_s=20.0):
+    """fp64 predictor oracle (pool, pooled scores, stable top-k, pack) on
+    bounded samples of query-tile rows, one head at a time, in TFLOP/s of the
+    rows' score products (2 T_k d per row; the pooling of the head's tiles is
+    in the timed work)."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+    tiles = W.sample_tiles(w)
+    per = tiles.shape[2]   # one call per head: the oracle pools the whole head on every call
+    units = [(b, h, 0) for b in range(w.B) for h in range(w.H)]
+
+    def run(u):
+        b, h, i0 = u
+        t = tiles[b, h, i0:i0 + per]
+        oracle.predict_mask(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], w.M, w.N, w.mask.sparsity_percent,
+                            tiles=t[None, None])
+        return 2 * len(t) * w.T_k * w.d
+
+    n, work, secs = _sampled(units, run, budget_s)
+    return {"value": work / secs / 1e12, "unit": "TFLOP/s", **_oracle_env(),
+            "sample": f"{n * per} sampled query-tile rows over {min(n, w.B * w.H)} heads (each head's pooling "
+                      f"included), fp64 numpy, {secs:.1f} s"}
+
+
 def derived_peak_tflops(dtype="bf16"):
     """The dense matrix-core peak re-derived from the device: compute units
     (torch) x the GPU agent's maximum clock (rocminfo) x the matrix cores'
@@ -247,7 +344,7 @@ BWD_METRIC = ("backward kept-tile effective TFLOPS (dQ, dK, dV; 5 GEMMs per kept
 BWD_SOURCES = ("tile_sparse_attention_amd/csrc/attention_bwd.h", "tile_sparse_attention_amd/csrc/attention_bwd.hip")
 
 
-def bench_backward(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws):
+def bench_backward(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws, q_cpu, k_cpu, v_cpu):
     """One step = one tsa_attention_bwd call (LSE/D preparation, the dK/dV kernel
     and the dQ kernel) on the workload, given the forward's O and LSE."""
     import torch
@@ -298,10 +395,13 @@ def bench_backward(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws)
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded normal Q/K/V/dO, generated masks)", "config": cfg, "roofline": roof}
+    if not args.no_cpu:
+        log("timing the CPU backward oracle on a bounded sample ...")
+        rec["cpu_baseline"] = cpu_baseline_backward(w, q_cpu, k_cpu, v_cpu, do.cpu(), mask)
     print(json.dumps(rec), flush=True)
 
 
-def bench_fp8(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws):
+def bench_fp8(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws, q_cpu, k_cpu, v_cpu):
     """One step = one tsa_attention_fwd_fp8 call (Q, K already quantised to e4m3
     and resident in HBM); the quantisation is timed on its own."""
     import torch
@@ -334,6 +434,62 @@ def bench_fp8(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws):
            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
                         "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
                         "kernel": "attn_oct_kernel (FP8 scores)"}}
+    if not args.no_cpu:
+        import oracle.fp8 as F
+        log("timing the CPU oracle (on the dequantised Q and K) on a bounded sample ...")
+        q8c, qsc, k8c, ksc = F.quantize_qk(q_cpu, k_cpu)
+        qdq = F.dequantize(q8c, qsc, F.Q_TILE_ROWS)
+        kdq = F.dequantize(k8c, ksc[..., None], w.L)
+        del q8c, k8c
+        rec["cpu_baseline"] = cpu_baseline(w, qdq, kdq, v_cpu, mask, kept_total=flops)
+        rec["cpu_baseline"]["sample"] += " (Q, K dequantised from e4m3)"
+    print(json.dumps(rec), flush=True)
+
+
+PREDICT_METRIC = ("pooled-score predictor throughput: fp32-accurate score products (2 T_q T_k d per head) "
+                  "per whole prediction (pool, products, top-k select, pack), TFLOP/s")
+
+
+def bench_predict(args, w, name, qd, kd, q_cpu, k_cpu):
+    """One step = one tsa_predict_mask call (Q, K in, keep-bitmap out), inputs
+    resident in HBM, with the workload's sparsity (85% unless it names one)."""
+    import torch
+
+    import tile_sparse_attention_amd as T
+    sp = w.mask.sparsity_percent if w.mask.kind == "predicted" else 85
+    out = torch.empty((w.B, w.H, w.T_q, T.mask_row_words(w.L, w.N)), dtype=torch.int32, device="cuda")
+    T.predict_mask(qd, kd, w.M, w.N, sp, out=out)
+    first = out.clone()
+    torch.cuda.synchronize()
+
+    def step():
+        T.predict_mask(qd, kd, w.M, w.N, sp, out=out)
+
+    st = {}
+    ms_step, ms_call, ms_min = time_calls(step, args.steps, args.warmup, stats=st)
+    if not torch.equal(first, out):
+        raise SystemExit("predictor: repeated calls gave different masks")
+    fl = 2 * w.B * w.H * w.T_q * w.T_k * w.d
+    tflops = fl / (ms_step * 1e-3) / 1e12
+    achieved = fl / (ms_call * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["f32"]
+    log(f"predictor: {ms_step:.3f} ms/step, call mean {ms_call:.3f} ms, {tflops:.1f} TFLOP/s of "
+        f"fp32-accurate score products")
+    rec = {"metric": PREDICT_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32 (products as three bf16 matrix-core products of hi/lo parts)",
+           "data": "synthetic (seeded normal Q/K with per-frame offsets)",
+           "config": {"workload": name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "M": w.M, "N": w.N,
+                      "T_q": w.T_q, "T_k": w.T_k, "sparsity_percent": sp, "score_flops": fl},
+           "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                        "frac": round(achieved / peak, 4), "traffic": None,
+                        "kernel": "pool_tiles_kernel + pooled_scores_kernel + select_pack_kernel",
+                        "call_ms": round(ms_call, 4), "call_median_ms": round(st["median_ms"], 4),
+                        "note": "the fp32 matrix-core peak: the products are fp32-accurate"}}
+    if not args.no_cpu:
+        log("timing the CPU predictor oracle on a bounded sample ...")
+        rec["cpu_baseline"] = cpu_baseline_predict(w, q_cpu, k_cpu)
     print(json.dumps(rec), flush=True)
 
 
@@ -374,6 +530,12 @@ def bench_mask_diff(args, w, name):
            "roofline": {"bound": "hbm", "achieved": sig(gbs), "peak": 8000.0, "unit": "GB/s",
                         "frac": sig(gbs / 8000.0), "traffic": None,
                         "kernel": "diff_rows_kernel + diff_heads_kernel"}}
+    if not args.no_cpu:
+        import oracle
+        words = a.shape[-1]
+        rec["cpu_baseline"] = cpu_baseline_rows(
+            w, [a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32)], oracle.mask_diff,
+            lambda rows, res: rows * (2 * words * 4 + 8))
     print(json.dumps(rec), flush=True)
 
 
@@ -420,6 +582,14 @@ def bench_compact(args, w, name):
            "roofline": {"bound": "hbm", "achieved": sig(gbs), "peak": 8000.0, "unit": "GB/s",
                         "frac": sig(gbs / 8000.0), "traffic": None,
                         "kernel": "compact_count_kernel + scan_groups_kernel + compact_fill_kernel"}}
+    if not args.no_cpu:
+        import numpy as np
+
+        import oracle
+        words = mask.shape[-1]
+        rec["cpu_baseline"] = cpu_baseline_rows(
+            w, [mask.cpu().numpy().view(np.uint32)], oracle.compact,
+            lambda rows, res: rows * (words * 4 + 8) + int(res[0][-1]) * 4)
     print(json.dumps(rec), flush=True)
 
 
@@ -442,6 +612,9 @@ def main():
     ap.add_argument("--mask-diff", action="store_true",
                     help="time tsa_mask_diff between the workload's mask and a reseeded one (mask reuse "
                          "across denoising steps) and print its own JSON line")
+    ap.add_argument("--predict", action="store_true",
+                    help="time tsa_predict_mask (pool, pooled scores, top-k select, pack) on the workload "
+                         "(default hunyuan720) and print its own JSON line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run one plain device copy of BYTES bytes (calibrates the HBM "
                          "byte counters of a profiler run) and exit")
@@ -465,7 +638,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": args.copy_probe}), flush=True)
         return
-    name = args.workload or W.HEADLINE
+    name = args.workload or ("hunyuan720" if args.predict else W.HEADLINE)
     w = W.get(name)
     if args.mask_diff:
         bench_mask_diff(args, w, name)
@@ -490,10 +663,13 @@ def main():
     log(f"kept FLOPs {flops:.4e} ({flops / dense_flops:.4f} of dense)")
 
     if args.backward:
-        bench_backward(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws)
+        bench_backward(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws, q, k, v)
         return
     if args.fp8:
-        bench_fp8(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws)
+        bench_fp8(args, w, name, qd, kd, vd, mask, flops, dense_flops, out, ws, q, k, v)
+        return
+    if args.predict:
+        bench_predict(args, w, name, qd, kd, q, k)
         return
 
     def step():

@@ -1,6 +1,7 @@
-"""The benchmark's output contract on the GPU, on the tiny workload (1x2x512x64,
-fp32, 16x16 tiles): one JSON line on stdout with the fields the measurement
-relies on, for the forward line and the compaction and mask-diff lines.  The
+"""The benchmark's output contract on the GPU, on small workloads (1x2x512x64
+fp32 16x16 tiles; 1x2x2048x128 bf16 16x8 and 16x16): one JSON line on stdout
+with the fields the measurement relies on, for the forward, backward, FP8,
+predictor, compaction and mask-diff lines, each with its CPU oracle timing.  The
 kept-tile counts it reports are checked against the host generator's mask.
 The file name sorts after every parity file, so a failure here never hides a
 parity test in a run that stops at the first failure."""
@@ -70,12 +71,42 @@ def test_forward_line_with_cpu_baseline():
     assert cb["extrapolated_ms_per_call"] > 0
 
 
+def _check_cpu(rec, unit):
+    cb = rec["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["unit"] == unit and cb["value"] > 0 and cb["sample"]
+    assert cb["cores"] >= 1 and cb["cpu_model"] and cb["blas"]
+
+
 def test_compaction_line():
     rec = _bench("--compact", "--workload", "tiny", "--steps", "3", "--warmup", "1")
     assert rec["unit"] == "GB/s" and rec["roofline"]["bound"] == "hbm"
     assert rec["config"]["kept_tiles"] == _kept_tiles()[0]
+    _check_cpu(rec, "GB/s")
+
+
+def test_backward_line():
+    rec = _bench("--backward", "--workload", "small_fine", "--steps", "3", "--warmup", "1")
+    assert rec["unit"] == "TFLOP/s" and rec["dtype"] == "bf16"
+    assert rec["roofline"]["bound"] == "mfma" and rec["config"]["speedup_vs_all_ones"] > 0
+    _check_cpu(rec, "TFLOP/s")
+
+
+def test_fp8_line():
+    rec = _bench("--fp8", "--workload", "small_fine", "--steps", "3", "--warmup", "1", "--no-dense")
+    assert rec["unit"] == "TFLOP/s" and rec["roofline"]["bound"] == "mfma"
+    assert rec["config"]["quantise_ms"] > 0
+    _check_cpu(rec, "TFLOP/s")
+
+
+def test_predict_line():
+    rec = _bench("--predict", "--workload", "small_pred", "--steps", "3", "--warmup", "1")
+    w = W.get("small_pred")
+    assert rec["unit"] == "TFLOP/s" and rec["roofline"]["peak"] == 157.3
+    assert rec["config"]["score_flops"] == 2 * w.B * w.H * w.T_q * w.T_k * w.d
+    _check_cpu(rec, "TFLOP/s")
 
 
 def test_mask_diff_line():
     rec = _bench("--mask-diff", "--workload", "tiny", "--steps", "3", "--warmup", "1")
     assert rec["unit"] == "GB/s" and rec["roofline"]["bound"] == "hbm"
+    _check_cpu(rec, "GB/s")

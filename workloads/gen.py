@@ -202,6 +202,16 @@ _add(Workload("wan480_struct", 1, 40, 32760, 128, 16, 8, "bf16",
                           "skipped, 12 diagonal (|q-k| <= 4914), 13 multi-diagonal (|q-k-1560t| <= "
                           "128, |t| <= 20), 13 vertical-stripe (k mod 1560 < 390)"))
 
+# Small bf16 problems for the benchmark's output-contract tests (every line of
+# bench.py in seconds); not workloads of the pages.
+_add(Workload("small_fine", 1, 2, 2048, 128, 16, 8, "bf16",
+              MaskRecipe("hash", p_near=0.3, p_far=0.3), BASE_SEED + 7,
+              description="1x2x2048x128 bf16, 16x8 tiles, i.i.d. keep p=0.3, diagonal kept"))
+_add(Workload("small_pred", 1, 2, 2048, 128, 16, 16, "bf16",
+              MaskRecipe("predicted", sparsity_percent=85, force_diag=False), BASE_SEED + 8,
+              description="1x2x2048x128 bf16, 16x16 tiles, mask predicted at the per-row 85th "
+                          "percentile of pooled scores"))
+
 HEADLINE = "wan480_fine"
 
 
