@@ -8,12 +8,13 @@
 //              past T_k cleared) and each work-group sums its 16 rows;
 //   2. scan:   one work-group turns the per-group sums into int64 offsets;
 //   3. fill:   one wave per row writes row_ptr, then takes its row 64 words
-//              at a time: one coalesced load (a word per lane), a wave prefix
-//              sum of the words' popcounts for each lane's first slot, each
-//              lane's kept tiles into the wave's LDS staging area in
-//              ascending order (placed at the output's alignment), and from
-//              there 16-byte stores of aligned runs, clipped at col_capacity.  A row that starts at or past
-//              col_capacity (a count-only call) reads no bits at all.
+//              at a time: a word per lane (loaded 16 blocks at a time, one
+//              such super-block ahead), a wave prefix sum of the words'
+//              popcounts for each lane's first slot, each lane's kept tiles
+//              into the wave's LDS staging area in ascending order (placed at
+//              the output's alignment), and from there 16-byte stores of
+//              aligned runs, clipped at col_capacity.  A row that starts at or
+//              past col_capacity (a count-only call) reads no bits at all.
 #include "tsa_device.h"
 #include "tsa.h"
 
@@ -21,6 +22,7 @@ namespace tsa {
 
 constexpr int kRowsPerGroup = 16;  // rows per count work-group (one wave each) and per scan entry
 constexpr int kFillWaves = 4;      // rows per fill work-group (one wave each)
+constexpr int kSuperBlock = 16;    // 64-word blocks of a row loaded together by the fill
 
 __global__ __launch_bounds__(64 * kRowsPerGroup) void compact_count_kernel(const uint32_t* __restrict__ mask,
                                                             long long rows, int words, int T_k,
@@ -109,10 +111,14 @@ __global__ __launch_bounds__(64 * kFillWaves) void compact_fill_kernel(
   const int wave = wave_uniform(threadIdx.x >> 6);
   const long long row = (long long)blockIdx.x * kFillWaves + wave;
   if (row >= rows) return;
-  // the row's count group's offset plus the counts of the group's earlier rows
+  // the row's count group's offset plus the counts of the group's earlier
+  // rows (lane i holds the count of the group's row i; one vector load)
   const long long grp = row / kRowsPerGroup, first = grp * kRowsPerGroup;
-  long long start = group_offsets[grp];
-  for (long long i = first; i < row; ++i) start += counts[i];
+  const int li = lane_id();
+  int before = li < (int)(row - first) ? counts[first + li] : 0;
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) before += __shfl_xor(before, off);  // lanes 0..15 hold all
+  long long start = group_offsets[grp] + (long long)__shfl(before, 0);
   if (lane_id() == 0) {
     row_ptr[row] = start;
     if (row == rows - 1) row_ptr[rows] = total[0];
@@ -122,51 +128,74 @@ __global__ __launch_bounds__(64 * kFillWaves) void compact_fill_kernel(
   const int lane = lane_id();
   int32_t* st = stage[wave];
   long long base = start;  // output slot of the block's first kept tile
-  // each block's words are loaded while the previous block is written
-  uint32_t xn = lane < words ? r[lane] : 0u;
-  for (int w0 = 0; w0 < words && base < col_capacity; w0 += 64) {
-    const int w = w0 + lane;
-    uint32_t x = xn;
-    xn = w + 64 < words ? r[w + 64] : 0u;
-    if (w < words) {
-      const int valid = T_k - 32 * w;  // 1..32 in the last word
-      if (valid < 32) x &= (1u << valid) - 1u;
-    }
-    const int c = __builtin_popcount(x);
-    int incl = c;  // inclusive prefix sum of the popcounts over the lanes
+  // The row's words come kSuperBlock 64-word blocks at a time, a word per
+  // lane per block, loaded one super-block ahead.  A vector-memory wait
+  // also waits for the stores issued before it, so waiting once per
+  // super-block instead of once per block lets a block's stores overlap the
+  // next blocks' expansion.
+  const int nblk = (words + 63) >> 6;
+  uint32_t xn[kSuperBlock];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
-    // staged at the output's alignment: stage slot a + s holds output slot
-    // base + s, with a = (address of col_idx[base] / 4) mod 4, so every four
-    // stage slots 4m..4m+3 are one 16-byte-aligned run of col_idx
-    const int a = (int)((reinterpret_cast<uintptr_t>(col_idx + base) >> 2) & 3);
-    int at = a + incl - c;
-    while (x != 0u) {
-      const int b = __builtin_ctz(x);
-      x &= x - 1u;
-      st[at++] = 32 * w + b;
-    }
-    wave_sync_lds();  // the staging writes of every lane precede the reads
-    const int total_blk = __shfl(incl, 63);
-    const long long g0 = base - a;  // output slot of stage slot 0 (16-byte aligned)
-    const int end = a + total_blk;  // stage slots a .. end-1 are this block's
-    for (int m = lane; 4 * m < end; m += 64) {
-      const int s0 = 4 * m;
-      const long long gs = g0 + s0;
-      if (s0 >= a && s0 + 4 <= end && gs + 4 <= col_capacity) {
-        const int4 v = *reinterpret_cast<const int4*>(&st[s0]);
-        *reinterpret_cast<int4*>(col_idx + gs) = v;
-      } else {
+  for (int u = 0; u < kSuperBlock; ++u) {
+    const int w = 64 * u + lane;
+    xn[u] = w < words ? r[w] : 0u;
+  }
+  for (int b0 = 0; b0 < nblk && base < col_capacity; b0 += kSuperBlock) {
+    uint32_t xc[kSuperBlock];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (s0 + e >= a && s0 + e < end && gs + e < col_capacity) col_idx[gs + e] = st[s0 + e];
+    for (int u = 0; u < kSuperBlock; ++u) xc[u] = xn[u];
+    if (b0 + kSuperBlock < nblk) {
+#pragma unroll
+      for (int u = 0; u < kSuperBlock; ++u) {
+        const int w = 64 * (b0 + kSuperBlock + u) + lane;
+        xn[u] = w < words ? r[w] : 0u;
       }
     }
-    wave_sync_lds();  // ... and the reads precede the next block's writes
-    base += total_blk;
+#pragma unroll
+    for (int u = 0; u < kSuperBlock; ++u) {
+      if (b0 + u >= nblk || base >= col_capacity) break;
+      const int w = 64 * (b0 + u) + lane;
+      uint32_t x = xc[u];
+      if (w < words) {
+        const int valid = T_k - 32 * w;  // 1..32 in the last word
+        if (valid < 32) x &= (1u << valid) - 1u;
+      }
+      const int c = __builtin_popcount(x);
+      int incl = c;  // inclusive prefix sum of the popcounts over the lanes
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      // staged at the output's alignment: stage slot a + s holds output slot
+      // base + s, with a = (address of col_idx[base] / 4) mod 4, so every four
+      // stage slots 4m..4m+3 are one 16-byte-aligned run of col_idx
+      const int a = (int)((reinterpret_cast<uintptr_t>(col_idx + base) >> 2) & 3);
+      int at = a + incl - c;
+      while (x != 0u) {
+        const int bb = __builtin_ctz(x);
+        x &= x - 1u;
+        st[at++] = 32 * w + bb;
+      }
+      wave_sync_lds();  // the staging writes of every lane precede the reads
+      const int total_blk = __shfl(incl, 63);
+      const long long g0 = base - a;  // output slot of stage slot 0 (16-byte aligned)
+      const int end = a + total_blk;  // stage slots a .. end-1 are this block's
+      for (int m = lane; 4 * m < end; m += 64) {
+        const int s0 = 4 * m;
+        const long long gs = g0 + s0;
+        if (s0 >= a && s0 + 4 <= end && gs + 4 <= col_capacity) {
+          const int4 v = *reinterpret_cast<const int4*>(&st[s0]);
+          *reinterpret_cast<int4*>(col_idx + gs) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (s0 + e >= a && s0 + e < end && gs + e < col_capacity) col_idx[gs + e] = st[s0 + e];
+        }
+      }
+      wave_sync_lds();  // ... and the reads precede the next block's writes
+      base += total_blk;
+    }
   }
 }
 
