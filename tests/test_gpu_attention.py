@@ -102,6 +102,36 @@ def test_short_sequences(L):
     full_compare(w, _hash_bits(w), f"bf16 16x4 L={L}")
 
 
+# kept key tiles per (query tile, 128-key chunk), cycled over tiles and
+# chunks: every count a pass boundary of the kernels can fall on (the key
+# kernel packs 32 keys per pass and runs a last pass with <= 16 real keys on
+# one score block; the octet kernel packs 4 octets and runs a last pass with
+# <= 2 real octets on one block)
+_PASS_COUNTS = {1: (0, 1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64, 65, 100, 127, 128),
+                2: (0, 1, 7, 8, 9, 15, 16, 17, 24, 31, 32, 33, 48, 63, 64),
+                4: (0, 1, 3, 4, 5, 7, 8, 9, 15, 16, 17, 24, 31, 32),
+                8: (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 15, 16),
+                16: (0, 1, 2, 3, 4, 5, 6, 7, 8)}
+
+
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 16])
+def test_kept_counts_at_pass_boundaries(N):
+    torch_or_skip()
+    L = 2048 + 77   # 16 whole chunks and a partial one
+    w = small_workload(f"passes_{N}", L, 128, 16, N, seed=200 + N)
+    tpc = 128 // N
+    counts = _PASS_COUNTS[N]
+    rng = np.random.default_rng(N)
+    keep = np.zeros((1, w.H, w.T_q, w.T_k), dtype=bool)
+    for h in range(w.H):
+        for i in range(w.T_q):
+            for c in range(-(-w.T_k // tpc)):
+                j0, j1 = c * tpc, min(c * tpc + tpc, w.T_k)
+                n = min(counts[(i + 3 * c + h) % len(counts)], j1 - j0)
+                keep[0, h, i, j0 + rng.choice(j1 - j0, n, replace=False)] = True
+    full_compare(w, W.pack_bits(keep), f"bf16 16x{N} kept counts at pass boundaries")
+
+
 def test_empty_mask_gives_zero_and_minus_inf():
     torch = torch_or_skip()
     w = small_workload("empty", 300, 128, 16, 8)

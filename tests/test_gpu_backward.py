@@ -63,6 +63,26 @@ def test_bwd_tile_grid_ragged(M, N):
     _run(w, W.mask_bits(w), f"bwd d128 {M}x{N} L=1000")
 
 
+@pytest.mark.parametrize("N", [1, 8])
+def test_bwd_kept_counts_at_pass_boundaries(N):
+    # kept key tiles per (query tile, 128-key chunk) cycled over the counts a
+    # dQ pass (32 keys, one score block when <= 16 remain) or a dK/dV unit
+    # pair can end on; the dK/dV side sees the same tiles from the key side
+    counts = {1: (0, 1, 15, 16, 17, 31, 32, 33, 48, 49, 128), 8: (0, 1, 2, 3, 4, 5, 8, 15, 16)}[N]
+    L = 1024 + 45
+    w = small_workload(f"bwd_passes_{N}", L, 128, 16, N, seed=300 + N)
+    tpc = 128 // N
+    rng = np.random.default_rng(100 + N)
+    keep = np.zeros((1, w.H, w.T_q, w.T_k), dtype=bool)
+    for h in range(w.H):
+        for i in range(w.T_q):
+            for c in range(-(-w.T_k // tpc)):
+                j0, j1 = c * tpc, min(c * tpc + tpc, w.T_k)
+                n = min(counts[(i + 3 * c + h) % len(counts)], j1 - j0)
+                keep[0, h, i, j0 + rng.choice(j1 - j0, n, replace=False)] = True
+    _run(w, W.pack_bits(keep), f"bwd 16x{N} kept counts at pass boundaries")
+
+
 @pytest.mark.parametrize("M,N,L", [(16, 8, 777), (64, 4, 1029), (16, 1, 500), (32, 64, 300)])
 def test_bwd_head_dim_64(M, N, L):
     w = small_workload(f"bwd64_{M}x{N}", L, 64, M, N, p=0.3, seed=400 + M + N + L)
