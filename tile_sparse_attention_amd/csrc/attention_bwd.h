@@ -127,8 +127,7 @@ struct DkdvCfg {
   static constexpr int RB = 2 * D;              // Q / dO row bytes in memory
   static constexpr int RS = RB + 32;            // row stride in LDS
   static constexpr int NI_T = (QC * RS + 1023) / 1024;  // 1-KB loads per Q (or dO) tile
-  static constexpr int NI = 2 * NI_T + 1;       // + one load of the chunk's lse2 and D
-  static constexpr int NI_W = (NI + W - 1) / W;
+  static constexpr int NQ_W = (NI_T + W - 1) / W;       // Q (and dO) pieces per wave
   static_assert(UNITS == 8 && D % 32 == 0, "shape");
 };
 
@@ -165,6 +164,7 @@ struct DkdvKernel {
   u32x4 kf[C::NSLAB], vf[C::NSLAB];
   f32x4 dk[C::NDB], dv[C::NDB];
   float cs;
+  uint32_t qoff[C::NQ_W];  // per-lane offsets of this wave's Q / dO pieces of a full chunk
 
   __device__ __forceinline__ DkdvKernel(const BwdParams& pp, Buf& b0, Buf& b1) : p(pp), bf0(b0), bf1(b1) {}
 
@@ -173,13 +173,12 @@ struct DkdvKernel {
     return B ? bf1 : bf0;
   }
 
-  // Byte offset read by lane `ln` for 1-KB load I of a chunk with `rows`
-  // query rows (Q tile, dO tile, then the lse2 / D block); out of range
-  // (zero) for row padding; rows past the last repeat it.
+  // Byte offset read by lane `ln` for 1-KB piece I of a chunk's Q (or dO)
+  // tile with `rows` query rows; out of range (zero) for row padding; rows
+  // past the last repeat it.
   __device__ __forceinline__ uint32_t dma_offset(int I, int ln, int rows) const {
     constexpr uint32_t OOB = 0x80000000u;
-    if (I >= 2 * C::NI_T) return 16u * (uint32_t)ln;
-    const int pos = (I < C::NI_T ? I : I - C::NI_T) * 1024 + 16 * ln;
+    const int pos = I * 1024 + 16 * ln;
     const int row = pos / C::RS, cb = pos - row * C::RS;
     const int r = row < rows ? row : rows - 1;
     return row < C::QC && cb < C::RB ? (uint32_t)(r * C::RB + cb) : OOB;
@@ -197,21 +196,29 @@ struct DkdvKernel {
         (void*)(og + (size_t)q0 * D), (short)0, rows * C::RB, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(ldg + (size_t)c * 256), (short)0, 1024, kBufferFlags);
-    const bool full = rows == C::QC;
+    if (rows < C::QC) {  // the last chunk (issued last): offsets for its rows
 #pragma unroll
-    for (int u = 0; u < C::NI_W; ++u) {
-      const int I = wave + C::W * u;
-      if (C::NI % C::W == 0 || I < C::NI) {
-        // (offsets recomputed per chunk: registers are tight)
-        const uint32_t off = dma_offset(I, lane, full ? C::QC : rows);
-        if (I < C::NI_T)
-          dma16(rq, bufr<B>().q + I * 1024, off);
-        else if (I < 2 * C::NI_T)
-          dma16(ro, bufr<B>().o + (I - C::NI_T) * 1024, off);
-        else
-          dma16(rl, bufr<B>().ld, off);
+      for (int u = 0; u < C::NQ_W; ++u) {
+        const int j = wave + C::W * u;
+        qoff[u] = dma_offset(j < C::NI_T ? j : 0, lane, rows);
       }
     }
+    // wave w loads Q and dO pieces w, w + W, ... (same offsets), wave 0 also
+    // the chunk's lse2 / D block
+    typedef __attribute__((address_space(3))) uint8_t* dst_t;
+    const dst_t dq_ = (dst_t)bufr<B>().q, do_ = (dst_t)bufr<B>().o;
+#pragma unroll
+    for (int u = 0; u < C::NQ_W; ++u) {
+      const int j = wave + C::W * u;
+      if (C::NI_T % C::W == 0 || u + 1 < C::NQ_W || j < C::NI_T) {
+        const uint32_t o = qoff[u];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(dq_ + j * 1024), 16,
+                                                 o, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (__attribute__((address_space(3))) void*)(do_ + j * 1024), 16,
+                                                 o, 0, 0, 0);
+      }
+    }
+    if (wave == 0) dma16(rl, bufr<B>().ld, 16u * (uint32_t)lane);
     const int r = q0 + 16 * (lane & (C::UNITS - 1)) < L ? q0 + 16 * (lane & (C::UNITS - 1)) : L - 1;
     return mhead[(size_t)(r / p.M) * p.words + mword];
   }
@@ -381,6 +388,11 @@ struct DkdvKernel {
       dv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const int n_chunks = p.n_qc;
+#pragma unroll
+    for (int u = 0; u < C::NQ_W; ++u) {
+      const int j = wave + C::W * u;
+      qoff[u] = dma_offset(j < C::NI_T ? j : 0, lane, C::QC);
+    }
     const uint32_t mw0 = issue_chunk<0>(0);
     __builtin_amdgcn_s_waitcnt(0);
     Units cur{0u, 0u};
@@ -432,9 +444,7 @@ struct DqCfg {
   static constexpr int NDB = D / 16;
   static constexpr int RB = 2 * D;              // K / V row bytes in memory
   static constexpr int RS = RB + 32;            // row stride in LDS
-  static constexpr int NI_T = (KC * RS + 1023) / 1024;
-  static constexpr int NI = 2 * NI_T;
-  static constexpr int NI_W = (NI + W - 1) / W;
+  static constexpr int NI_T = (KC * RS + 1023) / 1024;  // 1-KB loads per K (or V) tile
   static constexpr int LIST = KC + 32;          // list bytes per wave (entries + padding)
 };
 
@@ -466,6 +476,8 @@ struct DqKernel {
   u32x4 qf[C::NSLAB], df[C::NSLAB];
   f32x4 dq[C::NDB];
   float l2, dd, cs;  // lse2 and D of this lane's query row
+  static constexpr int NK_W = (C::NI_T + C::W - 1) / C::W;  // K (and V) pieces per wave
+  uint32_t koff[NK_W];  // per-lane offsets of this wave's pieces of a full chunk
 
   __device__ __forceinline__ DqKernel(const BwdParams& pp, Buf& b0, Buf& b1, Lists& l)
       : p(pp), bf0(b0), bf1(b1), ls(l) {}
@@ -475,9 +487,12 @@ struct DqKernel {
     return B ? bf1 : bf0;
   }
 
+  // Byte offset read by lane `ln` for 1-KB piece I of a chunk's K (or V)
+  // tile with `rows` keys; out of range (zero) for row padding; rows past
+  // the last repeat it.
   __device__ __forceinline__ uint32_t dma_offset(int I, int ln, int rows) const {
     constexpr uint32_t OOB = 0x80000000u;
-    const int pos = (I < C::NI_T ? I : I - C::NI_T) * 1024 + 16 * ln;
+    const int pos = I * 1024 + 16 * ln;
     const int row = pos / C::RS, cb = pos - row * C::RS;
     const int r = row < rows ? row : rows - 1;
     return row < C::KC && cb < C::RB ? (uint32_t)(r * C::RB + cb) : OOB;
@@ -491,17 +506,25 @@ struct DqKernel {
         (void*)(kg + (size_t)kbase * D), (short)0, rows * C::RB, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vg + (size_t)kbase * D), (short)0, rows * C::RB, kBufferFlags);
-    const bool full = rows == C::KC;
+    if (rows < C::KC) {  // the last chunk (issued last): offsets for its rows
 #pragma unroll
-    for (int u = 0; u < C::NI_W; ++u) {
-      const int I = wave + C::W * u;
-      if (C::NI % C::W == 0 || I < C::NI) {
-        // (offsets recomputed per chunk: registers are tight at 16 waves)
-        const uint32_t off = dma_offset(I, lane, full ? C::KC : rows);
-        if (I < C::NI_T)
-          dma16(rk, bufr<B>().k + I * 1024, off);
-        else
-          dma16(rv, bufr<B>().v + (I - C::NI_T) * 1024, off);
+      for (int u = 0; u < NK_W; ++u) {
+        const int j = wave + C::W * u;
+        koff[u] = dma_offset(j < C::NI_T ? j : 0, lane, rows);
+      }
+    }
+    // wave w loads K and V pieces w, w + W, ... (same offsets)
+    typedef __attribute__((address_space(3))) uint8_t* dst_t;
+    const dst_t dk_ = (dst_t)bufr<B>().k, dv_ = (dst_t)bufr<B>().v;
+#pragma unroll
+    for (int u = 0; u < NK_W; ++u) {
+      const int j = wave + C::W * u;
+      if (C::NI_T % C::W == 0 || u + 1 < NK_W || j < C::NI_T) {
+        const uint32_t o = koff[u];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dk_ + j * 1024), 16,
+                                                 o, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dv_ + j * 1024), 16,
+                                                 o, 0, 0, 0);
       }
     }
     const int w0 = (c * TPC) >> 5;
@@ -672,6 +695,11 @@ struct DqKernel {
 #pragma unroll
     for (int j = 0; j < C::NDB; ++j) dq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int n_chunks = (L + C::KC - 1) / C::KC;
+#pragma unroll
+    for (int u = 0; u < NK_W; ++u) {
+      const int j = wave + C::W * u;
+      koff[u] = dma_offset(j < C::NI_T ? j : 0, lane, C::KC);
+    }
     uint32_t mw[MW];
     issue_chunk<0>(0, mw);
     __builtin_amdgcn_s_waitcnt(0);

@@ -54,8 +54,7 @@ struct KeyCfg {
   static constexpr int RB = D * 2;                 // K / V row bytes in memory
   static constexpr int RS = RB + 32;               // K / V row stride in LDS
   static constexpr int NI_T = (KC * RS + 1023) / 1024;  // 1-KB loads per K (or V) tile
-  static constexpr int NI = 2 * NI_T;
-  static constexpr int NI_W = (NI + W - 1) / W;
+  static constexpr int NK_W = (NI_T + W - 1) / W;  // K (and V) pieces per wave
   static constexpr int LIST = KC + 32;             // list bytes per wave (entries + padding)
   static_assert(N == 1 || N == 2 || N == 4, "key kernel: N in {1,2,4}");
   static_assert(D % 32 == 0 && MW >= 1 && MW <= 4, "shape");
@@ -84,6 +83,7 @@ struct KeyKernel {
   const bf16_t* __restrict__ kg;
   const bf16_t* __restrict__ vg;
   const uint32_t* __restrict__ mrow;
+  uint32_t koff[C::NK_W];  // per-lane offsets of this wave's pieces of a full chunk
   u32x4 qf[C::NSLAB];
   f32x4 oacc[C::NDB + 1];
   float m_ref;        // reference max of this lane's query (log2 units)
@@ -101,13 +101,13 @@ struct KeyKernel {
     return B ? bf1 : bf0;
   }
 
-  // Byte offset read by lane `ln` for 1-KB load `I` (K tile for I < NI_T,
-  // else V tile) of a chunk with `rows` keys, relative to the tile's
-  // resource base; out of range (reads zero) for the padding bytes of an LDS
-  // row.  Rows past the last key repeat it.
+  // Byte offset read by lane `ln` for 1-KB piece `I` of a chunk's K (or V)
+  // tile with `rows` keys, relative to the tile's resource base; out of
+  // range (reads zero) for the padding bytes of an LDS row.  Rows past the
+  // last key repeat it.
   __device__ __forceinline__ uint32_t dma_offset(int I, int ln, int rows) const {
     constexpr uint32_t OOB = 0x80000000u;
-    const int pos = (I < C::NI_T ? I : I - C::NI_T) * 1024 + 16 * ln;
+    const int pos = I * 1024 + 16 * ln;
     const int row = pos / C::RS, cb = pos - row * C::RS;
     const int r = row < rows ? row : rows - 1;
     return row < C::KC && cb < C::RB ? (uint32_t)(r * C::RB + cb) : OOB;
@@ -123,20 +123,25 @@ struct KeyKernel {
         (void*)(kg + (size_t)kbase * D), (short)0, rows * C::RB, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vg + (size_t)kbase * D), (short)0, rows * C::RB, kBufferFlags);
-    const bool full = rows == C::KC;
+    if (rows < C::KC) {  // the last chunk (issued last): offsets for its rows
 #pragma unroll
-    for (int u = 0; u < C::NI_W; ++u) {
-      const int I = wave + C::W * u;
-      if (C::NI % C::W == 0 || I < C::NI) {
-        // (offsets recomputed per chunk: registers are tight at 16 waves)
-        const uint32_t off = dma_offset(I, lane, full ? C::KC : rows);
-        if (I < C::NI_T)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rk, (__attribute__((address_space(3))) void*)(bufr<B>().k + I * 1024), 16, off, 0, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rv, (__attribute__((address_space(3))) void*)(bufr<B>().v + (I - C::NI_T) * 1024), 16,
-              off, 0, 0, 0);
+      for (int u = 0; u < C::NK_W; ++u) {
+        const int j = wave + C::W * u;
+        koff[u] = dma_offset(j < C::NI_T ? j : 0, lane, rows);
+      }
+    }
+    // wave w loads K and V pieces w, w + W, ... (same offsets)
+    typedef __attribute__((address_space(3))) uint8_t* dst_t;
+    const dst_t dk_ = (dst_t)bufr<B>().k, dv_ = (dst_t)bufr<B>().v;
+#pragma unroll
+    for (int u = 0; u < C::NK_W; ++u) {
+      const int j = wave + C::W * u;
+      if (C::NI_T % C::W == 0 || u + 1 < C::NK_W || j < C::NI_T) {
+        const uint32_t o = koff[u];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dk_ + j * 1024), 16,
+                                                 o, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dv_ + j * 1024), 16,
+                                                 o, 0, 0, 0);
       }
     }
     const int w0 = (c * C::TPC) >> 5;
@@ -363,6 +368,11 @@ struct KeyKernel {
     ones = u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
 
     const int n_chunks = (L + C::KC - 1) / C::KC;
+#pragma unroll
+    for (int u = 0; u < C::NK_W; ++u) {
+      const int j = wave + C::W * u;
+      koff[u] = dma_offset(j < C::NI_T ? j : 0, lane, C::KC);
+    }
     uint32_t mw[C::MW];
     issue_chunk<0>(0, mw);
     __builtin_amdgcn_s_waitcnt(0);

@@ -80,8 +80,8 @@ struct OctCfg {
   static constexpr int VROWS_LDS = D;              // V^T rows staged (the ones row is not read)
   static constexpr int NI_K = (KC * KRS + 1023) / 1024;     // 1-KB loads per K chunk
   static constexpr int NI_V = (VROWS_LDS * VRS + 1023) / 1024;  // 1-KB loads per V^T chunk
-  static constexpr int NI = NI_K + NI_V;
-  static constexpr int NI_W = (NI + W - 1) / W;
+  static constexpr int NK_W = (NI_K + W - 1) / W;                // K pieces per wave
+  static constexpr int NV_W = (NI_V + W - 1) / W;                // V^T pieces per wave
   static_assert(N >= 8 && N <= 64 && (N & (N - 1)) == 0, "octet kernel: N in {8,16,32,64}");
   static_assert(D % 32 == 0, "head dim");
   static_assert(!F8 || D == 128, "FP8 scores: d = 128 (one 16x16x128 step)");
@@ -169,7 +169,7 @@ struct OctKernel {
   float cs;           // |scale| * log2(e)
   float thr;          // rescale threshold on unscaled scores: -inf before the first pass,
                       // then RESCALE_STEP / cs
-  uint32_t doff[C::NI_W];  // per-lane load offsets of a full chunk (chunk-invariant)
+  uint32_t doffk[C::NK_W], doffv[C::NV_W];  // per-lane load offsets of a full chunk's K and V^T pieces
 
   __device__ __forceinline__ OctKernel(const AttnParams& pp, Smem& s) : p(pp), sm(s) {}
 
@@ -198,19 +198,32 @@ struct OctKernel {
         (void*)(kg + (size_t)kbase * C::KRB), (short)0, rows * C::KRB, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vtg + kbase), (short)0, (C::VROWS * p.L_pad - kbase) * 2, kBufferFlags);
-    const bool full = rows == C::KC;
+    if (rows < C::KC) {  // the last chunk (visited last): K offsets for its rows
 #pragma unroll
-    for (int u = 0; u < C::NI_W; ++u) {
-      const int I = wave + C::W * u;
-      if (C::NI % C::W == 0 || I < C::NI) {
-        if (I < C::NI_K)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rk, (__attribute__((address_space(3))) void*)(sm.k[buf] + I * 1024), 16,
-              full ? doff[u] : dma_offset(I, lane, rows), 0, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rv, (__attribute__((address_space(3))) void*)(sm.vt[buf] + (I - C::NI_K) * 1024), 16,
-              doff[u], 0, 0, 0);
+      for (int u = 0; u < C::NK_W; ++u) {
+        const int j = wave + C::W * u;
+        if (j < C::NI_K) doffk[u] = dma_offset(j, lane, rows);
+      }
+    }
+    // wave w loads K pieces w, w + W, ... and V^T pieces w, w + W, ...
+    typedef __attribute__((address_space(3))) uint8_t* dst_t;
+    const dst_t dk = (dst_t)sm.k[buf], dv = (dst_t)sm.vt[buf];
+#pragma unroll
+    for (int u = 0; u < C::NK_W; ++u) {
+      const int j = wave + C::W * u;
+      if (C::NI_K % C::W == 0 || u + 1 < C::NK_W || j < C::NI_K) {
+        const uint32_t o = doffk[u];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dk + j * 1024), 16,
+                                                 o, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < C::NV_W; ++u) {
+      const int j = wave + C::W * u;
+      if (C::NI_V % C::W == 0 || u + 1 < C::NV_W || j < C::NI_V) {
+        const uint32_t o = doffv[u];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dv + j * 1024), 16,
+                                                 o, 0, 0, 0);
       }
     }
     const int wi = (c * C::TPC) >> 5;
@@ -486,9 +499,14 @@ struct OctKernel {
     ones = u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
 
 #pragma unroll
-    for (int u = 0; u < C::NI_W; ++u) {
-      const int I = wave + C::W * u;
-      doff[u] = I < C::NI ? dma_offset(I, lane, C::KC) : 0u;
+    for (int u = 0; u < C::NK_W; ++u) {
+      const int j = wave + C::W * u;
+      doffk[u] = j < C::NI_K ? dma_offset(j, lane, C::KC) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < C::NV_W; ++u) {
+      const int j = wave + C::W * u;
+      doffv[u] = j < C::NI_V ? dma_offset(C::NI_K + j, lane, C::KC) : 0u;
     }
     const int n_chunks = (L + C::KC - 1) / C::KC;
     if constexpr (SKIP) {
