@@ -114,11 +114,11 @@ _PASS_COUNTS = {1: (0, 1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64, 65, 100, 1
                 16: (0, 1, 2, 3, 4, 5, 6, 7, 8)}
 
 
-@pytest.mark.parametrize("N", [1, 2, 4, 8, 16])
-def test_kept_counts_at_pass_boundaries(N):
+@pytest.mark.parametrize("N,d", [(1, 128), (2, 128), (4, 128), (8, 128), (16, 128), (1, 64), (8, 64)])
+def test_kept_counts_at_pass_boundaries(N, d):
     torch_or_skip()
     L = 2048 + 77   # 16 whole chunks and a partial one
-    w = small_workload(f"passes_{N}", L, 128, 16, N, seed=200 + N)
+    w = small_workload(f"passes_{N}_{d}", L, d, 16, N, seed=200 + N + d)
     tpc = 128 // N
     counts = _PASS_COUNTS[N]
     rng = np.random.default_rng(N)
@@ -129,7 +129,7 @@ def test_kept_counts_at_pass_boundaries(N):
                 j0, j1 = c * tpc, min(c * tpc + tpc, w.T_k)
                 n = min(counts[(i + 3 * c + h) % len(counts)], j1 - j0)
                 keep[0, h, i, j0 + rng.choice(j1 - j0, n, replace=False)] = True
-    full_compare(w, W.pack_bits(keep), f"bf16 16x{N} kept counts at pass boundaries")
+    full_compare(w, W.pack_bits(keep), f"bf16 d={d} 16x{N} kept counts at pass boundaries")
 
 
 def test_empty_mask_gives_zero_and_minus_inf():
