@@ -206,18 +206,8 @@ struct DkdvKernel {
     // wave w loads Q and dO pieces w, w + W, ... (same offsets), wave 0 also
     // the chunk's lse2 / D block
     typedef __attribute__((address_space(3))) uint8_t* dst_t;
-    const dst_t dq_ = (dst_t)bufr<B>().q, do_ = (dst_t)bufr<B>().o;
-#pragma unroll
-    for (int u = 0; u < C::NQ_W; ++u) {
-      const int j = wave + C::W * u;
-      if (C::NI_T % C::W == 0 || u + 1 < C::NQ_W || j < C::NI_T) {
-        const uint32_t o = qoff[u];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(dq_ + j * 1024), 16,
-                                                 o, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (__attribute__((address_space(3))) void*)(do_ + j * 1024), 16,
-                                                 o, 0, 0, 0);
-      }
-    }
+    load_pieces<C::NI_T, C::W>(rq, (dst_t)bufr<B>().q, qoff, wave);
+    load_pieces<C::NI_T, C::W>(ro, (dst_t)bufr<B>().o, qoff, wave);
     if (wave == 0) dma16(rl, bufr<B>().ld, 16u * (uint32_t)lane);
     const int r = q0 + 16 * (lane & (C::UNITS - 1)) < L ? q0 + 16 * (lane & (C::UNITS - 1)) : L - 1;
     return mhead[(size_t)(r / p.M) * p.words + mword];
@@ -515,18 +505,8 @@ struct DqKernel {
     }
     // wave w loads K and V pieces w, w + W, ... (same offsets)
     typedef __attribute__((address_space(3))) uint8_t* dst_t;
-    const dst_t dk_ = (dst_t)bufr<B>().k, dv_ = (dst_t)bufr<B>().v;
-#pragma unroll
-    for (int u = 0; u < NK_W; ++u) {
-      const int j = wave + C::W * u;
-      if (C::NI_T % C::W == 0 || u + 1 < NK_W || j < C::NI_T) {
-        const uint32_t o = koff[u];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dk_ + j * 1024), 16,
-                                                 o, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dv_ + j * 1024), 16,
-                                                 o, 0, 0, 0);
-      }
-    }
+    load_pieces<C::NI_T, C::W>(rk, (dst_t)bufr<B>().k, koff, wave);
+    load_pieces<C::NI_T, C::W>(rv, (dst_t)bufr<B>().v, koff, wave);
     const int w0 = (c * TPC) >> 5;
 #pragma unroll
     for (int i = 0; i < MW; ++i) {

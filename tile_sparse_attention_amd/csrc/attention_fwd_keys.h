@@ -132,18 +132,8 @@ struct KeyKernel {
     }
     // wave w loads K and V pieces w, w + W, ... (same offsets)
     typedef __attribute__((address_space(3))) uint8_t* dst_t;
-    const dst_t dk_ = (dst_t)bufr<B>().k, dv_ = (dst_t)bufr<B>().v;
-#pragma unroll
-    for (int u = 0; u < C::NK_W; ++u) {
-      const int j = wave + C::W * u;
-      if (C::NI_T % C::W == 0 || u + 1 < C::NK_W || j < C::NI_T) {
-        const uint32_t o = koff[u];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dk_ + j * 1024), 16,
-                                                 o, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dv_ + j * 1024), 16,
-                                                 o, 0, 0, 0);
-      }
-    }
+    load_pieces<C::NI_T, C::W>(rk, (dst_t)bufr<B>().k, koff, wave);
+    load_pieces<C::NI_T, C::W>(rv, (dst_t)bufr<B>().v, koff, wave);
     const int w0 = (c * C::TPC) >> 5;
     // scalar loads (the mask is read-only here): the words land in scalar
     // registers

@@ -207,25 +207,8 @@ struct OctKernel {
     }
     // wave w loads K pieces w, w + W, ... and V^T pieces w, w + W, ...
     typedef __attribute__((address_space(3))) uint8_t* dst_t;
-    const dst_t dk = (dst_t)sm.k[buf], dv = (dst_t)sm.vt[buf];
-#pragma unroll
-    for (int u = 0; u < C::NK_W; ++u) {
-      const int j = wave + C::W * u;
-      if (C::NI_K % C::W == 0 || u + 1 < C::NK_W || j < C::NI_K) {
-        const uint32_t o = doffk[u];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dk + j * 1024), 16,
-                                                 o, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < C::NV_W; ++u) {
-      const int j = wave + C::W * u;
-      if (C::NI_V % C::W == 0 || u + 1 < C::NV_W || j < C::NI_V) {
-        const uint32_t o = doffv[u];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dv + j * 1024), 16,
-                                                 o, 0, 0, 0);
-      }
-    }
+    load_pieces<C::NI_K, C::W>(rk, (dst_t)sm.k[buf], doffk, wave);
+    load_pieces<C::NI_V, C::W>(rv, (dst_t)sm.vt[buf], doffv, wave);
     const int wi = (c * C::TPC) >> 5;
     // a scalar load (the mask is read-only here): it does not queue behind
     // the chunk's LDS loads

@@ -132,6 +132,26 @@ __device__ __forceinline__ u32x2 lds_read_tr16(lds_cptr a) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a));
 }
 
+// Direct global-to-LDS loads of a staged tile cut into NP pieces of 1 KB (16
+// bytes per lane): a wave issues pieces wave, wave + W, ... below NP, each from
+// buffer resource r at its lanes' source offsets off[u] (computed once by the
+// caller) into piece j of the LDS tile at dst.  Every wave takes the same
+// static slots, so no load picks its tile or computes its offset at run time.
+template <int NP, int W>
+__device__ __forceinline__ void load_pieces(__amdgpu_buffer_rsrc_t r, __attribute__((address_space(3))) uint8_t* dst,
+                                            const uint32_t (&off)[(NP + W - 1) / W], int wave) {
+  constexpr int NS = (NP + W - 1) / W;
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const int j = wave + W * u;
+    if (NP % W == 0 || u + 1 < NS || j < NP) {
+      const uint32_t o = off[u];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + j * 1024), 16, o,
+                                               0, 0, 0);
+    }
+  }
+}
+
 // a * b + c (24-bit operands, b wave-uniform) and (a << 4) + c as single
 // instructions; the compiler otherwise splits both into two.
 __device__ __forceinline__ uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c) {
