@@ -95,6 +95,28 @@ def test_fp8_attention_parity(M, N, L):
     _run(w, W.mask_bits(w), f"fp8 {M}x{N} L={L}")
 
 
+# kept tiles per (query tile, 128-key chunk) cycling through every count a
+# pass can end on: four octets per pass, a short last pass at one or two
+_PASS_COUNTS = {8: (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 15, 16), 16: (0, 1, 2, 3, 4, 5, 6, 7, 8)}
+
+
+@pytest.mark.parametrize("N", [8, 16])
+def test_fp8_kept_counts_at_pass_boundaries(N):
+    L = 2048 + 77   # 16 whole chunks and a partial one
+    w = small_workload(f"f8_passes_{N}", L, 128, 16, N, seed=840 + N)
+    tpc = 128 // N
+    counts = _PASS_COUNTS[N]
+    rng = np.random.default_rng(40 + N)
+    keep = np.zeros((1, w.H, w.T_q, w.T_k), dtype=bool)
+    for h in range(w.H):
+        for i in range(w.T_q):
+            for c in range(-(-w.T_k // tpc)):
+                j0, j1 = c * tpc, min(c * tpc + tpc, w.T_k)
+                n = min(counts[(i + 3 * c + h) % len(counts)], j1 - j0)
+                keep[0, h, i, j0 + rng.choice(j1 - j0, n, replace=False)] = True
+    _run(w, W.pack_bits(keep), f"fp8 16x{N} kept counts at pass boundaries")
+
+
 def test_fp8_attention_negative_scale_and_batch():
     w = W.Workload("f8_neg", 2, 3, 600, 128, 16, 16, "bf16",
                    W.MaskRecipe("hash", p_near=0.4, p_far=0.4, force_diag=True), 81)
