@@ -19,8 +19,10 @@
  *   - A query row with no kept key gets O = 0 and LSE = -inf.
  *   - Every call is asynchronous on the caller's `stream` (a hipStream_t; NULL
  *     is the default stream).  Outputs are valid once the stream has reached
- *     the work.  The library allocates no device memory and keeps no state
- *     between calls; the caller owns every buffer.
+ *     the work.  The library allocates no device memory and the caller owns
+ *     every buffer.  Between calls it keeps only the calling thread's
+ *     measurement events (tsa_set_timing_events), the last error text, and
+ *     the static per-GPU scratch of tsa_attention_fwd_noalloc.
  *   - Arguments are checked before anything is enqueued.  A failed check
  *     enqueues nothing and returns a status; no call aborts or throws.
  *     tsa_last_error() returns the calling thread's detail text of its last
