@@ -29,8 +29,10 @@
  *     failure.
  *
  * Supported problem set: dtype in {F32, BF16}; d in {64, 128}; M in {16, 32, 64};
- * N in {1, 2, 4, 8, 16, 32, 64}; 1 <= L <= 2^22; B*H <= 2^20.  Other values
- * return TSA_ERR_UNSUPPORTED.
+ * N in {1, 2, 4, 8, 16, 32, 64}; 1 <= L <= 2^22; B*H <= 2^20; and for the
+ * attention calls B*H*(L + 256) <= 2^30 - 1 (their grids hold about 4
+ * work-items per row; any problem whose tensors fit in device memory
+ * qualifies).  Other values return TSA_ERR_UNSUPPORTED.
  */
 #ifndef TSA_H_
 #define TSA_H_
@@ -133,7 +135,7 @@ tsa_status_t tsa_set_timing_events(void* start_event, void* stop_event);
  * of a head, and k_scale [B,H] fp32, one per head.  A scale is the tile's
  * largest |x| / 448 (1 for an all-zero tile); a value becomes the e4m3 number
  * nearest to x / scale, ties to even.  q8, k8: [B,H,L,128] bytes.  p->dtype must
- * be bf16, p->d 128 and B*H <= 65535; M and N are not read.  No workspace
+ * be bf16 and p->d 128; M and N are not read.  No workspace
  * (k8 serves as scratch for the per-head maxima before it is written).  The quantisation
  * is this library's reading of the per-tile scaling named beside the pages'
  * method (FG-Attn itself fixes no precision). */

@@ -41,10 +41,11 @@ def keep_matrix(mask_bits_head, L: int, M: int, N: int, rows=None) -> np.ndarray
     mask_bits_head: uint32 [T_q, words].  rows: query rows to expand (default all).
     """
     T_k = -(-L // N)
-    tiles = unpack_mask(mask_bits_head, T_k)               # [T_q, T_k]
     r = np.arange(L) if rows is None else np.asarray(rows)
     c = np.arange(L)
-    return tiles[r // M][:, c // N]
+    # only the bitmap rows of the requested query rows are unpacked
+    tiles = unpack_mask(np.asarray(mask_bits_head)[r // M], T_k)   # [len(r), T_k]
+    return tiles[:, c // N]
 
 
 def _softmax_pv(s: np.ndarray, keep: np.ndarray, v: np.ndarray):

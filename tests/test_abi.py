@@ -75,6 +75,15 @@ def test_attention_rejects_bad_problem(field, value, status):
     assert T.last_error() != ""
 
 
+def test_attention_rejects_grids_beyond_one_dispatch():
+    # a dispatch holds fewer than 2^32 work-items per dimension, and the
+    # attention grids hold 4 per (b, h) and row with 256 rows of padding
+    pr = T.problem(1, 1 << 20, 768, 64, 16, 16)     # 2^20 * 1024 * 4 = 2^32
+    assert _attn(pr) == T.ERR_UNSUPPORTED and "grid" in T.last_error()
+    pr = T.problem(1, 1 << 20, 767, 64, 16, 16)     # one row less: on to the workspace check
+    assert _attn(pr) == T.ERR_WORKSPACE_TOO_SMALL
+
+
 def test_attention_rejects_bad_pointers_and_scale():
     pr = T.problem(1, 2, 512, 64, 16, 16, T.DTYPE_F32)
     assert _attn(pr, q=0) == T.ERR_INVALID_ARGUMENT

@@ -1,0 +1,121 @@
+"""GPU parity at the limits of the supported problem set: the longest
+sequence (L = 2^22) and the most (batch, head) pairs (B*H = 2^20).
+
+Inputs are seeded and synthetic.  At L = 2^22 the bitmap of 16x8 tiles holds
+2^32 words (17 GB) and is made on the GPU by the counter-based generator;
+the sampled query tiles' rows come from the host generator (checked equal to
+the GPU's first) and the oracle evaluates those tiles one at a time.  At
+B*H = 2^20 every head takes its Q, K, V from one of 4096 seeded heads (head h
+of batch b uses head h mod 4096 of a [1, 4096, L, d] draw), while its mask
+rows are its own; sampled heads are compared in full, and the FP8
+quantisation of every sampled head is compared byte for byte.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import compare, say, torch_or_skip
+from oracle import fp8
+
+pytestmark = pytest.mark.gpu
+
+L_MAX = 1 << 22
+BH_MAX = 1 << 20
+
+
+@pytest.mark.timeout(900)
+def test_maximum_sequence_length():
+    """L = 2^22 (the plain octet kernel: more chunks than chunk skipping
+    handles), one head, 16x8 tiles, i.i.d. 2% keep with the diagonal kept:
+    16 sampled query tiles, the first and the last among them."""
+    torch = torch_or_skip()
+    import tile_sparse_attention_amd as T
+    w = W.Workload("maxlen", 1, 1, L_MAX, 128, 16, 8, "bf16",
+                   W.MaskRecipe("hash", p_near=0.02, p_far=0.02, force_diag=True), 4321)
+    say(f"limits L={w.L} 16x8: generating inputs")
+    q, k, v = W.make_qkv(w)
+    mask = T.maskgen_hash(w.B, w.H, w.L, w.M, w.N, **W.hash_params(w))
+    say(f"limits L={w.L} 16x8: attention on GPU (bitmap {mask.numel() * 4 / 2**30:.1f} GiB)")
+    o, lse = T.attention_fwd(q.cuda(), k.cuda(), v.cuda(), mask, w.M, w.N, w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(17)
+    tiles = np.unique(np.concatenate([[0, w.T_q - 1], rng.choice(w.T_q, 14, replace=False)]))
+    # host rows of the sampled tiles only (the rest of this zero array is never touched)
+    bits = np.zeros((w.T_q, w.words), dtype=np.uint32)
+    bits[tiles] = W.pack_bits(W.mask_rows_bool(w, [(0, 0, int(i)) for i in tiles]))
+    dev_rows = mask[0, 0, torch.from_numpy(tiles).cuda()].cpu().numpy().view(np.uint32)
+    assert np.array_equal(dev_rows, bits[tiles])
+    del mask
+    say(f"limits L={w.L} 16x8: oracle on {len(tiles)} tiles")
+    rows, ro, rl = oracle.attention_rows(q[0, 0], k[0, 0], v[0, 0], bits, w.M, w.N, w.scale, tiles, group=1)
+    compare(f"limits L={w.L}", o[0, 0, torch.from_numpy(rows).cuda()].float().cpu().numpy(), ro, w.dtype,
+            lse[0, 0, torch.from_numpy(rows).cuda()].cpu().numpy(), rl)
+
+
+def _max_heads_inputs(w_src, B, H):
+    """Q, K, V of B*H heads on the GPU, head (b, h) equal to head h mod the
+    source heads of the seeded draw w_src."""
+    torch_or_skip()
+    src = W.make_qkv(w_src)
+    reps = B * H // w_src.H
+    L, d = w_src.L, w_src.d
+    return [x.cuda().reshape(w_src.H, L, d).repeat(reps, 1, 1).reshape(B, H, L, d) for x in src], src
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("M,N", [(16, 8), (16, 1)])
+def test_maximum_heads(M, N):
+    """B*H = 2^20 (B = 16, H = 65536) at L = 40 (three query tiles, the last
+    partial), d = 64, bf16: the octet kernel (16x8) and the key kernel (16x1)
+    over a grid of 2^20 work-groups; eight sampled heads compared in full."""
+    torch = torch_or_skip()
+    import tile_sparse_attention_amd as T
+    B, H, L, d = 16, BH_MAX // 16, 40, 64
+    src = W.Workload("maxheads_src", 1, 4096, L, d, M, N, "bf16", W.MaskRecipe("hash", p_near=0.3, p_far=0.3), 97)
+    w = W.Workload("maxheads", B, H, L, d, M, N, "bf16",
+                   W.MaskRecipe("hash", p_near=0.3, p_far=0.3, force_diag=True), 98 + N)
+    say(f"limits B*H={B * H} L={L} d={d} {M}x{N}: inputs")
+    (qd, kd, vd), (q, k, v) = _max_heads_inputs(src, B, H)
+    mask = T.maskgen_hash(B, H, L, M, N, **W.hash_params(w))
+    say(f"limits B*H={B * H} {M}x{N}: attention on GPU")
+    o, lse = T.attention_fwd(qd, kd, vd, mask, M, N, w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    del qd, kd, vd
+    rng = np.random.default_rng(5 + N)
+    heads = [(0, 0), (0, 1), (B - 1, H - 1), (B // 2, 4095), (7, 4096)] + \
+            [(int(b), int(h)) for b, h in zip(rng.integers(0, B, 3), rng.integers(0, H, 3))]
+    got, ref, gl, rl = [], [], [], []
+    for b, h in heads:
+        bits = W.pack_bits(W.mask_rows_bool(w, [(b, h, i) for i in range(w.T_q)]))
+        assert np.array_equal(mask[b, h].cpu().numpy().view(np.uint32), bits)
+        s = h % src.H
+        ro, rlse = oracle.attention(q[:, s:s + 1], k[:, s:s + 1], v[:, s:s + 1], bits[None, None], M, N, w.scale)
+        got.append(o[b, h].float().cpu().numpy())
+        ref.append(ro[0, 0])
+        gl.append(lse[b, h].cpu().numpy())
+        rl.append(rlse[0, 0])
+    compare(f"limits B*H={B * H} {M}x{N}", np.concatenate(got), np.concatenate(ref), "bf16",
+            np.concatenate(gl), np.concatenate(rl))
+
+
+@pytest.mark.timeout(600)
+def test_fp8_quantisation_at_maximum_heads():
+    """The e4m3 quantisation of Q and K over B*H = 2^20 heads (L = 40, d = 128;
+    the per-head K maxima run over a one-dimensional grid of 64 slices per
+    head): sampled heads byte for byte against the oracle."""
+    torch = torch_or_skip()
+    import tile_sparse_attention_amd as T
+    B, H, L = 16, BH_MAX // 16, 40
+    src = W.Workload("maxheads_f8", 1, 4096, L, 128, 16, 8, "bf16", W.MaskRecipe("hash", p_near=0.3, p_far=0.3), 99)
+    say(f"limits B*H={B * H} L={L}: fp8 quantisation")
+    (qd, kd, _), (q, k, _) = _max_heads_inputs(src, B, H)
+    q8, qs, k8, ks = T.quantize_qk_fp8(qd, kd)
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (B - 1, H - 1), (3, 4097), (11, 60000)]:
+        s = h % src.H
+        rq, rqs, rk, rks = fp8.quantize_qk(q[:, s:s + 1], k[:, s:s + 1])
+        assert np.array_equal(qs[b, h].cpu().numpy(), rqs[0, 0]) and np.array_equal(ks[b, h].cpu().numpy(), rks[0, 0])
+        got_q = q8[b, h].cpu().view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+        got_k = k8[b, h].cpu().view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+        assert np.array_equal(got_q, rq[0, 0]) and np.array_equal(got_k, rk[0, 0])

@@ -55,7 +55,14 @@ bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(pt
 
 constexpr int kMaxL = 1 << 22;
 constexpr long long kMaxBH = 1 << 20;
-constexpr long long kMaxGrid = 0x7fffffffLL;
+// A dispatch holds fewer than 2^32 work-items in each grid dimension.  The
+// attention kernels' grids hold at most 4 work-items per (b, h) and key (or
+// query) row, padding included; every other kernel steps through its items
+// with a capped grid.
+constexpr long long kMaxWorkItems = 0xffffffffLL;
+inline bool attention_grid_fits(const tsa_problem_t* p) {
+  return (long long)p->B * p->H * ((long long)p->L + 256) * 4 <= kMaxWorkItems;
+}
 
 // Shape checks common to every call.  need_d: check d and dtype.
 tsa_status_t check_problem(const tsa_problem_t* p, bool need_d) {
@@ -78,10 +85,6 @@ tsa_status_t check_problem(const tsa_problem_t* p, bool need_d) {
   return TSA_OK;
 }
 
-long long n_rows(const tsa_problem_t* p) {
-  return (long long)p->B * p->H * ((p->L + p->M - 1) / p->M);
-}
-
 // Argument checks of the forward, shared by its two entry points.
 tsa_status_t check_fwd(const tsa_problem_t* p, const void* q, const void* k, const void* v,
                        const uint32_t* mask_bits, float scale, const void* o, const float* lse) {
@@ -94,8 +97,7 @@ tsa_status_t check_fwd(const tsa_problem_t* p, const void* q, const void* k, con
       !aligned(mask_bits, 4) || (lse && !aligned(lse, 4)))
     return fail(TSA_ERR_INVALID_ARGUMENT, "q/k/v/o need 16-byte, mask/lse 4-byte alignment");
   if (o == q || o == k || o == v) return fail(TSA_ERR_INVALID_ARGUMENT, "o aliases an input");
-  const long long blocks = (long long)p->B * p->H * ((p->L + 63) / 64);
-  if (blocks > kMaxGrid) return fail(TSA_ERR_UNSUPPORTED, "grid too large");
+  if (!attention_grid_fits(p)) return fail(TSA_ERR_UNSUPPORTED, "B*H*(L+256) above 2^30: grid too large");
   return TSA_OK;
 }
 
@@ -220,8 +222,6 @@ tsa_status_t tsa_quantize_qk_fp8(const tsa_problem_t* p, const void* q, const vo
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q8, 16) || !aligned(k8, 16) || !aligned(q_scale, 4) ||
       !aligned(k_scale, 4))
     return fail(TSA_ERR_INVALID_ARGUMENT, "tensors need 16-byte, scales 4-byte alignment");
-  if ((long long)p->B * p->H * (long long)p->L * 16 / 256 > kMaxGrid || (long long)p->B * p->H > 65535)
-    return fail(TSA_ERR_UNSUPPORTED, "grid too large (B*H <= 65535 for the FP8 quantisation)");
   const hipError_t e = tsa::launch_quantize_qk_fp8(p, q, k, q8, q_scale, k8, k_scale,
                                                    static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "FP8 quantisation launch");
@@ -248,8 +248,7 @@ tsa_status_t tsa_attention_fwd_fp8(const tsa_problem_t* p, const uint8_t* q8, co
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
     return fail(TSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, 256-byte aligned (got %zu)",
                 need, workspace_bytes);
-  const long long blocks = (long long)p->B * p->H * ((p->L + 63) / 64);
-  if (blocks > kMaxGrid) return fail(TSA_ERR_UNSUPPORTED, "grid too large");
+  if (!attention_grid_fits(p)) return fail(TSA_ERR_UNSUPPORTED, "B*H*(L+256) above 2^30: grid too large");
   tsa::AttnLaunch a{p, q8, k8, v, mask_bits, scale, o, lse, workspace, static_cast<hipStream_t>(stream)};
   a.q_scale = q_scale;
   a.k_scale = k_scale;
@@ -282,8 +281,7 @@ tsa_status_t tsa_attention_bwd(const tsa_problem_t* p, const void* q, const void
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
     return fail(TSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, 256-byte aligned (got %zu)",
                 need, workspace_bytes);
-  if ((long long)p->B * p->H * ((p->L + 127) / 128) > kMaxGrid)
-    return fail(TSA_ERR_UNSUPPORTED, "grid too large");
+  if (!attention_grid_fits(p)) return fail(TSA_ERR_UNSUPPORTED, "B*H*(L+256) above 2^30: grid too large");
   tsa::BwdLaunch a{p, q, k, v, o, d_o, lse, mask_bits, scale, dq, dk, dv, workspace,
                    static_cast<hipStream_t>(stream)};
   const hipError_t e = tsa::launch_attention_bwd(a);
@@ -300,7 +298,6 @@ tsa_status_t tsa_mask_diff(const tsa_problem_t* p, const uint32_t* mask_a, const
   if (!aligned(mask_a, 4) || !aligned(mask_b, 4) || !aligned(row_changed, 8) ||
       (head_changed && !aligned(head_changed, 8)))
     return fail(TSA_ERR_INVALID_ARGUMENT, "masks need 4-byte, counts 8-byte alignment");
-  if ((n_rows(p) + 3) / 4 > kMaxGrid) return fail(TSA_ERR_UNSUPPORTED, "grid too large");
   const hipError_t e = tsa::launch_mask_diff(p, mask_a, mask_b, row_changed, head_changed,
                                              static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mask diff launch");
@@ -317,7 +314,6 @@ tsa_status_t tsa_mask_compact(const tsa_problem_t* p, const uint32_t* mask_bits,
   if (col_capacity > 0 && !col_idx) return fail(TSA_ERR_INVALID_ARGUMENT, "col_idx is NULL");
   if (!aligned(mask_bits, 4) || !aligned(row_ptr, 8) || (col_idx && !aligned(col_idx, 4)))
     return fail(TSA_ERR_INVALID_ARGUMENT, "misaligned pointer");
-  if ((n_rows(p) + 3) / 4 > kMaxGrid) return fail(TSA_ERR_UNSUPPORTED, "too many rows");
   const size_t need = tsa::mask_compact_workspace(p);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
     return fail(TSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, 256-byte aligned (got %zu)",
@@ -355,8 +351,6 @@ tsa_status_t tsa_maskgen_hash(const tsa_problem_t* p, const tsa_maskgen_params_t
   if (!g || !mask_out) return fail(TSA_ERR_INVALID_ARGUMENT, "params and mask_out must be non-NULL");
   if (g->frame_tokens < 0 || g->frame_radius < 0 || g->thr_near > (1u << 24) || g->thr_far > (1u << 24))
     return fail(TSA_ERR_INVALID_ARGUMENT, "bad generator parameters");
-  const long long words = n_rows(p) * tsa_mask_row_words(p->L, p->N);
-  if ((words + 255) / 256 > kMaxGrid) return fail(TSA_ERR_UNSUPPORTED, "bitmap too large");
   const hipError_t e = tsa::launch_maskgen_hash(p, g, mask_out, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mask generator launch");
   return TSA_OK;
@@ -382,8 +376,6 @@ tsa_status_t tsa_maskgen_structured(const tsa_problem_t* p, const tsa_structured
       (multi && (g->frame_tokens <= 0 || g->reach < 0 || g->reach > 64)) ||
       (stripe && (g->stripe_period <= 0 || g->stripe_width < 0 || g->stripe_width > g->stripe_period)))
     return fail(TSA_ERR_INVALID_ARGUMENT, "bad structured-mask parameters");
-  const long long words = n_rows(p) * tsa_mask_row_words(p->L, p->N);
-  if ((words + 255) / 256 > kMaxGrid) return fail(TSA_ERR_UNSUPPORTED, "bitmap too large");
   const hipError_t e = tsa::launch_maskgen_structured(p, g, head_pattern, mask_out,
                                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mask generator launch");

@@ -598,8 +598,11 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const T* __restrict__ v, T
   constexpr int CPR = D / VEC;       // 16-byte chunks per V row
   constexpr int TS = D + 2;          // LDS row stride (elements), odd word stride for bf16
   __shared__ T tile[64 * TS];
-  const int bh = blockIdx.y;
-  const int k0 = blockIdx.x * 64;
+  // one-dimensional grid (B*H may exceed the y-dimension limit): block
+  // (bh, 64-key group) = blockIdx.x / groups, blockIdx.x % groups
+  const unsigned groups = (unsigned)(L_pad / 64);
+  const int bh = (int)(blockIdx.x / groups);
+  const int k0 = (int)(blockIdx.x - (unsigned)bh * groups) * 64;
   const T* src = v + ((size_t)bh * L) * D;
   for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
     const int r = i / CPR, ch = i % CPR;

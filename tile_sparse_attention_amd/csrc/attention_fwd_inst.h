@@ -37,9 +37,11 @@ inline AttnParams attn_params(const AttnLaunch& a, int rows_per_block) {
 
 template <typename T, int D>
 void launch_vt_pack(const AttnLaunch& a, const AttnParams& p) {
-  hipLaunchKernelGGL((vt_pack_kernel<T, D>), dim3((unsigned)(p.L_pad / 64), (unsigned)(a.p->B * a.p->H)),
-                     dim3(256), 0, a.stream, static_cast<const T*>(a.v), static_cast<T*>(a.workspace),
-                     a.p->L, p.L_pad);
+  // a block per 64 keys of each (b, h), on the x dimension only; any problem
+  // whose tensors fit in memory stays below 2^31 blocks
+  const long long blocks = (long long)(p.L_pad / 64) * a.p->B * a.p->H;
+  hipLaunchKernelGGL((vt_pack_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                     static_cast<const T*>(a.v), static_cast<T*>(a.workspace), a.p->L, p.L_pad);
 }
 
 template <typename T, int D, int N, int KC, int W, int TPW>

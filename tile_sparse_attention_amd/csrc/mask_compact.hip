@@ -3,7 +3,9 @@
 // FG-Attn ("FG-Attn: Leveraging Fine-Grained Sparse Attention in Video
 // Diffusion Models", section Abstract) makes one skip decision per M x N tile;
 // this turns each query-tile row of decisions into the ascending list of kept
-// key tiles.  Three passes, all bandwidth-bound scans of the bitmap:
+// key tiles.  Three passes, all bandwidth-bound scans of the bitmap (the
+// count and fill work-groups step through their row groups with the grid's
+// stride, so any number of rows fits one launch):
 //   1. count:  one wave per row sums the popcounts of its words (padding bits
 //              past T_k cleared) and each work-group sums its 16 rows;
 //   2. scan:   one work-group turns the per-group sums into int64 offsets;
@@ -31,37 +33,41 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void compact_count_kernel(const
   __shared__ int part[kRowsPerGroup];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const long long row = (long long)blockIdx.x * kRowsPerGroup + wave;
-  int cnt = 0;
-  if (row < rows) {
-    const uint32_t* r = mask + row * (long long)words;
-    // eight independent loads in flight per lane: the row's words are read
-    // at the memory system's rate, not at one load latency per 256 bytes
-    for (int w0 = 0; w0 < words; w0 += 64 * 8) {
-      uint32_t x[8];
+  const long long groups = (rows + kRowsPerGroup - 1) / kRowsPerGroup;
+  for (long long grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+    const long long row = grp * kRowsPerGroup + wave;
+    int cnt = 0;
+    if (row < rows) {
+      const uint32_t* r = mask + row * (long long)words;
+      // eight independent loads in flight per lane: the row's words are read
+      // at the memory system's rate, not at one load latency per 256 bytes
+      for (int w0 = 0; w0 < words; w0 += 64 * 8) {
+        uint32_t x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int w = w0 + 64 * u + lane;
-        x[u] = w < words ? r[w] : 0u;
+        for (int u = 0; u < 8; ++u) {
+          const int w = w0 + 64 * u + lane;
+          x[u] = w < words ? r[w] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int w = w0 + 64 * u + lane;
+          const int valid = T_k - 32 * w;
+          if (valid < 32) x[u] &= valid > 0 ? (1u << valid) - 1u : 0u;
+          cnt += __builtin_popcount(x[u]);
+        }
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int w = w0 + 64 * u + lane;
-        const int valid = T_k - 32 * w;
-        if (valid < 32) x[u] &= valid > 0 ? (1u << valid) - 1u : 0u;
-        cnt += __builtin_popcount(x[u]);
-      }
+      for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
+      if (lane == 0) counts[row] = cnt;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
-    if (lane == 0) counts[row] = cnt;
-  }
-  if (lane == 0) part[wave] = row < rows ? cnt : 0;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    long long s = 0;
-    for (int i = 0; i < kRowsPerGroup; ++i) s += part[i];
-    group_sums[blockIdx.x] = s;
+    if (lane == 0) part[wave] = row < rows ? cnt : 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      long long s = 0;
+      for (int i = 0; i < kRowsPerGroup; ++i) s += part[i];
+      group_sums[grp] = s;
+    }
+    __syncthreads();  // part is rewritten for the next group
   }
 }
 
@@ -101,16 +107,12 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__global__ __launch_bounds__(64 * kFillWaves) void compact_fill_kernel(
-    const uint32_t* __restrict__ mask, long long rows, int words, int T_k,
-    const int32_t* __restrict__ counts, const long long* __restrict__ group_offsets,
-    const long long* __restrict__ total, long long* __restrict__ row_ptr,
-    int32_t* __restrict__ col_idx, long long col_capacity) {
-  // a block's kept tiles per wave (up to 64 * 32), after up to 3 alignment slots
-  __shared__ __attribute__((aligned(16))) int32_t stage[kFillWaves][64 * 32 + 4];
-  const int wave = wave_uniform(threadIdx.x >> 6);
-  const long long row = (long long)blockIdx.x * kFillWaves + wave;
-  if (row >= rows) return;
+// One row of the fill, by one wave; st: the wave's LDS staging area.
+__device__ __forceinline__ void fill_row(const uint32_t* __restrict__ mask, long long row, long long rows,
+                                         int words, int T_k, const int32_t* __restrict__ counts,
+                                         const long long* __restrict__ group_offsets,
+                                         const long long* __restrict__ total, long long* __restrict__ row_ptr,
+                                         int32_t* __restrict__ col_idx, long long col_capacity, int32_t* st) {
   // the row's count group's offset plus the counts of the group's earlier
   // rows (lane i holds the count of the group's row i; one vector load)
   const long long grp = row / kRowsPerGroup, first = grp * kRowsPerGroup;
@@ -126,7 +128,6 @@ __global__ __launch_bounds__(64 * kFillWaves) void compact_fill_kernel(
   if (start >= col_capacity) return;
   const uint32_t* r = mask + row * (long long)words;
   const int lane = lane_id();
-  int32_t* st = stage[wave];
   long long base = start;  // output slot of the block's first kept tile
   // The row's words come kSuperBlock 64-word blocks at a time, a word per
   // lane per block, loaded one super-block ahead.  A vector-memory wait
@@ -199,6 +200,23 @@ __global__ __launch_bounds__(64 * kFillWaves) void compact_fill_kernel(
   }
 }
 
+__global__ __launch_bounds__(64 * kFillWaves) void compact_fill_kernel(
+    const uint32_t* __restrict__ mask, long long rows, int words, int T_k,
+    const int32_t* __restrict__ counts, const long long* __restrict__ group_offsets,
+    const long long* __restrict__ total, long long* __restrict__ row_ptr,
+    int32_t* __restrict__ col_idx, long long col_capacity) {
+  // a block's kept tiles per wave (up to 64 * 32), after up to 3 alignment slots
+  __shared__ __attribute__((aligned(16))) int32_t stage[kFillWaves][64 * 32 + 4];
+  const int wave = wave_uniform(threadIdx.x >> 6);
+  const long long fill_groups = (rows + kFillWaves - 1) / kFillWaves;
+  for (long long fg = blockIdx.x; fg < fill_groups; fg += gridDim.x) {
+    const long long row = fg * kFillWaves + wave;
+    if (row < rows)
+      fill_row(mask, row, rows, words, T_k, counts, group_offsets, total, row_ptr, col_idx, col_capacity,
+               stage[wave]);
+  }
+}
+
 hipError_t launch_mask_compact(const tsa_problem_t* p, const uint32_t* mask, int64_t* row_ptr,
                                int32_t* col_idx, int64_t col_capacity, void* workspace,
                                hipStream_t stream) {
@@ -215,10 +233,10 @@ hipError_t launch_mask_compact(const tsa_problem_t* p, const uint32_t* mask, int
   long long* total = reinterpret_cast<long long*>(ws + off);
 
   const long long fill_groups = (rows + kFillWaves - 1) / kFillWaves;
-  hipLaunchKernelGGL(compact_count_kernel, dim3((unsigned)groups), dim3(64 * kRowsPerGroup), 0, stream, mask,
+  hipLaunchKernelGGL(compact_count_kernel, dim3(stride_blocks(groups, 1)), dim3(64 * kRowsPerGroup), 0, stream, mask,
                      rows, words, T_k, counts, gsum);
   hipLaunchKernelGGL(scan_groups_kernel, dim3(1), dim3(1024), 0, stream, gsum, groups, total);
-  hipLaunchKernelGGL(compact_fill_kernel, dim3((unsigned)fill_groups), dim3(64 * kFillWaves), 0, stream, mask, rows,
+  hipLaunchKernelGGL(compact_fill_kernel, dim3(stride_blocks(fill_groups, 1)), dim3(64 * kFillWaves), 0, stream, mask, rows,
                      words, T_k, counts, gsum, total, reinterpret_cast<long long*>(row_ptr), col_idx,
                      (long long)col_capacity);
   return hipGetLastError();

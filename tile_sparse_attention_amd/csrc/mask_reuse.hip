@@ -17,6 +17,7 @@
 #include <stdint.h>
 
 #include "tsa.h"
+#include "tsa_device.h"
 
 namespace tsa {
 
@@ -32,39 +33,42 @@ __global__ __launch_bounds__(256) void diff_rows_kernel(const uint32_t* __restri
                                                         int words, uint32_t last_mask,
                                                         int64_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
-  const long long r0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave;
-  int cnt[kRowsPerWave];
+  // work-groups of 4 waves x kRowsPerWave rows, stepping with the grid's stride
+  for (long long blk = blockIdx.x; blk * 4 * kRowsPerWave < rows; blk += gridDim.x) {
+    const long long r0 = (blk * 4 + (threadIdx.x >> 6)) * kRowsPerWave;
+    int cnt[kRowsPerWave];
 #pragma unroll
-  for (int k = 0; k < kRowsPerWave; ++k) {
-    cnt[k] = 0;
-    const long long r = r0 + k;
-    if (r >= rows) continue;
-    const uint32_t* ra = a + r * words;
-    const uint32_t* rb = b + r * words;
-    if constexpr (VEC) {
-      // words % 4 == 0: 16-byte aligned rows, four words per lane per step
-      for (int w = 4 * lane; w < words; w += 256) {
-        const uint4 x = *reinterpret_cast<const uint4*>(ra + w);
-        const uint4 y = *reinterpret_cast<const uint4*>(rb + w);
-        uint32_t z3 = x.w ^ y.w;
-        if (w + 4 == words) z3 &= last_mask;
-        cnt[k] += __builtin_popcount(x.x ^ y.x) + __builtin_popcount(x.y ^ y.y) +
-                  __builtin_popcount(x.z ^ y.z) + __builtin_popcount(z3);
-      }
-    } else {
-      for (int w = lane; w < words; w += 64) {
-        uint32_t x = ra[w] ^ rb[w];
-        if (w == words - 1) x &= last_mask;
-        cnt[k] += __builtin_popcount(x);
+    for (int k = 0; k < kRowsPerWave; ++k) {
+      cnt[k] = 0;
+      const long long r = r0 + k;
+      if (r >= rows) continue;
+      const uint32_t* ra = a + r * words;
+      const uint32_t* rb = b + r * words;
+      if constexpr (VEC) {
+        // words % 4 == 0: 16-byte aligned rows, four words per lane per step
+        for (int w = 4 * lane; w < words; w += 256) {
+          const uint4 x = *reinterpret_cast<const uint4*>(ra + w);
+          const uint4 y = *reinterpret_cast<const uint4*>(rb + w);
+          uint32_t z3 = x.w ^ y.w;
+          if (w + 4 == words) z3 &= last_mask;
+          cnt[k] += __builtin_popcount(x.x ^ y.x) + __builtin_popcount(x.y ^ y.y) +
+                    __builtin_popcount(x.z ^ y.z) + __builtin_popcount(z3);
+        }
+      } else {
+        for (int w = lane; w < words; w += 64) {
+          uint32_t x = ra[w] ^ rb[w];
+          if (w == words - 1) x &= last_mask;
+          cnt[k] += __builtin_popcount(x);
+        }
       }
     }
-  }
 #pragma unroll
-  for (int k = 0; k < kRowsPerWave; ++k) {
-    int c = cnt[k];
+    for (int k = 0; k < kRowsPerWave; ++k) {
+      int c = cnt[k];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
-    if (lane == 0 && r0 + k < rows) out[r0 + k] = c;
+      for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+      if (lane == 0 && r0 + k < rows) out[r0 + k] = c;
+    }
   }
 }
 
@@ -90,7 +94,7 @@ hipError_t launch_mask_diff(const tsa_problem_t* p, const uint32_t* a, const uin
   const int words = (T_k + 31) / 32;
   const long long rows = (long long)p->B * p->H * T_q;
   const uint32_t last_mask = (T_k & 31) ? ((1u << (T_k & 31)) - 1u) : 0xffffffffu;
-  const unsigned blocks = (unsigned)((rows + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave));
+  const unsigned blocks = stride_blocks(rows, 4 * kRowsPerWave);
   if (words % 4 == 0)
     hipLaunchKernelGGL(diff_rows_kernel<true>, dim3(blocks), dim3(256), 0, stream, a, b, rows, words, last_mask,
                        rows_out);

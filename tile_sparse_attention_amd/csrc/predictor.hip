@@ -30,25 +30,25 @@ template <typename E>
 __global__ __launch_bounds__(256) void pool_tiles_kernel(const E* __restrict__ x, bf16_t* __restrict__ out_hi,
                                                          bf16_t* __restrict__ out_lo, long long total, int L,
                                                          int d, int T, int tile) {
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= total) return;
-  const int dd = (int)(idx % d);
-  const long long bt = idx / d;
-  const int t = (int)(bt % T);
-  const long long bh = bt / T;
-  const int r0 = t * tile;
-  const int r1 = r0 + tile < L ? r0 + tile : L;
-  const E* src = x + ((size_t)bh * L + r0) * d + dd;
-  float s = 0.f;
+  for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long long)gridDim.x * 256) {
+    const int dd = (int)(idx % d);
+    const long long bt = idx / d;
+    const int t = (int)(bt % T);
+    const long long bh = bt / T;
+    const int r0 = t * tile;
+    const int r1 = r0 + tile < L ? r0 + tile : L;
+    const E* src = x + ((size_t)bh * L + r0) * d + dd;
+    float s = 0.f;
 #pragma unroll 8
-  for (int r = r0; r < r1; ++r, src += d) {
-    if constexpr (sizeof(E) == 2) s += bf16_to_f32(*reinterpret_cast<const bf16_t*>(src));
-    else s += *src;
+    for (int r = r0; r < r1; ++r, src += d) {
+      if constexpr (sizeof(E) == 2) s += bf16_to_f32(*reinterpret_cast<const bf16_t*>(src));
+      else s += *src;
+    }
+    const float mean = s / (float)(r1 - r0);
+    const __bf16 hi = (__bf16)mean;
+    out_hi[idx] = __builtin_bit_cast(bf16_t, hi);
+    out_lo[idx] = __builtin_bit_cast(bf16_t, (__bf16)(mean - (float)hi));
   }
-  const float mean = s / (float)(r1 - r0);
-  const __bf16 hi = (__bf16)mean;
-  out_hi[idx] = __builtin_bit_cast(bf16_t, hi);
-  out_lo[idx] = __builtin_bit_cast(bf16_t, (__bf16)(mean - (float)hi));
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
@@ -386,14 +386,14 @@ hipError_t launch_predict_mask(const tsa_problem_t* p, const void* q, const void
   const long long nq = (long long)BH * pl.T_q * p->d;
   const long long nk = (long long)BH * pl.T_k * p->d;
   if (p->dtype == TSA_DTYPE_BF16) {
-    hipLaunchKernelGGL(pool_tiles_kernel<bf16_t>, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(pool_tiles_kernel<bf16_t>, dim3(stride_blocks(nq, 256)), dim3(256), 0, stream,
                        static_cast<const bf16_t*>(q), qhi, qlo, nq, p->L, p->d, pl.T_q, p->M);
-    hipLaunchKernelGGL(pool_tiles_kernel<bf16_t>, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(pool_tiles_kernel<bf16_t>, dim3(stride_blocks(nk, 256)), dim3(256), 0, stream,
                        static_cast<const bf16_t*>(k), khi, klo, nk, p->L, p->d, pl.T_k, p->N);
   } else {
-    hipLaunchKernelGGL(pool_tiles_kernel<float>, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(pool_tiles_kernel<float>, dim3(stride_blocks(nq, 256)), dim3(256), 0, stream,
                        static_cast<const float*>(q), qhi, qlo, nq, p->L, p->d, pl.T_q, p->M);
-    hipLaunchKernelGGL(pool_tiles_kernel<float>, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(pool_tiles_kernel<float>, dim3(stride_blocks(nk, 256)), dim3(256), 0, stream,
                        static_cast<const float*>(k), khi, klo, nk, p->L, p->d, pl.T_k, p->N);
   }
   hipError_t err = hipGetLastError();

@@ -30,13 +30,10 @@ __device__ __forceinline__ uint32_t to_e4m3x4(float a, float b, float c, float d
   return (uint32_t)w;
 }
 
-// One wave per 16-row Q tile: lane l takes row l/4, d = 32(l%4) .. +31.
-__global__ __launch_bounds__(256) void quantize_q_kernel(const bf16_t* __restrict__ q, int L, int t16,
-                                                         long long tiles, uint8_t* __restrict__ q8,
-                                                         float* __restrict__ q_scale) {
+// One wave per 16-row Q tile t: lane l takes row l/4, d = 32(l%4) .. +31.
+__device__ __forceinline__ void quantize_q_tile(const bf16_t* __restrict__ q, int L, int t16, long long t,
+                                                uint8_t* __restrict__ q8, float* __restrict__ q_scale) {
   const int lane = threadIdx.x & 63;
-  const long long t = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= tiles) return;
   const long long bh = t / t16;
   const int r = (int)(t - bh * t16) * 16 + (lane >> 2);
   const bool ok = r < L;
@@ -66,30 +63,43 @@ __global__ __launch_bounds__(256) void quantize_q_kernel(const bf16_t* __restric
   *reinterpret_cast<u32x4*>(q8 + off + 16) = y[1];
 }
 
-// Largest |k| of one slice of a (b, h): work-group (slice, b*H + h) of a
-// grid of S slices per head writes the maximum of its slice to
-// partial[(b*H + h) * S + slice].
+// Four tiles per work-group, stepping through the tiles with the grid's stride.
+__global__ __launch_bounds__(256) void quantize_q_kernel(const bf16_t* __restrict__ q, int L, int t16,
+                                                         long long tiles, uint8_t* __restrict__ q8,
+                                                         float* __restrict__ q_scale) {
+  for (long long tb = blockIdx.x; 4 * tb < tiles; tb += gridDim.x) {
+    const long long t = 4 * tb + (threadIdx.x >> 6);
+    if (t < tiles) quantize_q_tile(q, L, t16, t, q8, q_scale);
+  }
+}
+
+// Largest |k| of each slice of a (b, h): unit u = (b*H + h) * S + slice
+// writes the maximum of its slice to partial[u]; work-groups step through
+// the units with the grid's stride.
 constexpr int kKSlices = 64;  // slices per head (fewer for L < 2)
 
-__global__ __launch_bounds__(256) void k_amax_kernel(const bf16_t* __restrict__ k, int L,
+__global__ __launch_bounds__(256) void k_amax_kernel(const bf16_t* __restrict__ k, int L, int S, long long units,
                                                      float* __restrict__ partial) {
   __shared__ float part[4];
-  const int slice = blockIdx.x, bh = blockIdx.y, S = gridDim.x;
-  const size_t n8 = (size_t)L * kD / 8;
-  const size_t lo = n8 * slice / S, hi = n8 * (slice + 1) / S;
-  const u32x4* kh = reinterpret_cast<const u32x4*>(k + (size_t)bh * L * kD);
-  float m = 0.f;
-  for (size_t i = lo + threadIdx.x; i < hi; i += 256) {
-    const u32x4 x = kh[i];
+  for (long long u = blockIdx.x; u < units; u += gridDim.x) {
+    const long long bh = u / S;
+    const int slice = (int)(u - bh * S);
+    const size_t n8 = (size_t)L * kD / 8;
+    const size_t lo = n8 * slice / S, hi = n8 * (slice + 1) / S;
+    const u32x4* kh = reinterpret_cast<const u32x4*>(k + (size_t)bh * L * kD);
+    float m = 0.f;
+    for (size_t i = lo + threadIdx.x; i < hi; i += 256) {
+      const u32x4 x = kh[i];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(bf16_lo(x[e])), fabsf(bf16_hi(x[e]))));
+      for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(bf16_lo(x[e])), fabsf(bf16_hi(x[e]))));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) partial[u] = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    __syncthreads();  // part is rewritten for the next unit
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0)
-    partial[(size_t)bh * S + slice] = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
 }
 
 // k_scale[b*H + h] from the head's partial maxima.
@@ -106,14 +116,14 @@ __global__ __launch_bounds__(256) void k_scale_kernel(const float* __restrict__ 
 __global__ __launch_bounds__(256) void quantize_k_kernel(const bf16_t* __restrict__ k, long long per_head8,
                                                          long long total8, const float* __restrict__ k_scale,
                                                          uint8_t* __restrict__ k8) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total8) return;
-  const float s = k_scale[i / per_head8];
-  const u32x4 x = reinterpret_cast<const u32x4*>(k)[i];
-  u32x2 y;
-  y[0] = to_e4m3x4(bf16_lo(x[0]), bf16_hi(x[0]), bf16_lo(x[1]), bf16_hi(x[1]), s);
-  y[1] = to_e4m3x4(bf16_lo(x[2]), bf16_hi(x[2]), bf16_lo(x[3]), bf16_hi(x[3]), s);
-  reinterpret_cast<u32x2*>(k8)[i] = y;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total8; i += (long long)gridDim.x * 256) {
+    const float s = k_scale[i / per_head8];
+    const u32x4 x = reinterpret_cast<const u32x4*>(k)[i];
+    u32x2 y;
+    y[0] = to_e4m3x4(bf16_lo(x[0]), bf16_hi(x[0]), bf16_lo(x[1]), bf16_hi(x[1]), s);
+    y[1] = to_e4m3x4(bf16_lo(x[2]), bf16_hi(x[2]), bf16_lo(x[3]), bf16_hi(x[3]), s);
+    reinterpret_cast<u32x2*>(k8)[i] = y;
+  }
 }
 
 }  // namespace
@@ -123,7 +133,7 @@ hipError_t launch_quantize_qk_fp8(const tsa_problem_t* p, const void* q, const v
   const long long bh = (long long)p->B * p->H;
   const int t16 = (p->L + 15) / 16;
   const long long tiles = bh * t16;
-  hipLaunchKernelGGL(quantize_q_kernel, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(quantize_q_kernel, dim3(stride_blocks(tiles, 4)), dim3(256), 0, stream,
                      static_cast<const bf16_t*>(q), p->L, t16, tiles, q8, q_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -132,15 +142,15 @@ hipError_t launch_quantize_qk_fp8(const tsa_problem_t* p, const void* q, const v
   // only after k_scale_kernel has read them.
   const int S = p->L >= 2 ? kKSlices : 32;
   float* partial = reinterpret_cast<float*>(k8);
-  hipLaunchKernelGGL(k_amax_kernel, dim3((unsigned)S, (unsigned)bh), dim3(256), 0, stream,
-                     static_cast<const bf16_t*>(k), p->L, partial);
+  hipLaunchKernelGGL(k_amax_kernel, dim3(stride_blocks(S * bh, 1)), dim3(256), 0, stream,
+                     static_cast<const bf16_t*>(k), p->L, S, S * bh, partial);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_scale_kernel, dim3((unsigned)((bh + 255) / 256)), dim3(256), 0, stream, partial, S, bh,
                      k_scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long per_head8 = (long long)p->L * kD / 8;
   const long long total8 = bh * per_head8;
-  hipLaunchKernelGGL(quantize_k_kernel, dim3((unsigned)((total8 + 255) / 256)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(quantize_k_kernel, dim3(stride_blocks(total8, 256)), dim3(256), 0, stream,
                      static_cast<const bf16_t*>(k), per_head8, total8, k_scale, k8);
   return hipGetLastError();
 }

@@ -26,6 +26,16 @@ typedef uint16_t bf16_t;  // storage type of bf16 elements in memory
 // Fourth word of a raw (unformatted, unswizzled) buffer resource on gfx9.
 constexpr int kBufferFlags = 0x00020000;
 
+// One-dimensional launches over many items: a dispatch holds fewer than 2^32
+// work-items in each grid dimension, so such kernels take at most
+// kMaxStrideBlocks work-groups and step through their items with a stride
+// of gridDim.x work-groups.
+constexpr long long kMaxStrideBlocks = 1ll << 20;
+inline unsigned stride_blocks(long long items, long long per_block) {
+  const long long b = (items + per_block - 1) / per_block;
+  return (unsigned)(b < 1 ? 1 : b < kMaxStrideBlocks ? b : kMaxStrideBlocks);
+}
+
 __device__ __forceinline__ int lane_id() {
   return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 }
