@@ -7,8 +7,9 @@ the sampled query tiles' rows come from the host generator (checked equal to
 the GPU's first) and the oracle evaluates those tiles one at a time.  At
 B*H = 2^20 every head takes its Q, K, V from one of 4096 seeded heads (head h
 of batch b uses head h mod 4096 of a [1, 4096, L, d] draw), while its mask
-rows are its own; sampled heads are compared in full, and the FP8
-quantisation of every sampled head is compared byte for byte.
+rows are its own; sampled heads are compared in full (forward, and dQ, dK,
+dV of the backward), and the FP8 quantisation of sampled heads byte for
+byte.
 """
 import numpy as np
 import pytest
@@ -119,3 +120,43 @@ def test_fp8_quantisation_at_maximum_heads():
         got_q = q8[b, h].cpu().view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
         got_k = k8[b, h].cpu().view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
         assert np.array_equal(got_q, rq[0, 0]) and np.array_equal(got_k, rk[0, 0])
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("N", [8, 1])
+def test_backward_at_maximum_heads(N):
+    """The backward over B*H = 2^20 heads (L = 40, d = 64, 16xN): eight
+    sampled heads' dQ, dK, dV against the oracle, within the backward's
+    tolerance (max-abs 2% of max(1, max|ref|), mean-abs 1% of mean|ref| +
+    1e-5)."""
+    torch = torch_or_skip()
+    import tile_sparse_attention_amd as T
+    B, H, L, d, M = 16, BH_MAX // 16, 40, 64, 16
+    src = W.Workload("maxheads_bwd", 1, 4096, L, d, M, N, "bf16", W.MaskRecipe("hash", p_near=0.3, p_far=0.3), 91)
+    w = W.Workload("maxheads_bwd", B, H, L, d, M, N, "bf16",
+                   W.MaskRecipe("hash", p_near=0.3, p_far=0.3, force_diag=True), 92 + N)
+    say(f"limits B*H={B * H} L={L} d={d} {M}x{N}: backward inputs")
+    (qd, kd, vd), (q, k, v) = _max_heads_inputs(src, B, H)
+    do_src = W.make_do(src)
+    dod = do_src.cuda().reshape(src.H, L, d).repeat(B * H // src.H, 1, 1).reshape(B, H, L, d)
+    mask = T.maskgen_hash(B, H, L, M, N, **W.hash_params(w))
+    say(f"limits B*H={B * H} {M}x{N}: forward and backward on GPU")
+    o, lse = T.attention_fwd(qd, kd, vd, mask, M, N, w.scale, return_lse=True)
+    dq, dk, dv = T.attention_bwd(qd, kd, vd, o, dod, lse, mask, M, N, w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(60 + N)
+    heads = [(0, 0), (B - 1, H - 1), (5, 4096), (9, 12345)] + \
+            [(int(b), int(h)) for b, h in zip(rng.integers(0, B, 4), rng.integers(0, H, 4))]
+    for b, h in heads:
+        bits = W.pack_bits(W.mask_rows_bool(w, [(b, h, i) for i in range(w.T_q)]))
+        assert np.array_equal(mask[b, h].cpu().numpy().view(np.uint32), bits)
+        s = h % src.H
+        sl = slice(s, s + 1)
+        ref = oracle.attention_bwd(q[:, sl], k[:, sl], v[:, sl], do_src[:, sl], bits[None, None], M, N, w.scale)
+        for name, got, r in (("dQ", dq, ref[0]), ("dK", dk, ref[1]), ("dV", dv, ref[2])):
+            g = got[b, h].float().cpu().numpy()
+            err = np.abs(g - r[0, 0])
+            assert np.all(np.isfinite(g))
+            assert err.max() <= 2e-2 * max(1.0, float(np.abs(r).max())), (b, h, name, float(err.max()))
+            assert err.mean() <= 1e-2 * float(np.abs(r).mean()) + 1e-5, (b, h, name, float(err.mean()))
+    print(f"[parity] limits B*H={B * H} {M}x{N} backward: {len(heads)} heads within tolerance", flush=True)
