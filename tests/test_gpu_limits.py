@@ -160,3 +160,34 @@ def test_backward_at_maximum_heads(N):
             assert err.max() <= 2e-2 * max(1.0, float(np.abs(r).max())), (b, h, name, float(err.max()))
             assert err.mean() <= 1e-2 * float(np.abs(r).mean()) + 1e-5, (b, h, name, float(err.mean()))
     print(f"[parity] limits B*H={B * H} {M}x{N} backward: {len(heads)} heads within tolerance", flush=True)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("dtype,d,M,N,p", [("f32", 128, 16, 16, 0.02), ("bf16", 128, 16, 1, 0.002)])
+def test_maximum_sequence_length_other_kernels(dtype, d, M, N, p):
+    """L = 2^22 through the fp32 kernel (16x16; its V^T spans more than 2^31
+    bytes per head) and the bf16 key kernel (16x1; a 2^35-word, 137 GB
+    bitmap): one head, i.i.d. keep with the diagonal kept, 16 sampled query
+    tiles."""
+    torch = torch_or_skip()
+    import tile_sparse_attention_amd as T
+    w = W.Workload(f"maxlen_{dtype}_{N}", 1, 1, L_MAX, d, M, N, dtype,
+                   W.MaskRecipe("hash", p_near=p, p_far=p, force_diag=True), 4400 + N)
+    say(f"limits L={w.L} {dtype} {M}x{N}: generating inputs")
+    q, k, v = W.make_qkv(w)
+    mask = T.maskgen_hash(w.B, w.H, w.L, w.M, w.N, **W.hash_params(w))
+    say(f"limits L={w.L} {dtype} {M}x{N}: attention on GPU (bitmap {mask.numel() * 4 / 2**30:.1f} GiB)")
+    o, lse = T.attention_fwd(q.cuda(), k.cuda(), v.cuda(), mask, w.M, w.N, w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(19 + N)
+    tiles = np.unique(np.concatenate([[0, w.T_q - 1], rng.choice(w.T_q, 14, replace=False)]))
+    bits = np.zeros((w.T_q, w.words), dtype=np.uint32)
+    bits[tiles] = W.pack_bits(W.mask_rows_bool(w, [(0, 0, int(i)) for i in tiles]))
+    dev_rows = mask[0, 0, torch.from_numpy(tiles).cuda()].cpu().numpy().view(np.uint32)
+    assert np.array_equal(dev_rows, bits[tiles])
+    del mask
+    say(f"limits L={w.L} {dtype} {M}x{N}: oracle on {len(tiles)} tiles")
+    rows, ro, rl = oracle.attention_rows(q[0, 0], k[0, 0], v[0, 0], bits, w.M, w.N, w.scale, tiles, group=1)
+    idx = torch.from_numpy(rows).cuda()
+    compare(f"limits L={w.L} {dtype} {M}x{N}", o[0, 0, idx].float().cpu().numpy(), ro, w.dtype,
+            lse[0, 0, idx].cpu().numpy(), rl)

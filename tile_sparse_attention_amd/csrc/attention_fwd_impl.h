@@ -181,7 +181,9 @@ struct AttnKernel {
   // Byte offset (relative to the chunk's resource base) that lane `ln` of
   // tile load `I` reads, or an out-of-range offset for padding slots.
   __device__ __forceinline__ uint32_t dma_offset(int I, int ln) const {
-    constexpr uint32_t OOB = 0x80000000u;
+    // past every resource's range: an fp32 V^T resource spans up to
+    // 129 x 2^22 x 4 bytes, more than 2^31
+    constexpr uint32_t OOB = 0xfffffff0u;
     if (I < C::NI_K) {
       const int pos = I * 1024 + 16 * ln;
       const int row = pos / C::KRS, cb = pos - row * C::KRS;
@@ -189,7 +191,9 @@ struct AttnKernel {
     }
     const int pos = (I - C::NI_K) * 1024 + 16 * ln;
     const int row = pos / C::VRS, cb = pos - row * C::VRS;
-    return row < C::VROWS && cb < C::VRB ? (uint32_t)(row * p.L_pad * (int)sizeof(T) + cb) : OOB;
+    return row < C::VROWS && cb < C::VRB
+               ? (uint32_t)row * (uint32_t)p.L_pad * (uint32_t)sizeof(T) + (uint32_t)cb
+               : OOB;
   }
 
   // Issue the direct global->LDS loads of chunk c into buffer `buf` (this
@@ -202,7 +206,8 @@ struct AttnKernel {
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kg + (size_t)kbase * D), (short)0, rows * C::KRB, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vtg + kbase), (short)0, (C::VROWS * p.L_pad - kbase) * (int)sizeof(T), kBufferFlags);
+        (void*)(vtg + kbase), (short)0, (int)((uint32_t)(C::VROWS * p.L_pad - kbase) * (uint32_t)sizeof(T)),
+        kBufferFlags);
     // The per-lane offsets are loop-invariant; recomputing them (a few VALU
     // per load) keeps them out of the register budget instead of holding or
     // spilling them across the chunk loop.
