@@ -191,3 +191,54 @@ def test_maximum_sequence_length_other_kernels(dtype, d, M, N, p):
     idx = torch.from_numpy(rows).cuda()
     compare(f"limits L={w.L} {dtype} {M}x{N}", o[0, 0, idx].float().cpu().numpy(), ro, w.dtype,
             lse[0, 0, idx].cpu().numpy(), rl)
+
+
+@pytest.mark.timeout(900)
+def test_backward_at_maximum_sequence_length():
+    """The backward at L = 2^22 (one head, 16x8, 2% i.i.d. keep with the
+    diagonal kept).  dQ of 16 sampled query tiles against the oracle (each dQ
+    row needs only its own row of P); dK and dV need every query row, so they
+    are checked by identities that hold at any size when every row keeps a
+    key: sum_k dV[k] = sum_q dO[q] (the probabilities of a row sum to 1) and
+    sum_k dK[k] = 0 (sum_k dS[q, k] = D_q - D_q sum_k P[q, k] = 0).  Bound for
+    both: 1e-3 x sqrt(sum_q dO[q]^2) per d, against an expected rounding
+    residue of about 0.03 from the bf16 probabilities and outputs; a dropped
+    1% of rows would leave about 200."""
+    torch = torch_or_skip()
+    import tile_sparse_attention_amd as T
+    from oracle import backward as obwd
+    w = W.Workload("maxlen_bwd", 1, 1, L_MAX, 128, 16, 8, "bf16",
+                   W.MaskRecipe("hash", p_near=0.02, p_far=0.02, force_diag=True), 4500)
+    say(f"limits L={w.L} 16x8 backward: generating inputs")
+    q, k, v = W.make_qkv(w)
+    do = W.make_do(w)
+    mask = T.maskgen_hash(w.B, w.H, w.L, w.M, w.N, **W.hash_params(w))
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    say(f"limits L={w.L} 16x8 backward: forward and backward on GPU")
+    o, lse = T.attention_fwd(qd, kd, vd, mask, w.M, w.N, w.scale, return_lse=True)
+    dq, dk, dv = T.attention_bwd(qd, kd, vd, o, dod, lse, mask, w.M, w.N, w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(23)
+    tiles = np.unique(np.concatenate([[0, w.T_q - 1], rng.choice(w.T_q, 14, replace=False)]))
+    bits = np.zeros((w.T_q, w.words), dtype=np.uint32)
+    bits[tiles] = W.pack_bits(W.mask_rows_bool(w, [(0, 0, int(i)) for i in tiles]))
+    dev_rows = mask[0, 0, torch.from_numpy(tiles).cuda()].cpu().numpy().view(np.uint32)
+    assert np.array_equal(dev_rows, bits[tiles])
+    del mask, o, lse, qd, kd, vd, dod
+    say(f"limits L={w.L} 16x8 backward: oracle dQ on {len(tiles)} tiles")
+    qr, rdq, _, _, _ = obwd.attention_bwd_rows(q[0, 0], k[0, 0], v[0, 0], do[0, 0], bits, w.M, w.N, w.scale,
+                                               q_tiles=tiles, k_rows=None, group=16)
+    g = dq[0, 0, torch.from_numpy(qr).cuda()].float().cpu().numpy()
+    err = np.abs(g - rdq)
+    print(f"[parity] limits L={w.L} bwd dQ: max_abs={err.max():.3e} mean_abs={err.mean():.3e}", flush=True)
+    assert np.all(np.isfinite(g))
+    assert err.max() <= 2e-2 * max(1.0, float(np.abs(rdq).max()))
+    assert err.mean() <= 1e-2 * float(np.abs(rdq).mean()) + 1e-5
+    dof = do[0, 0].double().numpy()
+    bound = 1e-3 * np.sqrt((dof ** 2).sum(axis=0))
+    sdv = dv[0, 0].double().sum(dim=0).cpu().numpy()
+    sdk = dk[0, 0].double().sum(dim=0).cpu().numpy()
+    rv = np.abs(sdv - dof.sum(axis=0))
+    print(f"[parity] limits L={w.L} bwd: |sum dV - sum dO| max {rv.max():.3e}, |sum dK| max "
+          f"{np.abs(sdk).max():.3e} (bound {bound.min():.3e})", flush=True)
+    assert np.all(rv <= bound) and np.all(np.abs(sdk) <= bound)
