@@ -218,7 +218,11 @@ struct KeyKernel {
     }
     // V operands: lane (g, n) points at d = 4(n&3)..4(n&3)+3 of its V-side
     // key; the transposing read returns d = n of the group's four keys.
-    constexpr int EARLY = C::NDB / 2 - 2;
+    // EARLY of them are issued before the softmax: none, since every read
+    // held across the softmax costs registers the next pass's K reads need
+    // (at 16 x 1 and 80% sparsity, two early reads of the 8 d blocks ran
+    // 1.6% slower, one 0.6% slower).
+    constexpr int EARLY = 0;
     const lds_cptr vb = to_lds(bufr<B>().v) + 8 * (n & 3);
     const lds_cptr va0 = vb + kv0 * C::RS;
     const lds_cptr va1 = vb + kv1 * C::RS;
