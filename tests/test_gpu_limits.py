@@ -18,6 +18,7 @@ import oracle
 import workloads as W
 from gpu_util import compare, say, torch_or_skip
 from oracle import fp8
+from oracle.sparse_attention import tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -101,18 +102,23 @@ def test_maximum_heads(M, N):
 
 
 @pytest.mark.timeout(600)
-def test_fp8_quantisation_at_maximum_heads():
+def test_fp8_at_maximum_heads():
     """The e4m3 quantisation of Q and K over B*H = 2^20 heads (L = 40, d = 128;
     the per-head K maxima run over a one-dimensional grid of 64 slices per
-    head): sampled heads byte for byte against the oracle."""
+    head): sampled heads byte for byte against the oracle; then the FP8-score
+    attention over all heads (16x8), sampled heads against the oracle on the
+    dequantised Q and K."""
     torch = torch_or_skip()
     import tile_sparse_attention_amd as T
     B, H, L = 16, BH_MAX // 16, 40
     src = W.Workload("maxheads_f8", 1, 4096, L, 128, 16, 8, "bf16", W.MaskRecipe("hash", p_near=0.3, p_far=0.3), 99)
+    w = W.Workload("maxheads_f8", B, H, L, 128, 16, 8, "bf16",
+                   W.MaskRecipe("hash", p_near=0.3, p_far=0.3, force_diag=True), 100)
     say(f"limits B*H={B * H} L={L}: fp8 quantisation")
-    (qd, kd, _), (q, k, _) = _max_heads_inputs(src, B, H)
+    (qd, kd, vd), (q, k, v) = _max_heads_inputs(src, B, H)
     q8, qs, k8, ks = T.quantize_qk_fp8(qd, kd)
     torch.cuda.synchronize()
+    del qd, kd
     for b, h in [(0, 0), (B - 1, H - 1), (3, 4097), (11, 60000)]:
         s = h % src.H
         rq, rqs, rk, rks = fp8.quantize_qk(q[:, s:s + 1], k[:, s:s + 1])
@@ -120,6 +126,61 @@ def test_fp8_quantisation_at_maximum_heads():
         got_q = q8[b, h].cpu().view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
         got_k = k8[b, h].cpu().view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
         assert np.array_equal(got_q, rq[0, 0]) and np.array_equal(got_k, rk[0, 0])
+    say(f"limits B*H={B * H} L={L}: fp8 attention")
+    mask = T.maskgen_hash(B, H, L, w.M, w.N, **W.hash_params(w))
+    o = T.attention_fwd_fp8(q8, k8, qs, ks, vd, mask, w.M, w.N, w.scale)
+    torch.cuda.synchronize()
+    got, ref = [], []
+    for b, h in [(0, 0), (B - 1, H - 1), (3, 4097), (11, 60000)]:
+        s = h % src.H
+        bits = W.pack_bits(W.mask_rows_bool(w, [(b, h, i) for i in range(w.T_q)]))
+        assert np.array_equal(mask[b, h].cpu().numpy().view(np.uint32), bits)
+        rq, rqs, rk, rks = fp8.quantize_qk(q[:, s:s + 1], k[:, s:s + 1])
+        ro, _ = oracle.attention(fp8.dequantize(rq, rqs, 16), fp8.dequantize(rk, rks[..., None], L),
+                                 v[:, s:s + 1], bits[None, None], w.M, w.N, w.scale)
+        got.append(o[b, h].float().cpu().numpy())
+        ref.append(ro[0, 0])
+    compare(f"limits B*H={B * H} fp8 16x8", np.concatenate(got), np.concatenate(ref), "bf16")
+
+
+@pytest.mark.timeout(900)
+def test_fp8_attention_at_maximum_sequence_length():
+    """FP8-score attention at L = 2^22 (one head, 16x8, 2% i.i.d. keep with
+    the diagonal kept): 16 sampled query tiles against the oracle on the
+    dequantised Q and K (the oracle's own e4m3 rounding, bit-exact with the
+    GPU's by the quantisation tests)."""
+    torch = torch_or_skip()
+    import tile_sparse_attention_amd as T
+    w = W.Workload("maxlen_f8", 1, 1, L_MAX, 128, 16, 8, "bf16",
+                   W.MaskRecipe("hash", p_near=0.02, p_far=0.02, force_diag=True), 4600)
+    say(f"limits L={w.L} fp8 16x8: generating inputs")
+    q, k, v = W.make_qkv(w)
+    mask = T.maskgen_hash(w.B, w.H, w.L, w.M, w.N, **W.hash_params(w))
+    q8, qs, k8, ks = T.quantize_qk_fp8(q.cuda(), k.cuda())
+    say(f"limits L={w.L} fp8 16x8: attention on GPU")
+    o = T.attention_fwd_fp8(q8, k8, qs, ks, v.cuda(), mask, w.M, w.N, w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(29)
+    tiles = np.unique(np.concatenate([[0, w.T_q - 1], rng.choice(w.T_q, 14, replace=False)]))
+    bits = np.zeros((w.T_q, w.words), dtype=np.uint32)
+    bits[tiles] = W.pack_bits(W.mask_rows_bool(w, [(0, 0, int(i)) for i in tiles]))
+    dev_rows = mask[0, 0, torch.from_numpy(tiles).cuda()].cpu().numpy().view(np.uint32)
+    assert np.array_equal(dev_rows, bits[tiles])
+    del mask, q8, k8
+    say(f"limits L={w.L} fp8 16x8: oracle on {len(tiles)} tiles")
+    # Q scales are per 16-row tile, so the sampled tiles' rows quantise on
+    # their own; K has one scale per head
+    rows = tile_rows(w.L, w.M, tiles)
+    qv, qsc = fp8.quantize(q[0, 0].float().numpy()[rows], 16)
+    kv, ksc = fp8.quantize(k[0, 0].float().numpy(), w.L)
+    assert np.array_equal(qs[0, 0, torch.from_numpy(tiles).cuda()].cpu().numpy(), qsc)
+    assert np.array_equal(ks[0, 0].cpu().numpy().reshape(1), ksc)
+    qdq = np.zeros((w.L, w.d))          # only the sampled rows are read
+    qdq[rows] = fp8.dequantize(qv, qsc, 16)
+    kdq = fp8.dequantize(kv, ksc, w.L)
+    del kv
+    rows, ro, _ = oracle.attention_rows(qdq, kdq, v[0, 0], bits, w.M, w.N, w.scale, tiles, group=1)
+    compare(f"limits L={w.L} fp8 16x8", o[0, 0, torch.from_numpy(rows).cuda()].float().cpu().numpy(), ro, "bf16")
 
 
 @pytest.mark.timeout(600)
