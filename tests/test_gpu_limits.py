@@ -303,3 +303,46 @@ def test_backward_at_maximum_sequence_length():
     print(f"[parity] limits L={w.L} bwd: |sum dV - sum dO| max {rv.max():.3e}, |sum dK| max "
           f"{np.abs(sdk).max():.3e} (bound {bound.min():.3e})", flush=True)
     assert np.all(rv <= bound) and np.all(np.abs(sdk) <= bound)
+
+
+@pytest.mark.timeout(600)
+def test_mask_calls_at_maximum_heads():
+    """Compaction and mask diff over B*H = 2^20 heads at L = 272 (17 query
+    tiles of 34 key tiles, 16x8): 17.8 million bitmap rows, so the count,
+    fill and diff kernels all step through more work than their capped grids
+    hold.  Sampled rows bit for bit against the host generator's rows: each
+    row's list between its row_ptr entries, its diff count, and whole heads'
+    diff sums; row_ptr starts at 0, never decreases and ends at the list
+    length."""
+    torch = torch_or_skip()
+    import tile_sparse_attention_amd as T
+    B, H, L, M, N = 16, BH_MAX // 16, 272, 16, 8
+    wa = W.Workload("maxheads_ma", B, H, L, 64, M, N, "bf16", W.MaskRecipe("hash", p_near=0.3, p_far=0.3), 201)
+    wb = W.Workload("maxheads_mb", B, H, L, 64, M, N, "bf16", W.MaskRecipe("hash", p_near=0.3, p_far=0.3), 202)
+    say(f"limits B*H={B * H} L={L}: masks, compaction, diff")
+    a = T.maskgen_hash(B, H, L, M, N, **W.hash_params(wa))
+    b = T.maskgen_hash(B, H, L, M, N, **W.hash_params(wb))
+    row_ptr, col_idx = T.mask_compact(a, L, M, N)
+    rows_changed, heads_changed = T.mask_diff(a, b, L, M, N)
+    torch.cuda.synchronize()
+    n_rows = B * H * wa.T_q
+    assert int(row_ptr[0]) == 0 and int(row_ptr[-1]) == col_idx.numel()
+    assert bool((row_ptr[1:] >= row_ptr[:-1]).all())
+    rng = np.random.default_rng(31)
+    heads = [(0, 0), (B - 1, H - 1), (7, 4096)] + [(int(x), int(y)) for x, y in
+                                                   zip(rng.integers(0, B, 5), rng.integers(0, H, 5))]
+    rc = rows_changed.cpu().numpy()
+    hc = heads_changed.cpu().numpy()
+    for bb, hh in heads:
+        keys = [(bb, hh, i) for i in range(wa.T_q)]
+        ka, kb = W.mask_rows_bool(wa, keys), W.mask_rows_bool(wb, keys)
+        assert np.array_equal(a[bb, hh].cpu().numpy().view(np.uint32), W.pack_bits(ka))
+        assert np.array_equal(b[bb, hh].cpu().numpy().view(np.uint32), W.pack_bits(kb))
+        diff = (ka != kb).sum(axis=1)
+        assert np.array_equal(rc[bb, hh], diff) and hc[bb, hh] == diff.sum()
+        for i in range(wa.T_q):
+            r = (bb * H + hh) * wa.T_q + i
+            lo, hi = int(row_ptr[r]), int(row_ptr[r + 1])
+            assert np.array_equal(col_idx[lo:hi].cpu().numpy(), np.flatnonzero(ka[i]))
+    print(f"[parity] limits B*H={B * H} L={L}: {n_rows} rows, {col_idx.numel()} kept tiles; "
+          f"{len(heads)} heads' lists and diff counts exact", flush=True)
