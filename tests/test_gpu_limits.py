@@ -346,3 +346,34 @@ def test_mask_calls_at_maximum_heads():
             assert np.array_equal(col_idx[lo:hi].cpu().numpy(), np.flatnonzero(ka[i]))
     print(f"[parity] limits B*H={B * H} L={L}: {n_rows} rows, {col_idx.numel()} kept tiles; "
           f"{len(heads)} heads' lists and diff counts exact", flush=True)
+
+
+@pytest.mark.timeout(600)
+def test_predictor_at_maximum_heads():
+    """The mask predictor over B*H = 2^20 heads (L = 48, d = 64, 16x16 tiles:
+    3 x 3 pooled scores per head, the top one of three kept at 50%): heads go
+    through the score and select kernels 65535 at a time.  Sampled heads
+    against the oracle predictor: exactly k kept per row, and every tile
+    clearly above (below) the oracle's k-th score kept (dropped)."""
+    torch = torch_or_skip()
+    import tile_sparse_attention_amd as T
+    from oracle import predictor as opred
+    B, H, L, d, M, N, sp = 16, BH_MAX // 16, 48, 64, 16, 16, 50
+    src = W.Workload("maxheads_pred", 1, 4096, L, d, M, N, "bf16",
+                     W.MaskRecipe("predicted", sparsity_percent=sp), 301)
+    say(f"limits B*H={B * H} L={L}: predictor")
+    (qd, kd, _), (q, k, _) = _max_heads_inputs(src, B, H)
+    bits = T.predict_mask(qd, kd, M, N, sp)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(37)
+    heads = [(0, 0), (B - 1, H - 1), (0, 65534), (0, 65535), (1, 0)] + \
+            [(int(x), int(y)) for x, y in zip(rng.integers(0, B, 5), rng.integers(0, H, 5))]
+    T_k = -(-L // N)
+    kk = opred.topk_count(T_k, sp)
+    for bb, hh in heads:
+        s = opred.pooled_scores(q[0, hh % src.H], k[0, hh % src.H], M, N)
+        keep = oracle.unpack_mask(bits[bb, hh].cpu().numpy().view(np.uint32), T_k)
+        assert np.all(keep.sum(axis=1) == kk)
+        thr = -np.sort(-s, axis=1)[:, kk - 1]
+        delta = 1e-4 * np.abs(s).max(axis=1) + 1e-6
+        assert np.all(keep[s > (thr + delta)[:, None]]) and not np.any(keep[s < (thr - delta)[:, None]])

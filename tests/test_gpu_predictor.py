@@ -63,8 +63,9 @@ def test_predictor_ties_go_to_smaller_tile(L, M, N):
     torch = torch_or_skip()
     say(f"predictor ties L={L} {M}x{N}")
     d = 64
-    q = torch.randn(1, 1, L, d).to(torch.bfloat16)
-    k = torch.randn(1, 1, N, d).repeat(1, 1, L // N, 1).to(torch.bfloat16)   # all key tiles equal
+    g = torch.Generator().manual_seed(L + N)
+    q = torch.randn(1, 1, L, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(1, 1, N, d, generator=g).repeat(1, 1, L // N, 1).to(torch.bfloat16)   # all key tiles equal
     bits = _run(q, k, M, N, 50)
     keep = oracle.unpack_mask(bits[0, 0], L // N)
     kk = opred.topk_count(L // N, 50)

@@ -353,6 +353,7 @@ static PredictPlan predict_plan(const tsa_problem_t* p) {
     pl.R = pl.T_q;
     pl.G = (int)(cap / head_bytes);
     if (pl.G > BH) pl.G = BH;
+    if (pl.G > 65535) pl.G = 65535;  // the score grid's third dimension
     if (pl.G < 1) pl.G = 1;
   } else {
     pl.G = 1;
