@@ -85,3 +85,41 @@ def test_predictor_hunyuan_sampled_rows():
         s = opred.pooled_scores(q[0, h], k[0, h], w.M, w.N, rows=tiles[0, h])
         mism += _check_rows(bits[0, h, tiles[0, h]], s, 85)
     print(f"[predictor] near-threshold decisions differing from fp64: {mism}", flush=True)
+
+
+@pytest.mark.parametrize("L,M,N,sp", [(4096, 16, 16, 85), (6000, 16, 4, 70)])
+def test_predictor_rows_with_a_spike_of_equal_scores(L, M, N, sp):
+    """Most key tiles are copies of one tile, so every row holds a run of
+    equal scores: where the k-th largest falls in that run the row's bin
+    overflows and the row is finished by the exact per-row select, elsewhere
+    the run lies clear of the threshold.  Both kinds of rows keep exactly k,
+    respect the threshold band, and keep the equal scores of the run in
+    ascending j order (ties to the smaller tile)."""
+    torch = torch_or_skip()
+    say(f"predictor spike L={L} {M}x{N} sp={sp}")
+    d = 64
+    T_k = L // N
+    g = torch.Generator().manual_seed(L + sp)
+    q = torch.randn(1, 2, L, d, generator=g)
+    k = torch.randn(1, 2, L, d, generator=g)
+    copies = torch.rand(T_k, generator=g) < 0.6          # key tiles replaced by tile 0
+    kt = k.view(1, 2, T_k, N, d)
+    kt[:, :, copies] = kt[:, :, :1]
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    bits = _run(q, k, M, N, sp)
+    kk = opred.topk_count(T_k, sp)
+    run_rows = 0
+    for h in range(2):
+        s = opred.pooled_scores(q[0, h], k[0, h], M, N)
+        _check_rows(bits[0, h], s, sp)
+        keep = oracle.unpack_mask(bits[0, h], T_k)
+        srt = -np.sort(-s, axis=1)
+        for i in range(s.shape[0]):
+            same = np.flatnonzero(s[i] == s[i, 0])       # the copies of tile 0 (and tile 0)
+            kept = keep[i, same]
+            # kept members of the run form a prefix in j order
+            assert not np.any(~kept[:-1] & kept[1:]), f"row {i}: equal scores not kept by smaller j"
+            if srt[i, kk - 1] == s[i, 0] and 0 < kept.sum() < same.size:
+                run_rows += 1
+    print(f"[predictor] spike rows split inside the run: {run_rows}", flush=True)
+    assert run_rows > 0, "no row has its threshold inside the run of equal scores"
