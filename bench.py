@@ -484,7 +484,7 @@ def bench_predict(args, w, name, qd, kd, q_cpu, k_cpu):
                       "T_q": w.T_q, "T_k": w.T_k, "sparsity_percent": sp, "score_flops": fl},
            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                         "frac": round(achieved / peak, 4), "traffic": None,
-                        "kernel": "pool_tiles_kernel + pooled_scores_kernel + select_pack_kernel",
+                        "kernel": "pool_tiles_kernel + predict_fused_kernel + predict_rows_fallback_kernel",
                         "call_ms": round(ms_call, 4), "call_median_ms": round(st["median_ms"], 4),
                         "note": "the fp32 matrix-core peak: the products are fp32-accurate"}}
     if not args.no_cpu:

@@ -351,8 +351,8 @@ def test_mask_calls_at_maximum_heads():
 @pytest.mark.timeout(600)
 def test_predictor_at_maximum_heads():
     """The mask predictor over B*H = 2^20 heads (L = 48, d = 64, 16x16 tiles:
-    3 x 3 pooled scores per head, the top one of three kept at 50%): heads go
-    through the score and select kernels 65535 at a time.  Sampled heads
+    3 x 3 pooled scores per head, the top one of three kept at 50%): 2^20
+    work-groups of the fused score-and-select kernel in one launch.  Sampled heads
     against the oracle predictor: exactly k kept per row, and every tile
     clearly above (below) the oracle's k-th score kept (dropped)."""
     torch = torch_or_skip()

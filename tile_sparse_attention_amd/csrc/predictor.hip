@@ -6,17 +6,33 @@
 //   1. pool:    Qbar_i = mean of the valid rows of query tile i, Kbar_j = mean
 //               of the keys of key tile j (fp32 sums of the input elements),
 //               each stored as a bf16 high part and a bf16 low part;
-//   2. score:   s_ij = Qbar_i . Kbar_j for a block of query-tile rows, on the
-//               bf16 matrix cores with each fp32 operand split into two bf16
-//               parts (three products per pair), staged through LDS;
-//   3. select:  per row (held in registers when it has at most 8192 key tiles), an
-//               exact radix select of the k-th largest score on
-//               order-preserving 32-bit keys, then keep everything above it
-//               plus the first (by ascending j) of the scores equal to it, so
-//               exactly k tiles are kept and ties go to the smaller j;
-//               the decisions are packed 64 at a time with a wave ballot.
+//   2. score:   s_ij = Qbar_i . Kbar_j on the bf16 matrix cores with each fp32
+//               operand split into two bf16 parts (three products per pair);
+//   3. select:  per row, the k highest scores, equal scores going to the
+//               smaller j, packed into the row's keep bits.
 // k = T_k - 1 - floor(sparsity * (T_k - 1) / 100): with distinct scores these
 // are the tiles strictly above the row's linearly interpolated percentile.
+//
+// Steps 2 and 3 run in one kernel and no score is ever stored: a work-group
+// owns 64 query-tile rows and streams the head's pooled keys past them three
+// times.
+//   pass 1  mean mu and spread sigma of each row's scores (high parts only);
+//   pass 2  full scores counted into a per-row histogram over the window
+//           [mu - a sigma', mu + b sigma'] (sigma' = sigma with a margin),
+//           with a = sqrt(1/q - 1), b = sqrt(1/p - 1), p = k / T_k,
+//           q = (T_k - k + 1) / T_k: by Cantelli's inequality the k-th largest
+//           of any set of T_k values with that mean and spread lies in it;
+//           scores above the window are counted apart;
+//   pass 3  the same scores again: tiles above the bin that holds the k-th
+//           largest are kept, and that bin's scores (a few dozen) are
+//           collected with their j in LDS, where the ones to keep are picked
+//           exactly (by score, then by smaller j).
+// A row whose k-th largest falls outside its window, or whose bin holds more
+// than kPredCap scores (many equal scores), is finished by a second kernel
+// that recomputes the row's scores on the vector units and runs an exact
+// radix select over them.
+#include <cmath>
+
 #include "tsa_device.h"
 #include "tsa.h"
 
@@ -25,11 +41,13 @@ namespace tsa {
 // out_hi/out_lo[bh][t][dd]: the fp32 mean of tile t's valid rows of x at
 // column dd, split into a bf16 high part (round to nearest even) and a bf16
 // low part (the rounded remainder), the operands of the split-precision
-// score product below.
+// score product below.  The first thread also clears *clear (the count of
+// rows left to the exact fallback kernel), when given.
 template <typename E>
 __global__ __launch_bounds__(256) void pool_tiles_kernel(const E* __restrict__ x, bf16_t* __restrict__ out_hi,
                                                          bf16_t* __restrict__ out_lo, long long total, int L,
-                                                         int d, int T, int tile) {
+                                                         int d, int T, int tile, int* __restrict__ clear) {
+  if (clear != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *clear = 0;
   for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long long)gridDim.x * 256) {
     const int dd = (int)(idx % d);
     const long long bt = idx / d;
@@ -56,322 +74,557 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
                                                  0, 0, 0);
 }
 
-// scores[z][r][j] = Qbar[bh0+z][i0+r] . Kbar[bh0+z][j] for r < rows, j < T_k.
-// Each fp32 mean x is held as x = hi + lo with hi, lo bf16, and a product as
-// hi_q hi_k + hi_q lo_k + lo_q hi_k on the bf16 matrix cores (16x16x32, fp32
-// accumulation): the dropped lo_q lo_k term and the rounding of lo leave a
-// relative error near 2^-16 per term, against 2^-24 for fp32 products, at
-// the bf16 rate instead of the fp32 matrix-core rate.
-// A work-group owns 128 query-tile rows (wave w: rows 32w..32w+31, held as
-// register operands) and a run of 128-wide key-tile blocks, which stream
-// through two LDS buffers (hi and lo planes, rows 288 bytes apart: the
-// 16-byte operand reads of 16 rows are free of bank conflicts) filled by
-// direct global-to-LDS loads one block ahead.
-constexpr int kScoreTile = 128;
-
-template <int D>
-struct ScoreGemm {
-  static constexpr int TB = kScoreTile;
-  static constexpr int RB = D * 2;                       // bf16 row bytes
-  static constexpr int RS = RB + 32;                     // LDS row stride
-  static constexpr int NI_T = (TB * RS + 1023) / 1024;   // 1-KB loads per plane tile
-  static constexpr int NS = D / 32;                      // 32-wide d slabs
-  struct Buf {
-    __attribute__((aligned(16))) uint8_t hi[NI_T * 1024];
-    __attribute__((aligned(16))) uint8_t lo[NI_T * 1024];
-  };
-};
-
-template <int D>
-__global__ __launch_bounds__(256) void pooled_scores_kernel(const bf16_t* __restrict__ qhi,
-                                                            const bf16_t* __restrict__ qlo,
-                                                            const bf16_t* __restrict__ khi,
-                                                            const bf16_t* __restrict__ klo,
-                                                            float* __restrict__ scores, int T_q, int T_k,
-                                                            int T_kp, int i0, int rows, int R, int bh0,
-                                                            int blocks_per_wg) {
-  using G = ScoreGemm<D>;
-  constexpr int TB = G::TB;
-  __shared__ __attribute__((aligned(16))) typename G::Buf b0;
-  __shared__ __attribute__((aligned(16))) typename G::Buf b1;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
-  const int bh = bh0 + blockIdx.z;
-  const int rbase = TB * blockIdx.y;
-  const int nblk = T_kp / TB;
-  const int t0 = blockIdx.x * blocks_per_wg;
-  const int t1 = t0 + blocks_per_wg < nblk ? t0 + blocks_per_wg : nblk;
-  if (t0 >= t1) return;
-  // this wave's query operands: lane (g, n) holds row n of each 16-row
-  // block, d = 32 sl + 8g .. +7 of each slab
-  u32x4 ah[2][G::NS], al[2][G::NS];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int r = rbase + 32 * wave + 16 * rb + n;
-    const size_t row = (size_t)bh * T_q + i0 + (r < rows ? r : rows - 1);
-#pragma unroll
-    for (int sl = 0; sl < G::NS; ++sl) {
-      ah[rb][sl] = *reinterpret_cast<const u32x4*>(qhi + row * D + 32 * sl + 8 * g);
-      al[rb][sl] = *reinterpret_cast<const u32x4*>(qlo + row * D + 32 * sl + 8 * g);
-      if (r >= rows) ah[rb][sl] = al[rb][sl] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  // this wave's share of the loads of key block t into buffer bf: plane
-  // rows of keys past T_k read as zero (out of the buffer's range), as do
-  // the padding bytes of each LDS row
-  auto issue = [&](int t, typename G::Buf& bf) {
-    const int kb = t * TB;
-    const int nrows = T_k - kb < TB ? T_k - kb : TB;
-    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(khi + ((size_t)bh * T_k + kb) * D), (short)0, nrows * G::RB, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(klo + ((size_t)bh * T_k + kb) * D), (short)0, nrows * G::RB, kBufferFlags);
-    for (int I = wave; I < G::NI_T; I += 4) {
-      const int pos = I * 1024 + 16 * lane;
-      const int row = pos / G::RS, cb = pos - row * G::RS;
-      const uint32_t off = row < TB && cb < G::RB ? (uint32_t)(row * G::RB + cb) : 0x80000000u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (__attribute__((address_space(3))) void*)(bf.hi + I * 1024),
-                                               16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(bf.lo + I * 1024),
-                                               16, off, 0, 0, 0);
-    }
-  };
-  auto compute = [&](int t, const typename G::Buf& bf) {
-    f32x4 acc[2][TB / 16];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int jb = 0; jb < TB / 16; ++jb) acc[rb][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const lds_cptr ph = to_lds(bf.hi) + n * G::RS + 16 * g;
-    const lds_cptr pl = to_lds(bf.lo) + n * G::RS + 16 * g;
-#pragma unroll
-    for (int sl = 0; sl < G::NS; ++sl) {
-#pragma unroll
-      for (int jb = 0; jb < TB / 16; ++jb) {
-        const u32x4 bh_ = lds_read16(ph + 16 * jb * G::RS + 64 * sl);
-        const u32x4 bl_ = lds_read16(pl + 16 * jb * G::RS + 64 * sl);
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          acc[rb][jb] = mfma_bf16(ah[rb][sl], bh_, acc[rb][jb]);
-          acc[rb][jb] = mfma_bf16(ah[rb][sl], bl_, acc[rb][jb]);
-          acc[rb][jb] = mfma_bf16(al[rb][sl], bh_, acc[rb][jb]);
-        }
-      }
-    }
-    // D[m][c] of block (rb, jb): lane (g, n) holds rows 4g..4g+3, column n
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int jb = 0; jb < TB / 16; ++jb) {
-        const int j = t * TB + 16 * jb + n;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = rbase + 32 * wave + 16 * rb + 4 * g + i;
-          if (r < rows && j < T_k) scores[((size_t)blockIdx.z * R + r) * T_kp + j] = acc[rb][jb][i];
-        }
-      }
-  };
-  issue(t0, b0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  // two blocks per iteration, so that each buffer is named statically
-  for (int t = t0; t < t1; t += 2) {
-    // buffer 1 was last read in the previous iteration, which every wave has left
-    if (t + 1 < t1) issue(t + 1, b1);
-    compute(t, b0);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of block t+1 have landed
-    __syncthreads();                // ... and every other wave's; buffer 0 is free
-    if (t + 1 >= t1) break;
-    if (t + 2 < t1) issue(t + 2, b0);
-    compute(t + 1, b1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-}
-
+// Order-preserving 32-bit key of a float (larger float, larger key; -0 = +0).
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;  // -0 ranks with +0
+  if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Rows of up to this many key tiles are held in registers while they are
-// selected (32 keys per thread: thread t owns tiles t, t + 256, ...); longer
-// rows are read from the score block on every pass.
-constexpr int kSelectRowMax = 8192;
+constexpr int kPredRows = 64;  // query-tile rows per work-group
+constexpr int kPredCap = 64;   // scores of a row's threshold bin held in LDS
 
-template <bool IN_REG>
-__global__ __launch_bounds__(256) void select_pack_kernel(const float* __restrict__ scores,
-                                                          uint32_t* __restrict__ mask, int T_q,
-                                                          int T_k, int T_kp, int words, int i0,
-                                                          int rows, int R, int bh0, int k) {
-  // Histogram of one digit (4096 bins for the first, 1024 for the others),
-  // wave totals of its scan, and the pass's result.
+// Histogram bins of one row: 128 words, as 256 bins of 16-bit counts (rows of
+// at most 65535 key tiles) or 128 bins of 32-bit counts (longer rows).
+template <bool WIDE>
+struct PredBins {
+  static constexpr int NB = WIDE ? 128 : 256;
+  __device__ static int word(int b) { return WIDE ? b : b >> 1; }
+  __device__ static uint32_t inc(int b) { return WIDE ? 1u : 1u << ((b & 1) * 16); }
+  __device__ static int count(uint32_t w, int b) { return WIDE ? (int)w : (int)((w >> ((b & 1) * 16)) & 0xffffu); }
+};
+
+// The work-group's 64 query-tile rows stay in LDS (hi and lo planes, rows
+// 2d + 32 bytes apart so that the 16-byte operand reads of 16 rows hit
+// distinct banks).  Each wave takes the 32-key blocks w, w + 4, ... of the
+// head and streams their pooled keys from L2 straight into registers, one
+// 16-key block ahead, as the B operands of 16x16x32 products against all 64
+// rows: no key staging and no barrier per block.  Lane (g, n) of a 16-key
+// block holds the scores of rows 16 rb + 4g + i (rb, i < 4) for key n.
+template <int D, bool WIDE>
+__global__ __launch_bounds__(256, 2) void predict_fused_kernel(
+    const bf16_t* __restrict__ qhi, const bf16_t* __restrict__ qlo, const bf16_t* __restrict__ khi,
+    const bf16_t* __restrict__ klo, uint32_t* __restrict__ mask, int* __restrict__ fb_list,
+    int* __restrict__ fb_count, int T_q, int T_k, int words, int k, float wa, float wb, int blk0, int nblocks) {
+  using Bn = PredBins<WIDE>;
+  constexpr int R = kPredRows, NS = D / 32, RB = 2 * D, RS = RB + 32, NB = Bn::NB, CAP = kPredCap;
+  __shared__ __attribute__((aligned(16))) uint8_t qs_h[R * RS];
+  __shared__ __attribute__((aligned(16))) uint8_t qs_l[R * RS];
+  // per row: its histogram (128 words), later its threshold-bin scores
+  // (64 order keys, then their 64 j)
+  __shared__ __attribute__((aligned(16))) uint32_t hs[R * 128];
+  __shared__ float mom[4][R][3];  // per wave and row: shift, sum and sum of squares of deviations
+  __shared__ float mcnt[4];       // keys each wave saw
+  __shared__ int ok_sh[R];        // the row has a usable window
+  __shared__ int ca_sh[R];        // scores above the window
+  __shared__ int bs_sh[R];        // threshold bin, -1: row left to the fallback
+  __shared__ int kr_sh[R];        // scores of the threshold bin to keep
+  __shared__ int cn_sh[R];        // scores in the threshold bin
+  __shared__ int cc_sh[R];        // scores collected so far in pass 3
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int rblocks = (T_q + R - 1) / R;
+  const int lb = blk0 + xcd_major_block((int)blockIdx.x, nblocks);
+  const int bh = lb / rblocks;
+  const int i0 = (lb - bh * rblocks) * R;
+  const int rows = T_q - i0 < R ? T_q - i0 : R;
+  const size_t row0 = (size_t)bh * T_q + i0;  // first global row of the work-group
+
+  if (k <= 0) {  // a single key tile: nothing lies strictly above the percentile
+    for (int e = tid; e < rows * words; e += 256) mask[row0 * words + e] = 0u;
+    return;
+  }
+  // the rows' pooled queries to LDS (rows past T_q as zeros), histograms cleared
+  for (int e = tid; e < R * (RB / 16); e += 256) {
+    const int r = e / (RB / 16), c = e - r * (RB / 16);
+    u32x4 h = u32x4{0u, 0u, 0u, 0u}, l = h;
+    if (r < rows) {
+      h = *reinterpret_cast<const u32x4*>(qhi + (row0 + r) * D + 8 * c);
+      l = *reinterpret_cast<const u32x4*>(qlo + (row0 + r) * D + 8 * c);
+    }
+    *reinterpret_cast<u32x4*>(qs_h + r * RS + 16 * c) = h;
+    *reinterpret_cast<u32x4*>(qs_l + r * RS + 16 * c) = l;
+  }
+  for (int e = tid; e < R * 32; e += 256) reinterpret_cast<u32x4*>(hs)[e] = u32x4{0u, 0u, 0u, 0u};
+  if (tid < R) {
+    ca_sh[tid] = 0;
+    cc_sh[tid] = 0;
+  }
+  __syncthreads();
+
+  // this wave's 16-key blocks when the work-group takes every st-th 32-key
+  // block: q -> keys 32 st (wave + 4 (q >> 1)) + 16 (q & 1) + n
+  const int nsb = (T_k + 31) / 32;
+  auto nblocks_at = [&](int st) {
+    return st * wave < nsb ? 2 * ((nsb - st * wave + 4 * st - 1) / (4 * st)) : 0;
+  };
+  auto kbase = [&](int q, int st) { return 32 * st * (wave + 4 * (q >> 1)) + 16 * (q & 1); };
+  const __amdgpu_buffer_rsrc_t rkh = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(khi + (size_t)bh * T_k * D), (short)0, T_k * RB, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rkl = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(klo + (size_t)bh * T_k * D), (short)0, T_k * RB, kBufferFlags);
+  // slab sl of block q's B operands (keys past T_k read as zero: offsets
+  // past the resource)
+  auto load = [&](int q, int st, int sl, u32x4& kh, u32x4& kl, bool full) {
+    const uint32_t o = (uint32_t)(kbase(q, st) + n) * RB + 16 * g + 64 * sl;
+    kh = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rkh, o, 0, 0));
+    if (full) kl = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rkl, o, 0, 0));
+  };
+  const lds_cptr pqh = to_lds(qs_h) + n * RS + 16 * g;
+  const lds_cptr pql = to_lds(qs_l) + n * RS + 16 * g;
+  // every block of the wave: its scores against the 64 rows, the two 16-key
+  // blocks of a 32-key block together so that each query operand read from
+  // LDS feeds both.  Each slab's registers are refilled with the next 32-key
+  // block's slab as soon as its products are issued.
+  auto run = [&](bool full, int st, auto&& body) {
+    const int nq = nblocks_at(st);
+    if (nq == 0) return;
+    u32x4 h0[NS], l0[NS], h1[NS], l1[NS];
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+      load(0, st, sl, h0[sl], l0[sl], full);
+      load(1, st, sl, h1[sl], l1[sl], full);
+    }
+    for (int q = 0; q < nq; q += 2) {  // nq is even
+      // the query operands are the same for every block: read them again
+      // per block rather than holding all of them in registers
+      const int z = opaque_zero();
+      f32x4 a0[4], a1[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) a0[rb] = a1[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const u32x4 ah = lds_read16(pqh + z + 16 * rb * RS + 64 * sl);
+          a0[rb] = mfma_bf16(ah, h0[sl], a0[rb]);
+          a1[rb] = mfma_bf16(ah, h1[sl], a1[rb]);
+          if (full) {
+            const u32x4 al = lds_read16(pql + z + 16 * rb * RS + 64 * sl);
+            a0[rb] = mfma_bf16(ah, l0[sl], a0[rb]);
+            a1[rb] = mfma_bf16(ah, l1[sl], a1[rb]);
+            a0[rb] = mfma_bf16(al, h0[sl], a0[rb]);
+            a1[rb] = mfma_bf16(al, h1[sl], a1[rb]);
+          }
+        }
+        if (q + 2 < nq) {
+          load(q + 2, st, sl, h0[sl], l0[sl], full);
+          load(q + 3, st, sl, h1[sl], l1[sl], full);
+        }
+      }
+      body(kbase(q, st), q, a0);
+      body(kbase(q + 1, st), q + 1, a1);
+    }
+  };
+
+  // ---- pass 1: mean and spread of each row's scores (high parts only) over
+  // every fourth 32-key block of rows longer than 2048 key tiles, a sample
+  // spread evenly over the row (the moments only place the window: a row
+  // whose k-th largest falls outside it goes to the fallback), per wave as
+  // deviations from the wave's score of its first key ----
+  {
+    float c0[4][4], s1[4][4], s2[4][4], cnt = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c0[rb][i] = s1[rb][i] = s2[rb][i] = 0.f;
+    run(false, nsb > 64 ? 4 : 1, [&](int kb, int q, const f32x4 (&acc)[4]) {
+      if (q == 0) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) c0[rb][i] = __shfl(acc[rb][i], lane & 48);
+      }
+      const bool in = kb + n < T_k;
+      cnt += in ? 1.f : 0.f;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float dv = in ? acc[rb][i] - c0[rb][i] : 0.f;
+          s1[rb][i] += dv;
+          s2[rb][i] = fmaf(dv, dv, s2[rb][i]);
+        }
+    });
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) cnt += __shfl_xor(cnt, m);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float a = s1[rb][i], b = s2[rb][i];
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) {
+          a += __shfl_xor(a, m);
+          b += __shfl_xor(b, m);
+        }
+        if (n == 0) {
+          const int r = 16 * rb + 4 * g + i;
+          mom[wave][r][0] = c0[rb][i];
+          mom[wave][r][1] = a;
+          mom[wave][r][2] = b;
+        }
+      }
+    if (lane == 0) mcnt[wave] = cnt;
+  }
+  __syncthreads();
+  // the rows' windows, the four waves' moments combined about wave 0's shift.
+  // A score s is placed by x = (s - lo) inv, monotone in s: bin floor(x) for
+  // 0 <= x < NB, above the window for x >= NB.  A row without a window gets
+  // lo = +inf, inv = 0, so x is NaN and it is counted nowhere.
+  float wlo[4][4], winv[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rb + 4 * g + i;
+      const float c = mom[0][r][0];
+      const float ns = mcnt[0] + mcnt[1] + mcnt[2] + mcnt[3];  // keys sampled
+      float a = 0.f, b = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float nw = mcnt[w], dc = mom[w][r][0] - c, sw = mom[w][r][1];
+        a += sw + nw * dc;
+        b += mom[w][r][2] + 2.f * dc * sw + nw * dc * dc;
+      }
+      const float md = a / ns;
+      const float var = fmaxf(b / ns - md * md, 0.f);
+      const float mu = c + md;
+      const float sd = sqrtf(var);
+      const float sdw = sd * 1.0625f + 1e-5f * fabsf(mu);
+      const float lo = mu - wa * sdw, hi = mu + wb * sdw;
+      const float inv = (float)NB / (hi - lo);
+      const bool ok = r < rows && hi - lo > 0.f && __builtin_isfinite(inv) && __builtin_isfinite(lo) &&
+                      __builtin_isfinite(hi);
+      wlo[rb][i] = ok ? lo : __builtin_inff();
+      winv[rb][i] = ok ? inv : 0.f;
+      if (wave == 0 && n == 0) ok_sh[r] = ok ? 1 : 0;
+    }
+
+  // ---- pass 2: histogram of each row's scores in its window ----
+  {
+    int ca[4][4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ca[rb][i] = 0;
+    run(true, 1, [&](int kb, int, const f32x4 (&acc)[4]) {
+      const bool in = kb + n < T_k;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = (acc[rb][i] - wlo[rb][i]) * winv[rb][i];
+          if (in && x >= (float)NB) {
+            ++ca[rb][i];
+          } else if (in && x >= 0.f) {
+            const int b = (int)x;
+            const int r = 16 * rb + 4 * g + i;
+            atomicAdd(&hs[r * 128 + (Bn::word(b) ^ (r & 31))], Bn::inc(b));
+          }
+        }
+    });
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int a = ca[rb][i];
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) a += __shfl_xor(a, m);
+        if (n == 0 && a != 0) atomicAdd(&ca_sh[16 * rb + 4 * g + i], a);
+      }
+  }
+  __syncthreads();
+  // threshold bin of each row (wave w: rows 16w .. 16w + 15): lane l holds
+  // the bins NB-1-PER l .. NB-PER-PER l (descending), scanned across the wave
+  constexpr int PER = NB / 64;
+  for (int rl = 0; rl < 16; ++rl) {
+    const int r = 16 * wave + rl;
+    if (r >= rows) break;
+    const int need = ok_sh[r] ? k - ca_sh[r] : 0;
+    int bs = -1, kr = 0, cn = 0;
+    if (need > 0) {
+      int cnt[PER], sum = 0;
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const int b = NB - 1 - PER * lane - q;
+        cnt[q] = Bn::count(hs[r * 128 + (Bn::word(b) ^ (r & 31))], b);
+        sum += cnt[q];
+      }
+      int inc = sum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(inc, off);
+        if (lane >= off) inc += y;
+      }
+      const uint64_t reach = __ballot(inc >= need);
+      if (reach != 0ull) {  // else the k-th largest lies below the window
+        const int L = __builtin_ctzll(reach);
+        int cum = inc - sum, fb = 0, fk = 0, fc = 0;
+        bool found = false;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          if (!found && cum + cnt[q] >= need) {
+            found = true;
+            fb = NB - 1 - PER * lane - q;
+            fk = need - cum;
+            fc = cnt[q];
+          }
+          cum += cnt[q];
+        }
+        bs = __shfl(fb, L);
+        kr = __shfl(fk, L);
+        cn = __shfl(fc, L);
+        if (cn > CAP) bs = -1;
+      }
+    }
+    if (lane == 0) {
+      bs_sh[r] = bs;
+      kr_sh[r] = kr;
+      cn_sh[r] = cn;
+      if (bs < 0) fb_list[atomicAdd(fb_count, 1)] = (int)(row0 + r);
+    }
+  }
+  __syncthreads();  // every row's bin is known; the histograms are free
+
+  // ---- pass 3: keep bits above the threshold bin; that bin's scores to LDS ----
+  // With x as in pass 2, a score lies above the threshold bin b (or above the
+  // window) iff x >= b + 1, and in it iff not that and x >= b.  Rows left to
+  // the fallback keep nothing here (threshold +inf).
+  float tk[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rb + 4 * g + i;
+      const int bs = r < rows ? bs_sh[r] : -1;
+      tk[rb][i] = bs >= 0 ? (float)(bs + 1) : __builtin_inff();
+    }
+  // lane l stores the word of row l: keys 32 sb .. 32 sb + 31 of its super-block
+  const int srb = lane >> 4, sg = (lane >> 2) & 3, si = lane & 3;
+  const bool sok = lane < rows && bs_sh[lane] >= 0;
+  uint32_t* __restrict__ srow = mask + (row0 + lane) * (size_t)words;
+  uint32_t word = 0u;
+  run(true, 1, [&](int kb, int q, const f32x4 (&acc)[4]) {
+    const bool in = kb + n < T_k;
+    uint32_t half = 0u;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s = acc[rb][i];
+        const float x = (s - wlo[rb][i]) * winv[rb][i];
+        const bool keep = in && x >= tk[rb][i];
+        const uint64_t bal = __ballot(keep);
+        if (rb == srb && i == si) half = (uint32_t)(bal >> (16 * sg)) & 0xffffu;
+        if (in && !keep && x >= tk[rb][i] - 1.f) {
+          const int r = 16 * rb + 4 * g + i;
+          const int pos = atomicAdd(&cc_sh[r], 1);
+          if (pos < CAP) {
+            hs[r * 128 + pos] = order_key(s);
+            hs[r * 128 + 64 + pos] = (uint32_t)(kb + n);
+          }
+        }
+      }
+    if ((q & 1) == 0) {
+      word = half;
+    } else {
+      word |= half << 16;
+      const int w = kb >> 5;
+      if (sok && w < words) srow[w] = word;
+    }
+  });
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's word stores have landed
+  __syncthreads();                // ... and every wave's, before the ORs below
+  // ---- the threshold bin's scores: keep the kr best (larger key, then smaller j) ----
+  for (int rl = 0; rl < 16; ++rl) {
+    const int r = 16 * wave + rl;
+    if (r >= rows) break;
+    if (bs_sh[r] < 0) continue;
+    const int cnum = cc_sh[r];
+    if (cnum != cn_sh[r]) {  // not the count pass 2 found: leave the row to the fallback
+      if (lane == 0) fb_list[atomicAdd(fb_count, 1)] = (int)(row0 + r);
+      continue;
+    }
+    const int kr = kr_sh[r];
+    const uint32_t key = lane < cnum ? hs[r * 128 + lane] : 0u;
+    const uint32_t j = lane < cnum ? hs[r * 128 + 64 + lane] : 0u;
+    int rank = 0;  // candidates before this one: larger key, or equal key and smaller j
+    for (int c = 0; c < cnum; ++c) {
+      const uint32_t k2 = (uint32_t)__builtin_amdgcn_readlane((int)key, c);
+      const uint32_t j2 = (uint32_t)__builtin_amdgcn_readlane((int)j, c);
+      rank += (k2 > key || (k2 == key && j2 < j)) ? 1 : 0;
+    }
+    if (lane < cnum && rank < kr) atomicOr(&mask[(row0 + r) * words + (j >> 5)], 1u << (j & 31));
+  }
+}
+
+// Rows of at most this many key tiles are scored once into LDS by the
+// fallback kernel; longer rows are scored again on every pass.
+constexpr int kFallbackRowMax = 8192;
+
+// Exact select for the rows the fused kernel left (fb_list[0 .. *fb_count)):
+// one work-group per row computes the row's scores on the vector units
+// (fp32 fused multiply-adds of the same three split products), once into
+// LDS or, for long rows, whenever it needs them, finds the k-th largest by a radix select over order-preserving
+// keys (digits of 12, 10 and 10 bits, LDS histograms), and writes the row's
+// words in full: keys above it, then the first (by ascending j) of the keys
+// equal to it until k are kept.
+template <int D>
+__global__ __launch_bounds__(256) void predict_rows_fallback_kernel(
+    const bf16_t* __restrict__ qhi, const bf16_t* __restrict__ qlo, const bf16_t* __restrict__ khi,
+    const bf16_t* __restrict__ klo, uint32_t* __restrict__ mask, const int* __restrict__ fb_list,
+    const int* __restrict__ fb_count, int T_q, int T_k, int words, int k) {
+  __shared__ float qh_s[D], ql_s[D];
+  __shared__ float row_s[kFallbackRowMax];
   __shared__ int hbin[4096];
   __shared__ int wsum[4];
   __shared__ uint32_t sh_prefix;
   __shared__ int sh_kr, sh_eqn;
   __shared__ int sh_eq[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int z = blockIdx.x / rows, il = blockIdx.x % rows;
-  const float* srow = scores + ((size_t)z * R + il) * T_kp;
-  uint32_t* out = mask + ((size_t)(bh0 + z) * T_q + i0 + il) * words;
-  if (k <= 0) {  // a single key tile: nothing lies strictly above the percentile
-    for (int w = tid; w < words; w += 256) out[w] = 0u;
-    return;
-  }
-  // the thread's keys, read from the score block once (every load issued
-  // before the first is waited for); every later access of the thread is to
-  // one of its own tiles t + 256 i
-  constexpr int NPT = IN_REG ? kSelectRowMax / 256 : 1;
-  uint32_t rk[NPT];
-  if constexpr (IN_REG) {
-#pragma unroll
-    for (int t = 0; t < NPT; ++t) {
-      const int j = tid + 256 * t;
-      rk[t] = order_key(j < T_k ? srow[j] : 0.f);
-    }
-  }
-  // key of tile j = tid + 256 * t
-  auto key_at = [&](int t, int j) -> uint32_t {
-    if constexpr (IN_REG) return rk[t];
-    else return order_key(srow[j]);
-  };
-  constexpr int TMAX = IN_REG ? NPT : 0x7fffffff;  // bound of t (the real bound is j < T_k)
-
-  // -- radix select of the k-th largest key: digits of 12, 10 and 10 bits.
-  // The first digit (sign, exponent and three mantissa bits) spreads scores
-  // over many bins; later digits count only the keys under the prefix found
-  // so far, a few dozen at most. --
-  uint32_t prefix = 0, pmask = 0;
-  int kr = k;
-#pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 20 : pass == 1 ? 10 : 0;
-    const int nb = pass == 0 ? 4096 : 1024;
-    const uint32_t dmask = (uint32_t)nb - 1u;
-    for (int e = tid; e < nb; e += 256) hbin[e] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      const int j = tid + 256 * t;
-      if (j >= T_k) break;
-      const uint32_t key = key_at(t, j);
-      if ((key & pmask) == prefix) atomicAdd(&hbin[(key >> shift) & dmask], 1);
+  const int nrows = *fb_count;
+  for (int idx = blockIdx.x; idx < nrows; idx += gridDim.x) {
+    const int grow = fb_list[idx];
+    const int bh = grow / T_q;
+    uint32_t* out = mask + (size_t)grow * words;
+    __syncthreads();  // the previous row's readers of the LDS arrays are done
+    for (int dd = tid; dd < D; dd += 256) {
+      qh_s[dd] = bf16_to_f32(qhi[(size_t)grow * D + dd]);
+      ql_s[dd] = bf16_to_f32(qlo[(size_t)grow * D + dd]);
     }
     __syncthreads();
-    // thread t owns the digits nb-1-t*per .. nb-per-t*per (descending)
-    const int per = nb >> 8;
-    int s = 0;
-    for (int q = 0; q < per; ++q) s += hbin[nb - 1 - tid * per - q];
-    int inc = s;
+    const bf16_t* kh0 = khi + (size_t)bh * T_k * D;
+    const bf16_t* kl0 = klo + (size_t)bh * T_k * D;
+    auto score_at = [&](int j) -> float {
+      const u32x4* ph = reinterpret_cast<const u32x4*>(kh0 + (size_t)j * D);
+      const u32x4* pl = reinterpret_cast<const u32x4*>(kl0 + (size_t)j * D);
+      float s = 0.f;
+#pragma unroll 4
+      for (int c = 0; c < D / 8; ++c) {
+        const u32x4 h = ph[c], l = pl[c];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(inc, off);
-      if (lane >= off) inc += y;
-    }
-    if (lane == 63) wsum[wave] = inc;
-    __syncthreads();
-    for (int w = 0; w < wave; ++w) inc += wsum[w];
-    const int exc = inc - s;
-    if (exc < kr && inc >= kr) {
-      int cum = exc;
-      for (int q = 0; q < per; ++q) {
-        const int dgt = nb - 1 - tid * per - q;
-        const int c = hbin[dgt];
-        if (cum + c >= kr) {
-          sh_prefix = prefix | ((uint32_t)dgt << shift);
-          sh_kr = kr - cum;
-          sh_eqn = c;  // after the last digit: the keys equal to the k-th largest
-          break;
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t wh = h[e >> 1], wlo = l[e >> 1];
+          const float kh = __uint_as_float((e & 1) ? (wh & 0xffff0000u) : (wh << 16));
+          const float kl = __uint_as_float((e & 1) ? (wlo & 0xffff0000u) : (wlo << 16));
+          const float qh = qh_s[8 * c + e], ql = ql_s[8 * c + e];
+          s = fmaf(qh, kh, s);
+          s = fmaf(qh, kl, s);
+          s = fmaf(ql, kh, s);
         }
-        cum += c;
       }
+      return s;
+    };
+    const bool in_lds = T_k <= kFallbackRowMax;
+    if (in_lds) {
+      for (int j = tid; j < T_k; j += 256) row_s[j] = score_at(j);
+      __syncthreads();
     }
-    __syncthreads();
-    prefix = sh_prefix;
-    kr = sh_kr;
-    pmask |= dmask << shift;
-    __syncthreads();
-  }
-  // prefix = k-th largest key; keep key > prefix, and the first kr keys == prefix.
-  if (sh_eqn == kr) {
-    // every key equal to the k-th largest is kept (the usual case: no ties),
-    // so each wave packs 64-key runs on its own, with no ranks to count
+    auto key_at = [&](int j) -> uint32_t { return order_key(in_lds ? row_s[j] : score_at(j)); };
+    // radix select of the k-th largest key, digits of 12, 10 and 10 bits
+    uint32_t prefix = 0, pmask = 0;
+    int kr = k;
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 20 : pass == 1 ? 10 : 0;
+      const int nb = pass == 0 ? 4096 : 1024;
+      const uint32_t dmask = (uint32_t)nb - 1u;
+      for (int e = tid; e < nb; e += 256) hbin[e] = 0;
+      __syncthreads();
+      for (int j = tid; j < T_k; j += 256) {
+        const uint32_t key = key_at(j);
+        if ((key & pmask) == prefix) atomicAdd(&hbin[(key >> shift) & dmask], 1);
+      }
+      __syncthreads();
+      // thread t owns the digits nb-1-t*per .. nb-per-t*per (descending)
+      const int per = nb >> 8;
+      int s = 0;
+      for (int q = 0; q < per; ++q) s += hbin[nb - 1 - tid * per - q];
+      int inc = s;
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      const int base = 64 * wave + 256 * t, j = base + lane;
-      if (base >= T_k) break;
-      const uint64_t kb = __ballot(j < T_k && key_at(t, j) >= prefix);
-      const int w0 = base >> 5;
-      if (lane == 0) out[w0] = (uint32_t)kb;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(inc, off);
+        if (lane >= off) inc += y;
+      }
+      if (lane == 63) wsum[wave] = inc;
+      __syncthreads();
+      for (int w = 0; w < wave; ++w) inc += wsum[w];
+      const int exc = inc - s;
+      if (exc < kr && inc >= kr) {
+        int cum = exc;
+        for (int q = 0; q < per; ++q) {
+          const int dgt = nb - 1 - tid * per - q;
+          const int c = hbin[dgt];
+          if (cum + c >= kr) {
+            sh_prefix = prefix | ((uint32_t)dgt << shift);
+            sh_kr = kr - cum;
+            sh_eqn = c;  // after the last digit: the keys equal to the k-th largest
+            break;
+          }
+          cum += c;
+        }
+      }
+      __syncthreads();
+      prefix = sh_prefix;
+      kr = sh_kr;
+      pmask |= dmask << shift;
+      __syncthreads();
+    }
+    // prefix = k-th largest key; keep key > prefix, and the first kr keys == prefix
+    const bool all_eq = sh_eqn == kr;
+    int eq_before = 0;  // equal keys at smaller j, across earlier rounds
+    for (int base = 0; base < T_k; base += 256) {
+      const int j = base + tid;
+      const uint32_t key = j < T_k ? key_at(j) : 0u;
+      const bool eq = j < T_k && key == prefix;
+      bool keep;
+      if (all_eq) {
+        keep = j < T_k && key >= prefix;
+      } else {
+        const uint64_t eqb = __ballot(eq);
+        if (lane == 0) sh_eq[wave] = __builtin_popcountll(eqb);
+        __syncthreads();
+        int before = eq_before;
+        for (int w = 0; w < wave; ++w) before += sh_eq[w];
+        const int rank = before + (int)prefix_count64(eqb);
+        keep = j < T_k && (key > prefix || (eq && rank < kr));
+        eq_before += sh_eq[0] + sh_eq[1] + sh_eq[2] + sh_eq[3];
+        __syncthreads();
+      }
+      const uint64_t kb = __ballot(keep);
+      const int w0 = (base >> 5) + 2 * wave;
+      if (lane == 0 && w0 < words) out[w0] = (uint32_t)kb;
       if (lane == 1 && w0 + 1 < words) out[w0 + 1] = (uint32_t)(kb >> 32);
     }
-    return;
-  }
-  int eq_before = 0;  // equal keys at smaller j, across earlier rounds
-#pragma unroll
-  for (int t = 0; t < TMAX; ++t) {
-    const int base = 256 * t, j = base + tid;
-    if (base >= T_k) break;
-    const uint32_t key = j < T_k ? key_at(t, j) : 0u;
-    const bool eq = j < T_k && key == prefix;
-    const uint64_t eqb = __ballot(eq);
-    if (lane == 0) sh_eq[wave] = __builtin_popcountll(eqb);
-    __syncthreads();
-    int before = eq_before;
-    for (int w = 0; w < wave; ++w) before += sh_eq[w];
-    const int rank = before + (int)prefix_count64(eqb);
-    const bool keep = j < T_k && (key > prefix || (eq && rank < kr));
-    const uint64_t kb = __ballot(keep);
-    const int w0 = (base >> 5) + 2 * wave;
-    if (lane == 0 && w0 < words) out[w0] = (uint32_t)kb;
-    if (lane == 1 && w0 + 1 < words) out[w0 + 1] = (uint32_t)(kb >> 32);
-    eq_before += sh_eq[0] + sh_eq[1] + sh_eq[2] + sh_eq[3];
-    __syncthreads();
   }
 }
 
 struct PredictPlan {
-  int T_q, T_k, T_kp, words, R, G;
-  size_t q_plane_bytes, k_plane_bytes, score_bytes;
+  int T_q, T_k, words;
+  size_t q_plane_bytes, k_plane_bytes, list_bytes;
 };
 
-// Scores are materialised for G heads x R rows at a time, within a 224 MiB
-// cap: small enough that a block written by the score kernel is still in the
-// chip's 256 MB memory-side cache when the select kernel reads it.
 static PredictPlan predict_plan(const tsa_problem_t* p) {
   PredictPlan pl;
   pl.T_q = (p->L + p->M - 1) / p->M;
   pl.T_k = (p->L + p->N - 1) / p->N;
-  pl.T_kp = (pl.T_k + kScoreTile - 1) / kScoreTile * kScoreTile;
   pl.words = (pl.T_k + 31) / 32;
-  const size_t cap = (size_t)224 << 20;
-  const size_t row_bytes = (size_t)pl.T_kp * sizeof(float);
-  const size_t head_bytes = row_bytes * (size_t)pl.T_q;
-  const int BH = p->B * p->H;
-  if (head_bytes <= cap) {
-    pl.R = pl.T_q;
-    pl.G = (int)(cap / head_bytes);
-    if (pl.G > BH) pl.G = BH;
-    if (pl.G > 65535) pl.G = 65535;  // the score grid's third dimension
-    if (pl.G < 1) pl.G = 1;
-  } else {
-    pl.G = 1;
-    long long r = (long long)(cap / row_bytes) / kScoreTile * kScoreTile;
-    if (r < kScoreTile) r = kScoreTile;
-    pl.R = (int)(r < pl.T_q ? r : pl.T_q);
-  }
+  const size_t BH = (size_t)p->B * p->H;
   // bf16 hi and lo planes of the pooled means
-  pl.q_plane_bytes = ((size_t)BH * pl.T_q * p->d * sizeof(bf16_t) + 255) & ~(size_t)255;
-  pl.k_plane_bytes = ((size_t)BH * pl.T_k * p->d * sizeof(bf16_t) + 255) & ~(size_t)255;
-  pl.score_bytes = (size_t)pl.G * pl.R * row_bytes;
+  pl.q_plane_bytes = (BH * pl.T_q * p->d * sizeof(bf16_t) + 255) & ~(size_t)255;
+  pl.k_plane_bytes = (BH * pl.T_k * p->d * sizeof(bf16_t) + 255) & ~(size_t)255;
+  // the fallback's row count (one 256-byte slot), then its row list
+  pl.list_bytes = 256 + ((BH * pl.T_q * sizeof(int) + 255) & ~(size_t)255);
   return pl;
 }
 
 size_t predict_workspace(const tsa_problem_t* p) {
   const PredictPlan pl = predict_plan(p);
-  return 2 * pl.q_plane_bytes + 2 * pl.k_plane_bytes + pl.score_bytes;
+  return 2 * pl.q_plane_bytes + 2 * pl.k_plane_bytes + pl.list_bytes;
 }
+
+// Work-groups of the fallback kernel; each takes rows idx, idx + this, ...
+constexpr int kFallbackGroups = 1024;
 
 hipError_t launch_predict_mask(const tsa_problem_t* p, const void* q, const void* k,
                                int sparsity_percent, uint32_t* mask_out, void* workspace,
@@ -382,56 +635,56 @@ hipError_t launch_predict_mask(const tsa_problem_t* p, const void* q, const void
   bf16_t* qlo = reinterpret_cast<bf16_t*>(ws + pl.q_plane_bytes);
   bf16_t* khi = reinterpret_cast<bf16_t*>(ws + 2 * pl.q_plane_bytes);
   bf16_t* klo = reinterpret_cast<bf16_t*>(ws + 2 * pl.q_plane_bytes + pl.k_plane_bytes);
-  float* sc = reinterpret_cast<float*>(ws + 2 * pl.q_plane_bytes + 2 * pl.k_plane_bytes);
-  const int BH = p->B * p->H;
-  const long long nq = (long long)BH * pl.T_q * p->d;
-  const long long nk = (long long)BH * pl.T_k * p->d;
+  int* fb_count = reinterpret_cast<int*>(ws + 2 * pl.q_plane_bytes + 2 * pl.k_plane_bytes);
+  int* fb_list = fb_count + 64;
+  const long long BH = (long long)p->B * p->H;
+  const long long nq = BH * pl.T_q * p->d;
+  const long long nk = BH * pl.T_k * p->d;
   if (p->dtype == TSA_DTYPE_BF16) {
     hipLaunchKernelGGL(pool_tiles_kernel<bf16_t>, dim3(stride_blocks(nq, 256)), dim3(256), 0, stream,
-                       static_cast<const bf16_t*>(q), qhi, qlo, nq, p->L, p->d, pl.T_q, p->M);
+                       static_cast<const bf16_t*>(q), qhi, qlo, nq, p->L, p->d, pl.T_q, p->M, fb_count);
     hipLaunchKernelGGL(pool_tiles_kernel<bf16_t>, dim3(stride_blocks(nk, 256)), dim3(256), 0, stream,
-                       static_cast<const bf16_t*>(k), khi, klo, nk, p->L, p->d, pl.T_k, p->N);
+                       static_cast<const bf16_t*>(k), khi, klo, nk, p->L, p->d, pl.T_k, p->N, nullptr);
   } else {
     hipLaunchKernelGGL(pool_tiles_kernel<float>, dim3(stride_blocks(nq, 256)), dim3(256), 0, stream,
-                       static_cast<const float*>(q), qhi, qlo, nq, p->L, p->d, pl.T_q, p->M);
+                       static_cast<const float*>(q), qhi, qlo, nq, p->L, p->d, pl.T_q, p->M, fb_count);
     hipLaunchKernelGGL(pool_tiles_kernel<float>, dim3(stride_blocks(nk, 256)), dim3(256), 0, stream,
-                       static_cast<const float*>(k), khi, klo, nk, p->L, p->d, pl.T_k, p->N);
+                       static_cast<const float*>(k), khi, klo, nk, p->L, p->d, pl.T_k, p->N, nullptr);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int kk = pl.T_k - 1 - (int)(((long long)sparsity_percent * (pl.T_k - 1)) / 100);
-  const int nblk = pl.T_kp / kScoreTile;
-  for (int bh0 = 0; bh0 < BH; bh0 += pl.G) {
-    const int G = BH - bh0 < pl.G ? BH - bh0 : pl.G;
-    for (int i0 = 0; i0 < pl.T_q; i0 += pl.R) {
-      const int rows = pl.T_q - i0 < pl.R ? pl.T_q - i0 : pl.R;
-      // key blocks split over work-groups so that one round of them (one per
-      // compute unit: the two LDS buffers take most of its LDS) covers the
-      // chip: each work-group streams its run of blocks past resident rows
-      const int rblocks = (rows + kScoreTile - 1) / kScoreTile;
-      int splits = 256 / (rblocks * G);
-      if (splits < 1) splits = 1;
-      if (splits > nblk) splits = nblk;
-      const int per = (nblk + splits - 1) / splits;
-      splits = (nblk + per - 1) / per;
-      const dim3 grid((unsigned)splits, (unsigned)rblocks, (unsigned)G);
-      if (p->d == 128)
-        hipLaunchKernelGGL(pooled_scores_kernel<128>, grid, dim3(256), 0, stream, qhi, qlo, khi, klo, sc, pl.T_q,
-                           pl.T_k, pl.T_kp, i0, rows, pl.R, bh0, per);
-      else
-        hipLaunchKernelGGL(pooled_scores_kernel<64>, grid, dim3(256), 0, stream, qhi, qlo, khi, klo, sc, pl.T_q,
-                           pl.T_k, pl.T_kp, i0, rows, pl.R, bh0, per);
-      if (pl.T_k <= kSelectRowMax)  // rows held in registers
-        hipLaunchKernelGGL(select_pack_kernel<true>, dim3((unsigned)(G * rows)), dim3(256), 0, stream, sc,
-                           mask_out, pl.T_q, pl.T_k, pl.T_kp, pl.words, i0, rows, pl.R, bh0, kk);
-      else
-        hipLaunchKernelGGL(select_pack_kernel<false>, dim3((unsigned)(G * rows)), dim3(256), 0, stream, sc,
-                           mask_out, pl.T_q, pl.T_k, pl.T_kp, pl.words, i0, rows, pl.R, bh0, kk);
-      err = hipGetLastError();
-      if (err != hipSuccess) return err;
+  // Cantelli window multipliers: p = kk / T_k of the scores lie at or above
+  // the k-th largest, q = (T_k - kk + 1) / T_k at or below it
+  const double pf = (double)kk / pl.T_k, qf = (double)(pl.T_k - kk + 1) / pl.T_k;
+  const float wa = (float)std::sqrt(qf < 1.0 ? 1.0 / qf - 1.0 : 0.0);
+  const float wb = kk > 0 ? (float)std::sqrt(1.0 / pf - 1.0) : 0.f;
+  const long long rblocks = (pl.T_q + kPredRows - 1) / kPredRows;
+  const long long total = BH * rblocks;
+  const bool wide = pl.T_k > 65535;
+  for (long long b0 = 0; b0 < total; b0 += kMaxStrideBlocks) {
+    const int nb = (int)(total - b0 < kMaxStrideBlocks ? total - b0 : kMaxStrideBlocks);
+#define TSA_PRED_LAUNCH(D_, W_)                                                                            \
+  hipLaunchKernelGGL((predict_fused_kernel<D_, W_>), dim3((unsigned)nb), dim3(256), 0, stream, qhi, qlo, khi, klo, \
+                     mask_out, fb_list, fb_count, pl.T_q, pl.T_k, pl.words, kk, wa, wb, (int)b0, nb)
+    if (p->d == 128) {
+      if (wide) TSA_PRED_LAUNCH(128, true);
+      else TSA_PRED_LAUNCH(128, false);
+    } else {
+      if (wide) TSA_PRED_LAUNCH(64, true);
+      else TSA_PRED_LAUNCH(64, false);
     }
+#undef TSA_PRED_LAUNCH
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
   }
-  return hipSuccess;
+  if (p->d == 128)
+    hipLaunchKernelGGL(predict_rows_fallback_kernel<128>, dim3(kFallbackGroups), dim3(256), 0, stream, qhi, qlo,
+                       khi, klo, mask_out, fb_list, fb_count, pl.T_q, pl.T_k, pl.words, kk);
+  else
+    hipLaunchKernelGGL(predict_rows_fallback_kernel<64>, dim3(kFallbackGroups), dim3(256), 0, stream, qhi, qlo,
+                       khi, klo, mask_out, fb_list, fb_count, pl.T_q, pl.T_k, pl.words, kk);
+  return hipGetLastError();
 }
 
 }  // namespace tsa
