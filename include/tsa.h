@@ -214,6 +214,8 @@ tsa_status_t tsa_mask_compact(const tsa_problem_t* p, const uint32_t* mask_bits,
  * the tiles strictly above the row's linearly interpolated
  * sparsity_percent-th percentile.  q, k: [B,H,L,d]; 0 <= sparsity_percent < 100.
  * mask_out: [B,H,T_q,W] uint32, written in full (padding bits zero).
+ * No score is stored: the workspace holds the pooled means and a list of
+ * rows for an exact per-row pass.
  * workspace: tsa_workspace_size(TSA_OP_PREDICT_MASK) bytes. */
 tsa_status_t tsa_predict_mask(const tsa_problem_t* p, const void* q, const void* k,
                               int32_t sparsity_percent, uint32_t* mask_out,
