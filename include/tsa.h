@@ -150,8 +150,8 @@ tsa_status_t tsa_quantize_qk_fp8(const tsa_problem_t* p, const void* q, const vo
  * tsa_attention_fwd.  q8, k8, q_scale, k_scale as tsa_quantize_qk_fp8 writes
  * them; v, mask_bits, o, lse, scale and the workspace
  * (tsa_workspace_size(TSA_OP_ATTENTION_FWD)) as in tsa_attention_fwd.
- * Supported: p->dtype bf16, d = 128, M in {16, 32, 64}, N in {8, 16, 32, 64};
- * other shapes return TSA_ERR_UNSUPPORTED. */
+ * Supported: p->dtype bf16, d = 128, M in {16, 32, 64}, N in
+ * {1, 2, 4, 8, 16, 32, 64}; other shapes return TSA_ERR_UNSUPPORTED. */
 tsa_status_t tsa_attention_fwd_fp8(const tsa_problem_t* p,
                                    const uint8_t* q8, const uint8_t* k8,
                                    const float* q_scale, const float* k_scale,

@@ -89,18 +89,22 @@ def _run(w, bits, case, scale=None, q=None, k=None, v=None, normal_inputs=True):
 
 
 @pytest.mark.parametrize("M,N,L", [(16, 8, 1000), (16, 16, 1003), (32, 32, 777), (64, 64, 1029), (16, 8, 13),
-                                   (32, 8, 4099)])
+                                   (32, 8, 4099), (16, 1, 1000), (16, 2, 777), (16, 4, 1003), (32, 1, 300),
+                                   (64, 2, 515), (16, 1, 13)])
 def test_fp8_attention_parity(M, N, L):
     w = small_workload(f"f8_{M}x{N}", L, 128, M, N, p=0.3, seed=800 + M + N + L)
     _run(w, W.mask_bits(w), f"fp8 {M}x{N} L={L}")
 
 
 # kept tiles per (query tile, 128-key chunk) cycling through every count a
-# pass can end on: four octets per pass, a short last pass at one or two
-_PASS_COUNTS = {8: (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 15, 16), 16: (0, 1, 2, 3, 4, 5, 6, 7, 8)}
+# pass can end on: 32 keys per pass with a short last pass at 16 or fewer
+# (N < 8), four octets per pass with a short last pass at one or two (N >= 8)
+_PASS_COUNTS = {1: (0, 1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64, 65, 100, 127, 128),
+                4: (0, 1, 3, 4, 5, 7, 8, 9, 15, 16, 17, 24, 31, 32),
+                8: (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 15, 16), 16: (0, 1, 2, 3, 4, 5, 6, 7, 8)}
 
 
-@pytest.mark.parametrize("N", [8, 16])
+@pytest.mark.parametrize("N", [1, 4, 8, 16])
 def test_fp8_kept_counts_at_pass_boundaries(N):
     L = 2048 + 77   # 16 whole chunks and a partial one
     w = small_workload(f"f8_passes_{N}", L, 128, 16, N, seed=840 + N)
@@ -135,12 +139,18 @@ def test_fp8_attention_large_logits_and_empty_rows():
 
 
 def test_fp8_rejects_unsupported_shapes():
+    """d = 64 has no FP8 path (one 16x16x128 step would be half padding): the
+    call is refused before any kernel runs."""
     import tile_sparse_attention_amd as T
     torch = torch_or_skip()
-    w = small_workload("f8_n4", 300, 128, 16, 4, seed=83)
-    q, k, v = W.make_qkv(w)
-    q8, qs, k8, ks = _quantize_gpu(q, k)
+    B, H, L, d = 1, 2, 300, 64
+    q8 = torch.zeros((B, H, L, d), dtype=torch.uint8, device="cuda")
+    k8 = torch.zeros_like(q8)
+    qs = torch.ones((B, H, -(-L // 16)), dtype=torch.float32, device="cuda")
+    ks = torch.ones((B, H), dtype=torch.float32, device="cuda")
+    v = torch.zeros((B, H, L, d), dtype=torch.bfloat16, device="cuda")
+    mask = torch.zeros((B, H, -(-L // 16), T.mask_row_words(L, 8)), dtype=torch.int32, device="cuda")
     with pytest.raises(T.TsaError) as e:
-        T.attention_fwd_fp8(q8, k8, qs, ks, v.cuda(), to_dev_mask(W.mask_bits(w)), 16, 4)
+        T.attention_fwd_fp8(q8, k8, qs, ks, v, mask, 16, 8)
     assert e.value.status == T.ERR_UNSUPPORTED
     torch.cuda.synchronize()

@@ -234,8 +234,8 @@ tsa_status_t tsa_attention_fwd_fp8(const tsa_problem_t* p, const uint8_t* q8, co
                                    void* workspace, size_t workspace_bytes, void* stream) {
   tsa_status_t s = check_problem(p, true);
   if (s != TSA_OK) return s;
-  if (p->dtype != TSA_DTYPE_BF16 || p->d != 128 || p->N < 8)
-    return fail(TSA_ERR_UNSUPPORTED, "FP8 attention: bf16 v/o, d = 128 and N >= 8 (got d=%d N=%d)", p->d, p->N);
+  if (p->dtype != TSA_DTYPE_BF16 || p->d != 128)
+    return fail(TSA_ERR_UNSUPPORTED, "FP8 attention: bf16 v/o and d = 128 (got d=%d)", p->d);
   if (!q8 || !k8 || !q_scale || !k_scale || !v || !mask_bits || !o)
     return fail(TSA_ERR_INVALID_ARGUMENT, "q8, k8, q_scale, k_scale, v, mask_bits and o must be non-NULL");
   if (!std::isfinite(scale)) return fail(TSA_ERR_INVALID_ARGUMENT, "scale is not finite");

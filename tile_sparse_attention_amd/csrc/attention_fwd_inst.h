@@ -94,13 +94,13 @@ hipError_t launch_attn_oct(const AttnLaunch& a) {
 
 // bf16 with key tiles of N < 8: the key-packing kernel (V read as rows, no
 // V^T workspace).
-template <int D, int N>
+template <int D, int N, bool F8 = false>
 hipError_t launch_attn_key(const AttnLaunch& a) {
-  using C = KeyCfg<D, N>;
+  using C = KeyCfg<D, N, F8>;
   const AttnParams p = attn_params(a, C::ROWS);
   const long long blocks = (long long)a.p->B * a.p->H * p.n_qblocks;
   mark_event(a.ev_start, a.stream);
-  hipLaunchKernelGGL((attn_key_kernel<D, N>), dim3((unsigned)blocks), dim3(64 * C::W), 0, a.stream, p);
+  hipLaunchKernelGGL((attn_key_kernel<D, N, F8>), dim3((unsigned)blocks), dim3(64 * C::W), 0, a.stream, p);
   mark_event(a.ev_stop, a.stream);
   return hipGetLastError();
 }

@@ -41,7 +41,7 @@
 
 namespace tsa {
 
-template <int D, int N>
+template <int D, int N, bool F8 = false>
 struct KeyCfg {
   static constexpr int KC = 128;                   // keys per chunk
   static constexpr int W = 16;                     // waves per work-group
@@ -49,26 +49,34 @@ struct KeyCfg {
   static constexpr int TPC = KC / N;               // key tiles per chunk (32, 64, 128)
   static constexpr int MW = TPC / 32;              // mask words per chunk
   static constexpr int LOG2N = ilog2(N);
-  static constexpr int NSLAB = D / 32;             // 32-wide d slabs of the QK^T contraction
+  // Q/K elements: bf16, or FP8 (e4m3) whose 16x16x128 matrix-core step takes
+  // the whole d range: then the Q fragment is two 16-byte halves
+  static constexpr int ESZ = F8 ? 1 : 2;           // bytes per Q / K element
+  static constexpr int NSLAB = F8 ? 2 : D / 32;    // 32-wide d slabs of the QK^T contraction
   static constexpr int NDB = D / 16;               // 16-wide d blocks of O^T
-  static constexpr int RB = D * 2;                 // K / V row bytes in memory
-  static constexpr int RS = RB + 32;               // K / V row stride in LDS
-  static constexpr int NI_T = (KC * RS + 1023) / 1024;  // 1-KB loads per K (or V) tile
-  static constexpr int NK_W = (NI_T + W - 1) / W;  // K (and V) pieces per wave
+  static constexpr int RB = D * 2;                 // V row bytes in memory
+  static constexpr int RS = RB + 32;               // V row stride in LDS
+  static constexpr int KRB = D * ESZ;              // K row bytes in memory
+  static constexpr int KRS = KRB + 32;             // K row stride in LDS
+  static constexpr int NI_T = (KC * RS + 1023) / 1024;   // 1-KB loads per V tile
+  static constexpr int NI_K = (KC * KRS + 1023) / 1024;  // 1-KB loads per K tile
+  static constexpr int NK_W = (NI_T + W - 1) / W;  // V (and bf16 K) pieces per wave
+  static constexpr int NKK_W = (NI_K + W - 1) / W; // K pieces per wave
   static constexpr int LIST = KC + 32;             // list bytes per wave (entries + padding)
   static_assert(N == 1 || N == 2 || N == 4, "key kernel: N in {1,2,4}");
   static_assert(D % 32 == 0 && MW >= 1 && MW <= 4, "shape");
+  static_assert(!F8 || D == 128, "FP8 scores: d = 128 (one 16x16x128 step)");
 };
 
-template <int D, int N>
+template <int D, int N, bool F8 = false>
 struct KeyKernel {
-  using C = KeyCfg<D, N>;
+  using C = KeyCfg<D, N, F8>;
   static constexpr float RESCALE_STEP = 8.f;  // log2 units the max may grow before rescaling
 
   // one staging buffer (K and V rows of a chunk; the two buffers are separate
   // __shared__ objects, see lds_cptr) and the per-wave key lists
   struct Buf {
-    __attribute__((aligned(16))) uint8_t k[C::NI_T * 1024];
+    __attribute__((aligned(16))) uint8_t k[C::NI_K * 1024];
     __attribute__((aligned(16))) uint8_t v[C::NI_T * 1024];
   };
   struct Lists {
@@ -80,10 +88,11 @@ struct KeyKernel {
   Buf& bf1;
   Lists& ls;
   int lane, g, n, wave, L;
-  const bf16_t* __restrict__ kg;
+  const uint8_t* __restrict__ kg;
   const bf16_t* __restrict__ vg;
   const uint32_t* __restrict__ mrow;
-  uint32_t koff[C::NK_W];  // per-lane offsets of this wave's pieces of a full chunk
+  uint32_t koff[C::NK_W];  // per-lane offsets of this wave's pieces of a full chunk (V, and bf16 K)
+  uint32_t kkoff[F8 ? C::NKK_W : 1];  // the same for FP8 K rows
   u32x4 qf[C::NSLAB];
   f32x4 oacc[C::NDB + 1];
   float m_ref;        // reference max of this lane's query (log2 units)
@@ -101,16 +110,17 @@ struct KeyKernel {
     return B ? bf1 : bf0;
   }
 
-  // Byte offset read by lane `ln` for 1-KB piece `I` of a chunk's K (or V)
-  // tile with `rows` keys, relative to the tile's resource base; out of
-  // range (reads zero) for the padding bytes of an LDS row.  Rows past the
-  // last key repeat it.
+  // Byte offset read by lane `ln` for 1-KB piece `I` of a chunk's V (or K)
+  // tile with `rows` keys, relative to the tile's resource base (LDS rows RS
+  // apart, RB bytes each); out of range (reads zero) for the padding bytes of
+  // an LDS row.  Rows past the last key repeat it.
+  template <int RS = C::RS, int RB = C::RB>
   __device__ __forceinline__ uint32_t dma_offset(int I, int ln, int rows) const {
     constexpr uint32_t OOB = 0x80000000u;
     const int pos = I * 1024 + 16 * ln;
-    const int row = pos / C::RS, cb = pos - row * C::RS;
+    const int row = pos / RS, cb = pos - row * RS;
     const int r = row < rows ? row : rows - 1;
-    return row < C::KC && cb < C::RB ? (uint32_t)(r * C::RB + cb) : OOB;
+    return row < C::KC && cb < RB ? (uint32_t)(r * RB + cb) : OOB;
   }
 
   // This wave's share of the loads of chunk c into buffer `buf`, and the
@@ -120,7 +130,7 @@ struct KeyKernel {
     const int kbase = c * C::KC;
     const int rows = L - kbase < C::KC ? L - kbase : C::KC;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kg + (size_t)kbase * D), (short)0, rows * C::RB, kBufferFlags);
+        (void*)(kg + (size_t)kbase * C::KRB), (short)0, rows * C::KRB, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vg + (size_t)kbase * D), (short)0, rows * C::RB, kBufferFlags);
     if (rows < C::KC) {  // the last chunk (issued last): offsets for its rows
@@ -129,10 +139,18 @@ struct KeyKernel {
         const int j = wave + C::W * u;
         koff[u] = dma_offset(j < C::NI_T ? j : 0, lane, rows);
       }
+      if constexpr (F8) {
+#pragma unroll
+        for (int u = 0; u < C::NKK_W; ++u) {
+          const int j = wave + C::W * u;
+          kkoff[u] = dma_offset<C::KRS, C::KRB>(j < C::NI_K ? j : 0, lane, rows);
+        }
+      }
     }
-    // wave w loads K and V pieces w, w + W, ... (same offsets)
+    // wave w loads K and V pieces w, w + W, ... (bf16: the same offsets)
     typedef __attribute__((address_space(3))) uint8_t* dst_t;
-    load_pieces<C::NI_T, C::W>(rk, (dst_t)bufr<B>().k, koff, wave);
+    if constexpr (F8) load_pieces<C::NI_K, C::W>(rk, (dst_t)bufr<B>().k, kkoff, wave);
+    else load_pieces<C::NI_T, C::W>(rk, (dst_t)bufr<B>().k, koff, wave);
     load_pieces<C::NI_T, C::W>(rv, (dst_t)bufr<B>().v, koff, wave);
     const int w0 = (c * C::TPC) >> 5;
     // scalar loads (the mask is read-only here): the words land in scalar
@@ -193,21 +211,35 @@ struct KeyKernel {
     const uint32_t kk0 = lst[q0 + n];
     const int vp = q0 + 4 * g + (n >> 2);
     const uint32_t kv0 = lst[vp];
-    const lds_cptr kb = to_lds(bufr<B>().k) + 16 * g;
-    const lds_cptr ka0 = kb + kk0 * C::RS;
+    const lds_cptr kb = to_lds(bufr<B>().k) + (F8 ? 32 : 16) * g;
+    const lds_cptr ka0 = kb + kk0 * C::KRS;
     f32x4 s0 = nm4, s1 = nm4;
     uint32_t kv1 = 0;
     // raised wave priority from the score MFMAs through the softmax (as in
     // the octet kernel)
     __builtin_amdgcn_s_setprio(1);
-    if constexpr (SINGLE) {
+    if constexpr (F8) {
+      // one 16x16x128 FP8 step per score block: lane (g, n) supplies d =
+      // 32g..32g+31 of the K row of position q0+16b+n and of its query row
+      if constexpr (SINGLE) {
+        s0 = mac_fp8(lds_read16(ka0), lds_read16(ka0 + 16), qf[0], qf[1], s0);
+      } else {
+        const uint32_t kk1 = lst[q0 + 16 + n];
+        kv1 = lst[vp + 16];
+        const lds_cptr ka1 = kb + kk1 * C::KRS;
+        const u32x4 a0 = lds_read16(ka0), a1 = lds_read16(ka0 + 16);
+        const u32x4 b0 = lds_read16(ka1), b1 = lds_read16(ka1 + 16);
+        s0 = mac_fp8(a0, a1, qf[0], qf[1], s0);
+        s1 = mac_fp8(b0, b1, qf[0], qf[1], s1);
+      }
+    } else if constexpr (SINGLE) {
 #pragma unroll
       for (int sl = 0; sl < C::NSLAB; ++sl)
         s0 = Mma<bf16_t>::mac8(lds_read16(ka0 + 64 * sl), qf[sl], s0);
     } else {
       const uint32_t kk1 = lst[q0 + 16 + n];
       kv1 = lst[vp + 16];
-      const lds_cptr ka1 = kb + kk1 * C::RS;
+      const lds_cptr ka1 = kb + kk1 * C::KRS;
 #pragma unroll
       for (int sl = 0; sl < C::NSLAB; ++sl) {
         const u32x4 a0 = lds_read16(ka0 + 64 * sl);
@@ -334,25 +366,33 @@ struct KeyKernel {
     const int qb = lb - bh * p.n_qblocks;
     L = p.L;
     const size_t head_off = (size_t)bh * (size_t)L * D;
-    const bf16_t* __restrict__ qg = reinterpret_cast<const bf16_t*>(p.q) + head_off;
-    kg = reinterpret_cast<const bf16_t*>(p.k) + head_off;
+    kg = reinterpret_cast<const uint8_t*>(p.k) + head_off * C::ESZ;
     vg = reinterpret_cast<const bf16_t*>(p.v) + head_off;
 
     const int row0 = qb * C::ROWS + 16 * wave;
     const bool act = row0 < L;
     mrow = p.mask + ((size_t)bh * p.T_q + (size_t)(act ? row0 / p.M : 0)) * p.words;
     const int rq = row0 + n < L ? row0 + n : L - 1;
+    // lane (g, n): row n of the tile, d = 8g.. of each 32-wide slab (bf16),
+    // or d = 32g..32g+31 (FP8)
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(p.q) + (head_off + (size_t)rq * D) * C::ESZ;
 #pragma unroll
     for (int s = 0; s < C::NSLAB; ++s)
-      qf[s] = *reinterpret_cast<const u32x4*>(qg + (size_t)rq * D + 32 * s + 8 * g);
+      qf[s] = *reinterpret_cast<const u32x4*>(qrow + (F8 ? 32 * g + 16 * s : 64 * s + 16 * g));
     if (row0 + n >= L)
 #pragma unroll
       for (int s = 0; s < C::NSLAB; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
     cs = p.scale_log2;
-    if (cs < 0.f) {  // c*s = |c| * ((-q) . k), and negating bf16 is exact
+    if (cs < 0.f) {  // c*s = |c| * ((-q) . k), and negating bf16 / FP8 is exact
       cs = -cs;
+      constexpr uint32_t SIGN = F8 ? 0x80808080u : 0x80008000u;
 #pragma unroll
-      for (int s = 0; s < C::NSLAB; ++s) qf[s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      for (int s = 0; s < C::NSLAB; ++s) qf[s] ^= u32x4{SIGN, SIGN, SIGN, SIGN};
+    }
+    if constexpr (F8) {
+      // scores in FP8 units: the Q tile's and the head's K scale join c
+      const int t16 = (L + 15) >> 4;
+      cs *= p.q_scale[(size_t)bh * t16 + (act ? row0 >> 4 : 0)] * p.k_scale[bh];
     }
 #pragma unroll
     for (int j = 0; j <= C::NDB; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -366,6 +406,13 @@ struct KeyKernel {
     for (int u = 0; u < C::NK_W; ++u) {
       const int j = wave + C::W * u;
       koff[u] = dma_offset(j < C::NI_T ? j : 0, lane, C::KC);
+    }
+    if constexpr (F8) {
+#pragma unroll
+      for (int u = 0; u < C::NKK_W; ++u) {
+        const int j = wave + C::W * u;
+        kkoff[u] = dma_offset<C::KRS, C::KRB>(j < C::NI_K ? j : 0, lane, C::KC);
+      }
     }
     uint32_t mw[C::MW];
     issue_chunk<0>(0, mw);
@@ -397,10 +444,10 @@ struct KeyKernel {
   }
 };
 
-template <int D, int N>
+template <int D, int N, bool F8 = false>
 __global__ __launch_bounds__(1024) void attn_key_kernel(AttnParams p) {
-  static_assert(KeyCfg<D, N>::W == 16, "launch bounds: 16 waves");
-  using K = KeyKernel<D, N>;
+  static_assert(KeyCfg<D, N, F8>::W == 16, "launch bounds: 16 waves");
+  using K = KeyKernel<D, N, F8>;
   __shared__ __attribute__((aligned(16))) typename K::Buf b0;
   __shared__ __attribute__((aligned(16))) typename K::Buf b1;
   __shared__ __attribute__((aligned(16))) typename K::Lists lists;

@@ -128,16 +128,6 @@ __device__ __forceinline__ uint32_t octet_mask(uint32_t tb) {
   }
 }
 
-// One 16x16x128 FP8 (e4m3) matrix-core step, block scales 2^0: lane (g, n)
-// supplies 32 bytes of A's row n and of B's column n (a0|a1, b0|b1), the
-// same 32 k positions of the contraction in both.
-__device__ __forceinline__ f32x4 mac_fp8(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x4 c) {
-  typedef int i32x8 __attribute__((ext_vector_type(8)));
-  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-}
-
 // SKIP: the work-group visits only the chunks its bitmap marks as needed
 // (work-groups flagged by chunk_need_kernel); otherwise every chunk (the
 // work-groups not flagged).
