@@ -1,5 +1,6 @@
 """Parity of the backward and of the FP8 path at the full 16x8 benchmark shape
-(1 x 40 x 32760 x 128), on sampled outputs the oracle computes one by one.
+(1 x 40 x 32760 x 128), and of the FP8 path at the 16x1 shape (1 x 40 x
+75600 x 128), on sampled outputs the oracle computes one by one.
 
 The GPU computes everything; the oracle the sampled rows of two heads (0 and
 H-1): dQ of 16 sampled query tiles, dK and dV of 64 sampled keys (which needs
@@ -89,3 +90,41 @@ def test_fp8_full_shape_sampled():
         got.append(o[0, h][rows])
         ref.append(ro)
     compare("fp8 wan480_fine sampled", np.concatenate(got), np.concatenate(ref), "bf16")
+
+
+@pytest.mark.timeout(900)
+def test_fp8_wan720_n1_sampled():
+    """The FP8-score path of the key kernel at the full 16x1 shape
+    (1 x 40 x 75600 x 128, 80% i.i.d. per-key sparsity): the FP8 bytes and
+    scales of heads 0 and 39 in full, and their 256 sampled query tiles
+    against the oracle on the dequantised inputs."""
+    torch = torch_or_skip()
+    import tile_sparse_attention_amd as T
+    w = W.get("wan720_n1")
+    say("large-next wan720_n1 FP8: generating inputs")
+    q, k, v = W.make_qkv(w)
+    mask = T.maskgen_hash(w.B, w.H, w.L, w.M, w.N, **W.hash_params(w))
+    say("large-next wan720_n1 FP8: quantisation and attention on GPU")
+    q8, qs, k8, ks = T.quantize_qk_fp8(q.cuda(), k.cuda())
+    o = T.attention_fwd_fp8(q8, k8, qs, ks, v.cuda(), mask, w.M, w.N, w.scale)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    tiles = W.sample_tiles(w)
+    mnp = mask_to_np(mask)
+    got, ref = [], []
+    for h in (0, w.H - 1):
+        bits = np.zeros((w.T_q, w.words), dtype=np.uint32)
+        bits[tiles[0, h]] = W.pack_bits(W.mask_rows_bool(w, [(0, h, int(i)) for i in tiles[0, h]]))
+        assert np.array_equal(mnp[0, h, tiles[0, h]], bits[tiles[0, h]])
+        rq, rqs, rk, rks = fp8.quantize_qk(q[:, h:h + 1], k[:, h:h + 1])
+        gq = q8[:, h:h + 1].cpu().view(torch.float8_e4m3fn).float().numpy()
+        gk = k8[:, h:h + 1].cpu().view(torch.float8_e4m3fn).float().numpy()
+        assert np.array_equal(gq, rq) and np.array_equal(gk, rk)
+        assert np.array_equal(qs[:, h:h + 1].cpu().numpy(), rqs) and np.array_equal(ks[:, h:h + 1].cpu().numpy(), rks)
+        qdq = fp8.dequantize(rq, rqs, 16)[0, 0]
+        kdq = fp8.dequantize(rk, rks[..., None], w.L)[0, 0]
+        say(f"large-next wan720_n1 FP8: oracle head {h}")
+        rows, ro, _ = oracle.attention_rows(qdq, kdq, v[0, h], bits, w.M, w.N, w.scale, tiles[0, h])
+        got.append(o[0, h][rows])
+        ref.append(ro)
+    compare("fp8 wan720_n1 sampled", np.concatenate(got), np.concatenate(ref), "bf16")
