@@ -106,8 +106,8 @@ def test_fp8_at_maximum_heads():
     """The e4m3 quantisation of Q and K over B*H = 2^20 heads (L = 40, d = 128;
     the per-head K maxima run over a one-dimensional grid of 64 slices per
     head): sampled heads byte for byte against the oracle; then the FP8-score
-    attention over all heads (16x8), sampled heads against the oracle on the
-    dequantised Q and K."""
+    attention over all heads (16x8 through the octet kernel, 16x1 through the
+    key kernel), sampled heads against the oracle on the dequantised Q and K."""
     torch = torch_or_skip()
     import tile_sparse_attention_amd as T
     B, H, L = 16, BH_MAX // 16, 40
@@ -141,6 +141,25 @@ def test_fp8_at_maximum_heads():
         got.append(o[b, h].float().cpu().numpy())
         ref.append(ro[0, 0])
     compare(f"limits B*H={B * H} fp8 16x8", np.concatenate(got), np.concatenate(ref), "bf16")
+    # the key kernel's FP8 mode (16x1) over all heads, on the same e4m3 inputs
+    del mask, o
+    w1 = W.Workload("maxheads_f8_n1", B, H, L, 128, 16, 1, "bf16",
+                    W.MaskRecipe("hash", p_near=0.3, p_far=0.3, force_diag=True), 101)
+    say(f"limits B*H={B * H} L={L}: fp8 attention 16x1")
+    mask = T.maskgen_hash(B, H, L, w1.M, w1.N, **W.hash_params(w1))
+    o = T.attention_fwd_fp8(q8, k8, qs, ks, vd, mask, w1.M, w1.N, w1.scale)
+    torch.cuda.synchronize()
+    got, ref = [], []
+    for b, h in [(0, 0), (B - 1, H - 1), (3, 4097), (11, 60000)]:
+        s = h % src.H
+        bits = W.pack_bits(W.mask_rows_bool(w1, [(b, h, i) for i in range(w1.T_q)]))
+        assert np.array_equal(mask[b, h].cpu().numpy().view(np.uint32), bits)
+        rq, rqs, rk, rks = fp8.quantize_qk(q[:, s:s + 1], k[:, s:s + 1])
+        ro, _ = oracle.attention(fp8.dequantize(rq, rqs, 16), fp8.dequantize(rk, rks[..., None], L),
+                                 v[:, s:s + 1], bits[None, None], w1.M, w1.N, w1.scale)
+        got.append(o[b, h].float().cpu().numpy())
+        ref.append(ro[0, 0])
+    compare(f"limits B*H={B * H} fp8 16x1", np.concatenate(got), np.concatenate(ref), "bf16")
 
 
 @pytest.mark.timeout(900)
