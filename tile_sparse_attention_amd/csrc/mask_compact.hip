@@ -113,10 +113,25 @@ __device__ __forceinline__ void fill_row(const uint32_t* __restrict__ mask, long
                                          const long long* __restrict__ group_offsets,
                                          const long long* __restrict__ total, long long* __restrict__ row_ptr,
                                          int32_t* __restrict__ col_idx, long long col_capacity, int32_t* st) {
+  const uint32_t* r = mask + row * (long long)words;
+  const int lane = lane_id();
+  // The row's words come kSuperBlock 64-word blocks at a time, a word per
+  // lane per block, loaded one super-block ahead.  The first super-block is
+  // requested before the row's offset is known, so that the two loads'
+  // latencies overlap; a count-only call (capacity 0) reads no words.
+  const int nblk = (words + 63) >> 6;
+  uint32_t xn[kSuperBlock];
+  if (col_capacity > 0) {
+#pragma unroll
+    for (int u = 0; u < kSuperBlock; ++u) {
+      const int w = 64 * u + lane;
+      xn[u] = w < words ? r[w] : 0u;
+    }
+  }
   // the row's count group's offset plus the counts of the group's earlier
   // rows (lane i holds the count of the group's row i; one vector load)
   const long long grp = row / kRowsPerGroup, first = grp * kRowsPerGroup;
-  const int li = lane_id();
+  const int li = lane;
   int before = li < (int)(row - first) ? counts[first + li] : 0;
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) before += __shfl_xor(before, off);  // lanes 0..15 hold all
@@ -126,21 +141,10 @@ __device__ __forceinline__ void fill_row(const uint32_t* __restrict__ mask, long
     if (row == rows - 1) row_ptr[rows] = total[0];
   }
   if (start >= col_capacity) return;
-  const uint32_t* r = mask + row * (long long)words;
-  const int lane = lane_id();
   long long base = start;  // output slot of the block's first kept tile
-  // The row's words come kSuperBlock 64-word blocks at a time, a word per
-  // lane per block, loaded one super-block ahead.  A vector-memory wait
-  // also waits for the stores issued before it, so waiting once per
-  // super-block instead of once per block lets a block's stores overlap the
-  // next blocks' expansion.
-  const int nblk = (words + 63) >> 6;
-  uint32_t xn[kSuperBlock];
-#pragma unroll
-  for (int u = 0; u < kSuperBlock; ++u) {
-    const int w = 64 * u + lane;
-    xn[u] = w < words ? r[w] : 0u;
-  }
+  // A vector-memory wait also waits for the stores issued before it, so
+  // waiting once per super-block instead of once per block lets a block's
+  // stores overlap the next blocks' expansion.
   for (int b0 = 0; b0 < nblk && base < col_capacity; b0 += kSuperBlock) {
     uint32_t xc[kSuperBlock];
 #pragma unroll
