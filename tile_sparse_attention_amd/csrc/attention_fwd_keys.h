@@ -70,6 +70,8 @@ struct KeyCfg {
   static_assert(N == 1 || N == 2 || N == 4, "key kernel: N in {1,2,4}");
   static_assert(D % 32 == 0 && MW >= 1 && MW <= 4, "shape");
   static_assert(!F8 || D == 128, "FP8 scores: d = 128 (one 16x16x128 step)");
+  // bf16 K pieces are loaded with the V pieces' offsets and count
+  static_assert(F8 || (KRS == RS && NI_K == NI_T), "bf16 K and V tiles share one load geometry");
 };
 
 template <int D, int N, bool F8 = false>
