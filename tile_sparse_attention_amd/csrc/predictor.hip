@@ -16,7 +16,8 @@
 // Steps 2 and 3 run in one kernel and no score is ever stored: a work-group
 // owns 64 query-tile rows and streams the head's pooled keys past them three
 // times.
-//   pass 1  mean mu and spread sigma of each row's scores (high parts only);
+//   pass 1  mean mu and spread sigma of each row's scores (high parts only,
+//           over an even quarter of the keys of rows longer than 2048 tiles);
 //   pass 2  full scores counted into a per-row histogram over the window
 //           [mu - a sigma', mu + b sigma'] (sigma' = sigma with a margin),
 //           with a = sqrt(1/q - 1), b = sqrt(1/p - 1), p = k / T_k,
@@ -98,9 +99,9 @@ struct PredBins {
 // 2d + 32 bytes apart so that the 16-byte operand reads of 16 rows hit
 // distinct banks).  Each wave takes the 32-key blocks w, w + 4, ... of the
 // head and streams their pooled keys from L2 straight into registers, one
-// 16-key block ahead, as the B operands of 16x16x32 products against all 64
+// 32-key block ahead, as the B operands of 16x16x32 products against all 64
 // rows: no key staging and no barrier per block.  Lane (g, n) of a 16-key
-// block holds the scores of rows 16 rb + 4g + i (rb, i < 4) for key n.
+// half holds the scores of rows 16 rb + 4g + i (rb, i < 4) for key n.
 template <int D, bool WIDE>
 __global__ __launch_bounds__(256, 2) void predict_fused_kernel(
     const bf16_t* __restrict__ qhi, const bf16_t* __restrict__ qlo, const bf16_t* __restrict__ khi,
