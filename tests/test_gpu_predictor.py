@@ -123,3 +123,21 @@ def test_predictor_rows_with_a_spike_of_equal_scores(L, M, N, sp):
                 run_rows += 1
     print(f"[predictor] spike rows split inside the run: {run_rows}", flush=True)
     assert run_rows > 0, "no row has its threshold inside the run of equal scores"
+
+
+def test_predictor_rows_longer_than_65535_tiles():
+    """Rows of 70000 key tiles (L = 70000, 64x1 tiles): the fused kernel's
+    histograms switch from 16-bit to 32-bit counts past 65535 tiles.  Every
+    row of both heads against the oracle (exact k, threshold band)."""
+    torch_or_skip()
+    w = W.Workload("p_wide", 1, 2, 70000, 64, 64, 1, "bf16", W.MaskRecipe("predicted", sparsity_percent=85),
+                   77, offset_frame_tokens=14000, offset_sigma=0.5)
+    say("predictor rows of 70000 key tiles")
+    q, k, _ = W.make_qkv(w)
+    bits = _run(q, k, w.M, w.N, 85)
+    mism = 0
+    for h in range(w.H):
+        s = opred.pooled_scores(q[0, h], k[0, h], w.M, w.N)
+        assert s.shape[1] > 65535
+        mism += _check_rows(bits[0, h], s, 85)
+    print(f"[predictor] 70000-tile rows: near-threshold decisions differing from fp64: {mism}", flush=True)
