@@ -121,10 +121,11 @@ def test_fp8_kept_counts_at_pass_boundaries(N):
     _run(w, W.pack_bits(keep), f"fp8 16x{N} kept counts at pass boundaries")
 
 
-def test_fp8_attention_negative_scale_and_batch():
-    w = W.Workload("f8_neg", 2, 3, 600, 128, 16, 16, "bf16",
-                   W.MaskRecipe("hash", p_near=0.4, p_far=0.4, force_diag=True), 81)
-    _run(w, W.mask_bits(w), "fp8 16x16 B=2 H=3 scale<0", scale=-w.scale)
+@pytest.mark.parametrize("N", [16, 1])
+def test_fp8_attention_negative_scale_and_batch(N):
+    w = W.Workload(f"f8_neg_{N}", 2, 3, 600, 128, 16, N, "bf16",
+                   W.MaskRecipe("hash", p_near=0.4, p_far=0.4, force_diag=True), 81 + N)
+    _run(w, W.mask_bits(w), f"fp8 16x{N} B=2 H=3 scale<0", scale=-w.scale)
 
 
 def test_fp8_attention_large_logits_and_empty_rows():
