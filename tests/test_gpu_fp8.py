@@ -128,15 +128,16 @@ def test_fp8_attention_negative_scale_and_batch(N):
     _run(w, W.mask_bits(w), f"fp8 16x{N} B=2 H=3 scale<0", scale=-w.scale)
 
 
-def test_fp8_attention_large_logits_and_empty_rows():
+@pytest.mark.parametrize("N", [8, 1])
+def test_fp8_attention_large_logits_and_empty_rows(N):
     torch = torch_or_skip()
-    w = small_workload("f8_big", 700, 128, 16, 8, p=0.5, seed=82)
+    w = small_workload(f"f8_big_{N}", 700, 128, 16, N, p=0.5, seed=82 + N)
     q, k, v = W.make_qkv(w)
     q = (q.float() * 8).to(torch.bfloat16)
     keep = W.mask_rows_bool(w, np.array([(0, h, i) for h in range(2) for i in range(w.T_q)]))
     keep = keep.reshape(1, 2, w.T_q, w.T_k)
     keep[0, 1, ::4] = False
-    _run(w, W.pack_bits(keep), "fp8 16x8 logits x8, empty rows", q=q, k=k, v=v, normal_inputs=False)
+    _run(w, W.pack_bits(keep), f"fp8 16x{N} logits x8, empty rows", q=q, k=k, v=v, normal_inputs=False)
 
 
 def test_fp8_rejects_unsupported_shapes():
